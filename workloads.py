@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for KDA chunked prefill (test and bench infrastructure).
+
+This module only draws random tensors with the shapes and value distributions of
+the KDA prefill workloads; it holds no step of the delta-rule arithmetic, so both
+the HIP path and the oracle may take their inputs from it.
+
+Value recipe (the reading of the workloads; the pages fix only the gate floor):
+  * q, k ~ N(0, 1), L2-normalised over the key channels per (token, head) in
+    float32, then rounded to the compute dtype (bf16 round-to-nearest-even);
+  * v ~ N(0, 1), rounded to the compute dtype;
+  * g = -5 * sigmoid(N(0, 1)) in float32: a per-token, per-channel log decay in
+    [-5, 0].  -5 is the production ``gate_lower_bound`` the cudnn-frontend
+    Hopper KDA prefill PR (#1056, description and "Correctness") measures at;
+  * beta = sigmoid(N(0, 1)) in float32, already a value in (0, 1) (the
+    TensorRT-LLM KDA prefill fix PR #19826 names a "beta_sigmoid" test);
+  * initial state ~ N(0, 0.1^2) in float32 (sigma = 0.1), or zeros;
+  * the long-sequence workload pins 13 of 128 channels of every head at exactly
+    g = -5 for every token (10% of channels at the gate floor).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+GATE_LOWER_BOUND = -5.0
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    lengths: tuple          # per-sequence token counts
+    H: int
+    D: int                  # d_k == d_v
+    dtype: str              # "bf16" or "f32" for q, k, v, out
+    dense: bool             # [B, T, H, D] tensors (equal lengths) or packed + cu_seqlens
+    zero_state: bool = False
+    floor_channels: int = 0  # channels per head pinned at g = -5
+    seed: int = 0
+
+    @property
+    def n_seq(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def tokens(self) -> int:
+        return int(sum(self.lengths))
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "n_seq": self.n_seq, "tokens": self.tokens,
+                "H": self.H, "d_k": self.D, "d_v": self.D, "dtype": self.dtype,
+                "layout": "dense" if self.dense else "packed",
+                "initial_state": "zeros" if self.zero_state else "N(0,0.1^2)",
+                "seed": self.seed}
+
+
+def varlen_lengths(seed: int = 14, n: int = 8, hi: int = 8192) -> List[int]:
+    """Eight lengths uniform in [1, 8192]; seed 14 gives a ~32K-token total."""
+    return [int(x) for x in np.random.default_rng(seed).integers(1, hi + 1, n)]
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", (256,), H=2, D=64, dtype="f32", dense=True, zero_state=True),
+    "eqlen": Workload("eqlen", (4096,) * 2, H=16, D=128, dtype="bf16", dense=True),
+    "varlen": Workload("varlen", tuple(varlen_lengths()), H=32, D=128, dtype="bf16", dense=False),
+    "varlen_padded": Workload("varlen_padded", (4000,) * 8, H=32, D=128, dtype="bf16", dense=True),
+    "long": Workload("long", (65536,), H=8, D=128, dtype="bf16", dense=True, floor_channels=13),
+    "large": Workload("large", (8192,) * 16, H=64, D=128, dtype="bf16", dense=True),
+}
+
+
+def custom(lengths, H=2, D=128, dtype="bf16", dense=False, zero_state=False,
+           floor_channels=0, seed=0, name="custom") -> Workload:
+    return Workload(name, tuple(int(x) for x in lengths), H=H, D=D, dtype=dtype, dense=dense,
+                    zero_state=zero_state, floor_channels=floor_channels, seed=seed)
+
+
+def _torch_dtype(name: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def make_inputs(w: Workload, device="cpu", gate: Optional[str] = None) -> dict:
+    """Draw the inputs of workload ``w`` on ``device`` from a torch generator seeded
+    with ``w.seed``.  Returns a dict with q, k, v, g, beta, initial_state (or None),
+    cu_seqlens (int32, or None in dense layout) and lengths.
+
+    ``gate`` overrides the gate distribution for edge cases: "floor" sets every g
+    to -5, "zero" sets every g to 0.
+    """
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    N, H, D = w.n_seq, w.H, w.D
+    T_tot = w.tokens
+    dt = _torch_dtype(w.dtype)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    def unit_rows(x):
+        return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min(1e-30)
+
+    q = unit_rows(randn(T_tot, H, D)).to(dt)
+    k = unit_rows(randn(T_tot, H, D)).to(dt)
+    v = randn(T_tot, H, D).to(dt)
+    g = GATE_LOWER_BOUND * torch.sigmoid(randn(T_tot, H, D))
+    beta = torch.sigmoid(randn(T_tot, H))
+    if w.floor_channels:
+        for h in range(H):
+            ch = torch.randperm(D, generator=gen, device=dev)[: w.floor_channels]
+            g[:, h, ch] = GATE_LOWER_BOUND
+    if gate == "floor":
+        g.fill_(GATE_LOWER_BOUND)
+    elif gate == "zero":
+        g.zero_()
+    s0 = None if w.zero_state else 0.1 * randn(N, H, D, D)
+
+    out = {"lengths": list(w.lengths), "initial_state": s0}
+    if w.dense:
+        L = w.lengths[0]
+        assert all(x == L for x in w.lengths), "dense layout needs equal lengths"
+        out.update(q=q.view(N, L, H, D), k=k.view(N, L, H, D), v=v.view(N, L, H, D),
+                   g=g.view(N, L, H, D), beta=beta.view(N, L, H), cu_seqlens=None)
+    else:
+        cu = torch.zeros(N + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(w.lengths, dtype=torch.int64), 0).to(torch.int32)
+        out.update(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu.to(dev))
+    return out
+
+
+def to_packed(x: torch.Tensor) -> torch.Tensor:
+    """[B, T, ...] -> [B*T, ...] (a view change only)."""
+    return x.reshape(x.shape[0] * x.shape[1], *x.shape[2:])
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu
