@@ -1,0 +1,221 @@
+"""MI355X (gfx950) Kimi Delta Attention chunked prefill.
+
+A thin ctypes binding over ``libkda.so`` (C ABI in ``include/kda.h``): it only
+turns torch tensors into descriptors, allocates outputs/workspace with torch
+and passes the current HIP stream.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback.  Importing works without a GPU
+(so the ABI can be inspected on a CPU host), but every compute entry point
+raises if the library or a GPU is missing.
+
+Names follow the C ABI: ``prefill`` (kda_prefill / kda_prefill_ws),
+``workspace_size``, ``prep`` (kda_prep), ``profile_enable``/``profile_read``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_BF16, KDA_F32, KDA_I32 = 0, 1, 2
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_LAYOUT",
+          5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP"}
+EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prep",
+           "kda_release_cached_workspace", "kda_profile_enable", "kda_profile_read",
+           "kda_status_string", "kda_last_error", "kda_abi_version")
+
+
+class KdaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class KdaOptions(ctypes.Structure):
+    _fields_ = [("nseg", ctypes.c_int32), ("prep", ctypes.c_int32),
+                ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libkda.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m gated_delta_rule_38_amd.build`")
+    lib = ctypes.CDLL(path)
+    T = ctypes.POINTER(KdaTensor)
+    O = ctypes.POINTER(KdaOptions)
+    V = ctypes.c_void_p
+    lib.kda_prefill.argtypes = [T, T, T, T, T, T, T, T, T, V]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_ws.argtypes = [T, T, T, T, T, T, T, T, T, O, V, ctypes.c_size_t, V]
+    lib.kda_prefill_ws.restype = ctypes.c_int
+    lib.kda_prefill_workspace_size.argtypes = [T, T, T, T, T, T, T, T, T, O, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_prefill_workspace_size.restype = ctypes.c_int
+    lib.kda_prep.argtypes = [T, T, T, V]
+    lib.kda_prep.restype = ctypes.c_int
+    lib.kda_release_cached_workspace.argtypes = []
+    lib.kda_release_cached_workspace.restype = None
+    lib.kda_profile_enable.argtypes = [ctypes.c_int]
+    lib.kda_profile_enable.restype = None
+    lib.kda_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.kda_profile_read.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KdaError(status, load_library().kda_last_error().decode())
+
+
+def describe(t, dtype_code: Optional[int] = None) -> KdaTensor:
+    """A torch tensor as a kda_tensor_t (strides in elements)."""
+    import torch
+    d = KdaTensor()
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    code = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32, torch.int32: KDA_I32}.get(t.dtype)
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = code if dtype_code is None else dtype_code
+    if d.dtype is None:
+        d.dtype = -1
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(d: Optional[KdaTensor]):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state):
+    return [describe(q), describe(k), describe(v), describe(g), describe(beta),
+            describe(initial_state) if initial_state is not None else None,
+            describe(cu_seqlens) if cu_seqlens is not None else None,
+            describe(out), describe(final_state) if final_state is not None else None]
+
+
+def _require_gpu(*tensors):
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("gated_delta_rule_38_amd needs a ROCm GPU (gfx950); none is visible")
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0) -> KdaOptions:
+    o = KdaOptions()
+    o.nseg, o.prep = nseg, prep
+    o.stall_wave = stall_wave + 1 if stall_wave >= 0 else 0
+    o.stall_cycles = stall_cycles
+    return o
+
+
+def _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, want_final):
+    import torch
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    if final_state is None and want_final:
+        N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else q.shape[0]
+        H, D = q.shape[-2], q.shape[-1]
+        final_state = torch.empty((N, H, D, v.shape[-1]), dtype=torch.float32, device=q.device)
+    return out, final_state
+
+
+def workspace_size(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
+                   nseg: int = 0, prep: int = 0) -> int:
+    lib = load_library()
+    out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, False)
+    ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    n = ctypes.c_size_t(0)
+    _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(options(nseg, prep)),
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
+            output_final_state: bool = True, nseg: int = 0, prep: int = 0, stall_wave: int = -1,
+            stall_cycles: int = 0, workspace=None, stream=None) -> Tuple:
+    """KDA chunked prefill.  Returns (out, final_state).
+
+    Dense layout: q, k, g [B, T, H, K], v [B, T, H, V], beta [B, T, H].
+    Packed layout: q, k, g [T, H, K], v [T, H, V], beta [T, H] and int32
+    ``cu_seqlens`` [N + 1] on the GPU.  States are fp32 [N, H, K, V].
+    With the default knobs this calls ``kda_prefill`` (library-cached
+    workspace); any knob or a ``workspace`` tensor routes through
+    ``kda_prefill_ws`` with a torch-allocated workspace.
+    """
+    import torch
+    lib = load_library()
+    _require_gpu(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, output_final_state)
+    ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    plain = nseg == 0 and prep == 0 and stall_wave < 0 and workspace is None
+    if plain:
+        _check(lib.kda_prefill(*[_ptr(d) for d in ds], ctypes.c_void_p(st)))
+        return out, final_state
+    opts = options(nseg, prep, stall_wave, stall_cycles)
+    need = ctypes.c_size_t(0)
+    _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(need)))
+    if workspace is None and need.value:
+        workspace = torch.empty(need.value + 256, dtype=torch.uint8, device=q.device)
+    wptr, wbytes = None, 0
+    if workspace is not None:
+        base = workspace.data_ptr()
+        aligned = (base + 255) // 256 * 256
+        wptr, wbytes = aligned, workspace.numel() - (aligned - base)
+    _check(lib.kda_prefill_ws(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.c_void_p(wptr),
+                              ctypes.c_size_t(wbytes), ctypes.c_void_p(st)))
+    return out, final_state
+
+
+def prep(g, cu_seqlens=None, gamma=None, stream=None):
+    """Standalone PREP kernel: in-chunk (64-token) inclusive cumsum of g."""
+    import torch
+    lib = load_library()
+    _require_gpu(g, cu_seqlens, gamma)
+    if gamma is None:
+        gamma = torch.empty_like(g)
+    st = torch.cuda.current_stream(g.device).cuda_stream if stream is None else stream
+    dc = describe(cu_seqlens) if cu_seqlens is not None else None
+    _check(lib.kda_prep(ctypes.byref(describe(g)), _ptr(dc), ctypes.byref(describe(gamma)), ctypes.c_void_p(st)))
+    return gamma
+
+
+def profile_enable(on: bool = True) -> None:
+    load_library().kda_profile_enable(1 if on else 0)
+
+
+def profile_read(kernel: Optional[str] = None) -> Tuple[float, int]:
+    """(summed milliseconds, launches) of the library's kernels whose name
+    contains ``kernel`` since the last read; synchronises their events."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(load_library().kda_profile_read(kernel.encode() if kernel else None, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def release_cached_workspace() -> None:
+    load_library().kda_release_cached_workspace()

@@ -1,0 +1,568 @@
+// Host side of the KDA prefill C ABI (include/kda.h): descriptor validation,
+// the launch plan, workspace sizing/caching and kernel enqueueing.
+//
+// Plan (host-known values only, never a device read): chains = N * H.  When
+// chains fill the GPU's compute units one chunk-kernel workgroup runs each
+// chain start to end (one launch, no workspace).  When they do not, each chain
+// is cut into nseg segments and the path is PREP -> segment build (M, C) ->
+// COMBINE -> segment outputs, following the PREP / SEG / COMB pipeline of the
+// cudnn-frontend Hopper KDA prefill PR (#1056), whose launch selection picks
+// the segment count from the SM count and N*H; here the CU count of the device
+// plays that role.  The workspace is sized exactly for the plan and is empty
+// when nseg == 1 (that PR's review found segment buffers sized by N*H but never
+// used on the single-segment path).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status_t fail(kda_status_t st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kda_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+size_t elem_size(int32_t dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+Span span_of(const kda_tensor_t *t)
+{
+    Span s;
+    if (!t || !t->data) return s;
+    int64_t last = 0;
+    for (int d = 0; d < t->ndim; ++d) {
+        if (t->shape[d] == 0) return s;
+        last += (t->shape[d] - 1) * t->stride[d];
+    }
+    s.lo = (uintptr_t)t->data;
+    s.hi = s.lo + (uintptr_t)((last + 1) * (int64_t)elem_size(t->dtype));
+    return s;
+}
+
+bool overlaps(const Span &a, const Span &b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool same_view(const kda_tensor_t *a, const kda_tensor_t *b)
+{
+    if (a->data != b->data || a->ndim != b->ndim || a->dtype != b->dtype) return false;
+    for (int d = 0; d < a->ndim; ++d)
+        if (a->shape[d] != b->shape[d] || (a->shape[d] > 1 && a->stride[d] != b->stride[d])) return false;
+    return true;
+}
+
+int64_t numel(const kda_tensor_t *t)
+{
+    int64_t n = 1;
+    for (int d = 0; d < t->ndim; ++d) n *= t->shape[d];
+    return n;
+}
+
+// Strides of a token-major view as (batch, token, head) in elements.
+struct Tok {
+    int64_t sb = 0, st = 0, sh = 0;
+};
+
+struct Problem {
+    bool dense = true;
+    int64_t B = 0, T = 0, Ttot = 0, N = 0, H = 0, D = 0;
+    bool fp32 = false;
+    Tok q, k, v, g, beta, out;
+    int64_t s0_sn = 0, s0_sh = 0, s0_sr = 0, sT_sn = 0, sT_sh = 0, sT_sr = 0;
+    const kda_tensor_t *tq, *tk, *tv, *tg, *tb, *ts0, *tcu, *tout, *tsT;
+};
+
+kda_status_t check_basic(const kda_tensor_t *t, const char *name, bool allow_null)
+{
+    if (!t) return allow_null ? KDA_OK : fail(KDA_ERR_NULL, "%s descriptor is NULL", name);
+    if (t->ndim < 1 || t->ndim > 4) return fail(KDA_ERR_SHAPE, "%s: ndim %d not in 1..4", name, t->ndim);
+    for (int d = 0; d < t->ndim; ++d) {
+        if (t->shape[d] < 0) return fail(KDA_ERR_SHAPE, "%s: negative extent", name);
+        if (t->stride[d] < 0) return fail(KDA_ERR_LAYOUT, "%s: negative stride", name);
+    }
+    if (t->shape[t->ndim - 1] > 1 && t->stride[t->ndim - 1] != 1)
+        return fail(KDA_ERR_LAYOUT, "%s: last-dimension stride must be 1", name);
+    if (t->dtype != KDA_BF16 && t->dtype != KDA_F32 && t->dtype != KDA_I32)
+        return fail(KDA_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+    if (!t->data && numel(t) > 0) return fail(KDA_ERR_NULL, "%s: data pointer is NULL", name);
+    return KDA_OK;
+}
+
+// token-major tensor: dense [B, T, H, X] or packed [Ttot, H, X] / [1, Ttot, H, X];
+// beta drops the last dimension.
+kda_status_t tok_view(const kda_tensor_t *t, const char *name, const Problem &P, int64_t X, bool has_x, Tok &o)
+{
+    const int want = (P.dense ? 4 : 3) - (has_x ? 0 : 1);
+    int64_t sh[4], sd[4];
+    int nd = t->ndim;
+    for (int d = 0; d < nd; ++d) { sh[d] = t->shape[d]; sd[d] = t->stride[d]; }
+    if (!P.dense && nd == want + 1 && sh[0] == 1) {   // [1, Ttot, ...]
+        for (int d = 0; d + 1 < nd; ++d) { sh[d] = sh[d + 1]; sd[d] = sd[d + 1]; }
+        --nd;
+    }
+    if (nd != want) return fail(KDA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, want, t->ndim);
+    int i = 0;
+    if (P.dense) {
+        if (sh[0] != P.B) return fail(KDA_ERR_SHAPE, "%s: batch %lld != %lld", name, (long long)sh[0], (long long)P.B);
+        o.sb = sd[0];
+        i = 1;
+    }
+    if (sh[i] != (P.dense ? P.T : P.Ttot)) return fail(KDA_ERR_SHAPE, "%s: token extent mismatch", name);
+    o.st = sd[i];
+    if (sh[i + 1] != P.H) return fail(KDA_ERR_SHAPE, "%s: head extent mismatch", name);
+    o.sh = sd[i + 1];
+    if (has_x && sh[i + 2] != X) return fail(KDA_ERR_SHAPE, "%s: last extent %lld != %lld", name, (long long)sh[i + 2], (long long)X);
+    return KDA_OK;
+}
+
+kda_status_t state_view(const kda_tensor_t *t, const char *name, const Problem &P, int64_t &sn, int64_t &sh, int64_t &sr)
+{
+    if (t->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "%s must be fp32", name);
+    if (t->ndim != 4) return fail(KDA_ERR_SHAPE, "%s must be [N, H, K, V]", name);
+    if (t->shape[0] != P.N || t->shape[1] != P.H || t->shape[2] != P.D || t->shape[3] != P.D)
+        return fail(KDA_ERR_SHAPE, "%s: shape must be [%lld, %lld, %lld, %lld]", name, (long long)P.N,
+                    (long long)P.H, (long long)P.D, (long long)P.D);
+    sn = t->stride[0];
+    sh = t->stride[1];
+    sr = t->stride[2];
+    return KDA_OK;
+}
+
+kda_status_t validate(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v, const kda_tensor_t *g,
+                      const kda_tensor_t *beta, const kda_tensor_t *s0, const kda_tensor_t *cu,
+                      const kda_tensor_t *out, const kda_tensor_t *sT, Problem &P)
+{
+    kda_status_t st;
+    if ((st = check_basic(q, "q", false)) || (st = check_basic(k, "k", false)) || (st = check_basic(v, "v", false)) ||
+        (st = check_basic(g, "g", false)) || (st = check_basic(beta, "beta", false)) ||
+        (st = check_basic(out, "out", false)) || (st = check_basic(s0, "initial_state", true)) ||
+        (st = check_basic(cu, "cu_seqlens", true)) || (st = check_basic(sT, "final_state", true)))
+        return st;
+    P.tq = q; P.tk = k; P.tv = v; P.tg = g; P.tb = beta; P.ts0 = s0; P.tcu = cu; P.tout = out; P.tsT = sT;
+    if (q->dtype != KDA_BF16 && q->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "q must be bf16 or fp32");
+    if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
+        return fail(KDA_ERR_DTYPE, "q, k, v and out must share one dtype");
+    if (g->dtype != KDA_F32 || beta->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "g and beta must be fp32");
+    P.fp32 = q->dtype == KDA_F32;
+    P.dense = (cu == nullptr);
+    if (P.dense) {
+        if (q->ndim != 4) return fail(KDA_ERR_SHAPE, "dense q must be [B, T, H, K]");
+        P.B = q->shape[0];
+        P.T = q->shape[1];
+        P.N = P.B;
+        P.Ttot = P.B * P.T;
+        P.H = q->shape[2];
+        P.D = q->shape[3];
+    } else {
+        if (cu->dtype != KDA_I32) return fail(KDA_ERR_DTYPE, "cu_seqlens must be int32");
+        if (cu->ndim != 1 || cu->shape[0] < 1) return fail(KDA_ERR_SHAPE, "cu_seqlens must be [N + 1]");
+        P.N = cu->shape[0] - 1;
+        if (q->ndim == 4) {
+            if (q->shape[0] != 1) return fail(KDA_ERR_SHAPE, "packed 4-D q needs batch 1");
+            P.Ttot = q->shape[1]; P.H = q->shape[2]; P.D = q->shape[3];
+        } else if (q->ndim == 3) {
+            P.Ttot = q->shape[0]; P.H = q->shape[1]; P.D = q->shape[2];
+        } else {
+            return fail(KDA_ERR_SHAPE, "packed q must be [T, H, K] or [1, T, H, K]");
+        }
+        P.B = 1;
+        P.T = 0;
+    }
+    if (P.H < 1) return fail(KDA_ERR_SHAPE, "H must be >= 1");
+    if (P.D != 64 && P.D != 128) return fail(KDA_ERR_UNSUPPORTED, "head size %lld not in {64, 128}", (long long)P.D);
+    if (P.fp32 && P.D != 64) return fail(KDA_ERR_UNSUPPORTED, "the fp32 debug mode supports head size 64 only");
+    if (P.Ttot >= (int64_t)1 << 31 || P.N >= (int64_t)1 << 31 || P.N * P.H >= (int64_t)1 << 31)
+        return fail(KDA_ERR_SHAPE, "problem too large for 32-bit token indexing");
+    if ((st = tok_view(q, "q", P, P.D, true, P.q)) || (st = tok_view(k, "k", P, P.D, true, P.k)) ||
+        (st = tok_view(v, "v", P, P.D, true, P.v)) || (st = tok_view(g, "g", P, P.D, true, P.g)) ||
+        (st = tok_view(beta, "beta", P, 0, false, P.beta)) || (st = tok_view(out, "out", P, P.D, true, P.out)))
+        return st;
+    if (s0 && (st = state_view(s0, "initial_state", P, P.s0_sn, P.s0_sh, P.s0_sr))) return st;
+    if (sT && (st = state_view(sT, "final_state", P, P.sT_sn, P.sT_sh, P.sT_sr))) return st;
+    // vector widths: 4 consecutive channels per access, rows aligned to them
+    auto aligned = [&](const kda_tensor_t *t) {
+        if (!t || !t->data) return true;
+        const size_t es = elem_size(t->dtype), vec = 4 * es;
+        if ((uintptr_t)t->data % vec) return false;
+        for (int d = 0; d + 1 < t->ndim; ++d)
+            if (t->shape[d] > 1 && (t->stride[d] * es) % vec) return false;
+        return true;
+    };
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(g) || !aligned(out))
+        return fail(KDA_ERR_LAYOUT, "q, k, v, g, out need 4-element-aligned base addresses and strides");
+    // aliasing
+    const Span so = span_of(out);
+    const kda_tensor_t *ins[] = {q, k, v, g, beta, s0, cu};
+    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "cu_seqlens"};
+    for (int i = 0; i < 7; ++i)
+        if (ins[i] && overlaps(so, span_of(ins[i]))) return fail(KDA_ERR_ALIAS, "out overlaps %s", names[i]);
+    if (sT) {
+        const Span ss = span_of(sT);
+        if (overlaps(ss, so)) return fail(KDA_ERR_ALIAS, "final_state overlaps out");
+        for (int i = 0; i < 7; ++i) {
+            if (!ins[i]) continue;
+            if (i == 5 && same_view(sT, s0)) continue;   // exact in-place state update
+            if (overlaps(ss, span_of(ins[i]))) return fail(KDA_ERR_ALIAS, "final_state overlaps %s", names[i]);
+        }
+    }
+    return KDA_OK;
+}
+
+// ------------------------------------------------------------------ plan
+struct Plan {
+    int nseg = 1;
+    bool standalone_prep = false;
+    size_t off_gamma = 0, off_maps = 0, off_start = 0, bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    return cus;
+}
+
+kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
+{
+    const int64_t chains = P.N * P.H;
+    const int64_t max_chunks = P.dense ? (P.T + 63) / 64 : (P.Ttot + 63) / 64;
+    if (o && o->nseg > 0) {
+        if (o->nseg > 64) return fail(KDA_ERR_UNSUPPORTED, "nseg %d > 64", o->nseg);
+        pl.nseg = o->nseg;
+    } else {
+        const int cus = device_cus();
+        int64_t nseg = 1;
+        if (chains > 0 && chains < cus) {
+            nseg = std::min<int64_t>(cus / chains, 32);
+            nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, max_chunks / 4));   // >= ~4 chunks per segment
+        }
+        pl.nseg = (int)std::max<int64_t>(1, nseg);
+    }
+    const int prep = o ? o->prep : 0;
+    if (prep < 0 || prep > 2) return fail(KDA_ERR_UNSUPPORTED, "prep mode %d", prep);
+    pl.standalone_prep = prep == 1 || (prep == 0 && pl.nseg > 1);
+    size_t off = 0;
+    if (pl.standalone_prep) {
+        pl.off_gamma = off;
+        off += align256((size_t)P.Ttot * P.H * P.D * 4);
+    }
+    if (pl.nseg > 1) {
+        const size_t dd = (size_t)P.D * P.D * 4;
+        pl.off_maps = off;
+        off += align256((size_t)chains * pl.nseg * 2 * dd);
+        pl.off_start = off;
+        off += align256((size_t)chains * pl.nseg * dd);
+    }
+    pl.bytes = off;
+    return KDA_OK;
+}
+
+// ------------------------------------------------------------- profiling
+struct ProfRec {
+    const char *name;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+bool g_prof_on = false;
+
+template <typename F>
+hipError_t timed(const char *name, hipStream_t st, F &&launch)
+{
+    if (!g_prof_on) return launch();
+    ProfRec r{name, nullptr, nullptr};
+    hipError_t e;
+    if ((e = hipEventCreate(&r.a)) != hipSuccess) return e;
+    if ((e = hipEventCreate(&r.b)) != hipSuccess) return e;
+    if ((e = hipEventRecord(r.a, st)) != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(r.b, st)) != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back(r);
+    return hipSuccess;
+}
+
+// --------------------------------------------------------------- enqueue
+kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void *ws, size_t ws_bytes, hipStream_t st)
+{
+    if (ws_bytes < pl.bytes || (pl.bytes && !ws))
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.bytes);
+    if (pl.bytes && ((uintptr_t)ws % 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const int64_t chains = P.N * P.H;
+    if (chains == 0) return KDA_OK;
+    char *wsb = (char *)ws;
+
+    kda::ChunkParams cp{};
+    cp.q = P.tq->data; cp.k = P.tk->data; cp.v = P.tv->data;
+    cp.g = (const float *)P.tg->data; cp.beta = (const float *)P.tb->data;
+    cp.s0 = P.ts0 ? (const float *)P.ts0->data : nullptr;
+    cp.o = P.tout->data;
+    cp.sT = P.tsT ? (float *)P.tsT->data : nullptr;
+    cp.cu = P.tcu ? (const int32_t *)P.tcu->data : nullptr;
+    cp.q_sb = P.q.sb; cp.q_st = P.q.st; cp.q_sh = P.q.sh;
+    cp.k_sb = P.k.sb; cp.k_st = P.k.st; cp.k_sh = P.k.sh;
+    cp.v_sb = P.v.sb; cp.v_st = P.v.st; cp.v_sh = P.v.sh;
+    cp.g_sb = P.g.sb; cp.g_st = P.g.st; cp.g_sh = P.g.sh;
+    cp.b_sb = P.beta.sb; cp.b_st = P.beta.st; cp.b_sh = P.beta.sh;
+    cp.o_sb = P.out.sb; cp.o_st = P.out.st; cp.o_sh = P.out.sh;
+    cp.s0_sn = P.s0_sn; cp.s0_sh = P.s0_sh; cp.s0_sr = P.s0_sr;
+    cp.sT_sn = P.sT_sn; cp.sT_sh = P.sT_sh; cp.sT_sr = P.sT_sr;
+    cp.N = (int32_t)P.N; cp.H = (int32_t)P.H; cp.T = (int32_t)P.T;
+    cp.nseg = pl.nseg;
+    cp.g_is_gamma = 0;
+    cp.stall_wave = (o && o->stall_wave > 0) ? o->stall_wave - 1 : -1;
+    cp.stall_iters = (o && o->stall_cycles > 0) ? std::max(1, o->stall_cycles / 127) : 0;
+    const bool stall = cp.stall_wave >= 0 && cp.stall_iters > 0;
+    const int D = (int)P.D;
+    hipError_t e;
+
+    if (pl.standalone_prep) {
+        kda::PrepParams pp{};
+        float *gam = (float *)(wsb + pl.off_gamma);
+        pp.g = cp.g; pp.gamma = gam; pp.cu = cp.cu;
+        pp.g_sb = P.g.sb; pp.g_st = P.g.st; pp.g_sh = P.g.sh;
+        // workspace Gamma: contiguous [B*T or Ttot, H, D]
+        pp.y_st = P.H * P.D; pp.y_sh = P.D; pp.y_sb = P.dense ? P.T * P.H * P.D : 0;
+        pp.N = (int32_t)P.N; pp.H = (int32_t)P.H; pp.T = (int32_t)P.T; pp.D = D;
+        pp.chunks_per_seq = P.dense ? (int32_t)((P.T + 63) / 64) : 0;
+        const int64_t nvc = P.dense ? P.B * ((P.T + 63) / 64) : (P.Ttot + 63) / 64 + P.N;
+        if ((e = timed("kda_prep", st, [&] { return kda::launch_prep(pp, (int)nvc, st); })) != hipSuccess)
+            return hip_fail(e, "PREP launch");
+        cp.g = gam;
+        cp.g_sb = pp.y_sb; cp.g_st = pp.y_st; cp.g_sh = pp.y_sh;
+        cp.g_is_gamma = 1;
+    }
+    if (pl.nseg == 1) {
+        cp.role = kda::ROLE_OUT;
+        if ((e = timed("kda_chunk", st, [&] { return kda::launch_chunk(cp, D, P.fp32, (int)chains, stall, st); })) != hipSuccess)
+            return hip_fail(e, "chunk launch");
+        return KDA_OK;
+    }
+    cp.ws_maps = (float *)(wsb + pl.off_maps);
+    cp.ws_start = (const float *)(wsb + pl.off_start);
+    cp.role = kda::ROLE_SEG_M;   // the launch covers both M and C roles
+    if ((e = timed("kda_chunk_segbuild", st, [&] {
+             return kda::launch_chunk(cp, D, P.fp32, (int)(chains * pl.nseg * 2), stall, st);
+         })) != hipSuccess)
+        return hip_fail(e, "segment-build launch");
+    kda::CombineParams mp{};
+    mp.maps = cp.ws_maps; mp.start = (float *)(wsb + pl.off_start);
+    mp.s0 = cp.s0; mp.s0_sn = P.s0_sn; mp.s0_sh = P.s0_sh; mp.s0_sr = P.s0_sr;
+    mp.N = (int32_t)P.N; mp.H = (int32_t)P.H; mp.nseg = pl.nseg;
+    if ((e = timed("kda_combine", st, [&] { return kda::launch_combine(mp, D, (int)chains, st); })) != hipSuccess)
+        return hip_fail(e, "combine launch");
+    cp.role = kda::ROLE_SEG_OUT;
+    if ((e = timed("kda_chunk_segout", st, [&] {
+             return kda::launch_chunk(cp, D, P.fp32, (int)(chains * pl.nseg), stall, st);
+         })) != hipSuccess)
+        return hip_fail(e, "segment-output launch");
+    return KDA_OK;
+}
+
+// cached workspace of kda_prefill, per device
+std::mutex g_ws_mu;
+struct CachedWs {
+    void *p = nullptr;
+    size_t bytes = 0;
+};
+std::vector<CachedWs> g_ws;
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_prefill_workspace_size(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                                        const kda_tensor_t *g, const kda_tensor_t *beta,
+                                        const kda_tensor_t *initial_state, const kda_tensor_t *cu_seqlens,
+                                        const kda_tensor_t *out, const kda_tensor_t *final_state,
+                                        const kda_options_t *opts, size_t *bytes)
+{
+    if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
+    Problem P;
+    kda_status_t st = validate(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, P);
+    if (st) return st;
+    Plan pl;
+    if ((st = make_plan(P, opts, pl))) return st;
+    *bytes = pl.bytes;
+    return KDA_OK;
+}
+
+kda_status_t kda_prefill_ws(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                            const kda_tensor_t *g, const kda_tensor_t *beta, const kda_tensor_t *initial_state,
+                            const kda_tensor_t *cu_seqlens, kda_tensor_t *out, kda_tensor_t *final_state,
+                            const kda_options_t *opts, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Problem P;
+    kda_status_t st = validate(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, P);
+    if (st) return st;
+    Plan pl;
+    if ((st = make_plan(P, opts, pl))) return st;
+    return run(P, pl, opts, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v, const kda_tensor_t *g,
+                         const kda_tensor_t *beta, const kda_tensor_t *initial_state,
+                         const kda_tensor_t *cu_seqlens, kda_tensor_t *out, kda_tensor_t *final_state, void *stream)
+{
+    Problem P;
+    kda_status_t st = validate(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, P);
+    if (st) return st;
+    Plan pl;
+    if ((st = make_plan(P, nullptr, pl))) return st;
+    void *ws = nullptr;
+    if (pl.bytes) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+        CachedWs &c = g_ws[dev];
+        if (c.bytes < pl.bytes) {
+            if (c.p) {
+                if ((e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess) return hip_fail(e, "workspace sync");
+                hipFree(c.p);
+                c.p = nullptr;
+                c.bytes = 0;
+            }
+            if ((e = hipMalloc(&c.p, pl.bytes)) != hipSuccess) {
+                c.p = nullptr;
+                return fail(KDA_ERR_WORKSPACE, "hipMalloc(%zu): %s", pl.bytes, hipGetErrorString(e));
+            }
+            c.bytes = pl.bytes;
+        }
+        ws = c.p;
+    }
+    return run(P, pl, nullptr, ws, pl.bytes, (hipStream_t)stream);
+}
+
+kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, kda_tensor_t *gamma, void *stream)
+{
+    kda_status_t st;
+    if ((st = check_basic(g, "g", false)) || (st = check_basic(gamma, "gamma", false)) ||
+        (st = check_basic(cu_seqlens, "cu_seqlens", true)))
+        return st;
+    if (g->dtype != KDA_F32 || gamma->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "g and gamma must be fp32");
+    if (g->ndim != gamma->ndim) return fail(KDA_ERR_SHAPE, "gamma must have g's shape");
+    for (int d = 0; d < g->ndim; ++d)
+        if (g->shape[d] != gamma->shape[d]) return fail(KDA_ERR_SHAPE, "gamma must have g's shape");
+    if (overlaps(span_of(g), span_of(gamma))) return fail(KDA_ERR_ALIAS, "gamma overlaps g");
+    Problem P;
+    P.dense = cu_seqlens == nullptr;
+    if (P.dense) {
+        if (g->ndim != 4) return fail(KDA_ERR_SHAPE, "dense g must be [B, T, H, K]");
+        P.B = g->shape[0]; P.T = g->shape[1]; P.N = P.B; P.H = g->shape[2]; P.D = g->shape[3];
+        P.Ttot = P.B * P.T;
+    } else {
+        if (cu_seqlens->dtype != KDA_I32 || cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1)
+            return fail(KDA_ERR_SHAPE, "cu_seqlens must be int32 [N + 1]");
+        P.N = cu_seqlens->shape[0] - 1;
+        if (g->ndim == 4 && g->shape[0] == 1) { P.Ttot = g->shape[1]; P.H = g->shape[2]; P.D = g->shape[3]; }
+        else if (g->ndim == 3) { P.Ttot = g->shape[0]; P.H = g->shape[1]; P.D = g->shape[2]; }
+        else return fail(KDA_ERR_SHAPE, "packed g must be [T, H, K]");
+    }
+    if (P.D < 1 || P.D > 128) return fail(KDA_ERR_UNSUPPORTED, "PREP supports 1..128 channels");
+    Tok tg, ty;
+    if ((st = tok_view(g, "g", P, P.D, true, tg)) || (st = tok_view(gamma, "gamma", P, P.D, true, ty))) return st;
+    kda::PrepParams pp{};
+    pp.g = (const float *)g->data; pp.gamma = (float *)gamma->data;
+    pp.cu = cu_seqlens ? (const int32_t *)cu_seqlens->data : nullptr;
+    pp.g_sb = tg.sb; pp.g_st = tg.st; pp.g_sh = tg.sh;
+    pp.y_sb = ty.sb; pp.y_st = ty.st; pp.y_sh = ty.sh;
+    pp.N = (int32_t)P.N; pp.H = (int32_t)P.H; pp.T = (int32_t)P.T; pp.D = (int32_t)P.D;
+    pp.chunks_per_seq = P.dense ? (int32_t)((P.T + 63) / 64) : 0;
+    if (P.N == 0 || (P.dense && P.T == 0)) return KDA_OK;
+    const int64_t nvc = P.dense ? P.B * ((P.T + 63) / 64) : (P.Ttot + 63) / 64 + P.N;
+    hipError_t e = timed("kda_prep", (hipStream_t)stream, [&] { return kda::launch_prep(pp, (int)nvc, (hipStream_t)stream); });
+    return e == hipSuccess ? KDA_OK : hip_fail(e, "PREP launch");
+}
+
+void kda_release_cached_workspace(void)
+{
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (size_t d = 0; d < g_ws.size(); ++d) {
+        if (!g_ws[d].p) continue;
+        (void)hipSetDevice((int)d);
+        (void)hipDeviceSynchronize();
+        (void)hipFree(g_ws[d].p);
+        g_ws[d] = CachedWs{};
+    }
+    (void)hipSetDevice(cur);
+}
+
+void kda_profile_enable(int on) { g_prof_on = on != 0; }
+
+kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *launches)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    double tot = 0.0;
+    int64_t cnt = 0;
+    kda_status_t st = KDA_OK;
+    for (auto &r : g_prof) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == KDA_OK) st = hip_fail(e, "profile event");
+        if (!kernel || strstr(r.name, kernel)) {
+            tot += ms;
+            ++cnt;
+        }
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    g_prof.clear();
+    if (total_ms) *total_ms = tot;
+    if (launches) *launches = cnt;
+    return st;
+}
+
+const char *kda_status_string(kda_status_t s)
+{
+    switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_LAYOUT: return "KDA_ERR_LAYOUT";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_error(void) { return g_last_error.c_str(); }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// Device-side building blocks for the gfx950 KDA prefill kernels: element
+// types, MFMA wrappers, LDS fragment loaders and the kernel parameter blocks.
+//
+// Matrix-core conventions used by every kernel (CDNA3/CDNA4 wave64 MFMA):
+//   32x32 tiles  (v_mfma_f32_32x32x16_bf16, v_mfma_f32_32x32x2_f32)
+//       accumulator: lane l holds column l%32, register 4q+r holds row
+//       8q + 4(l/32) + r  (q = 0..3, r = 0..3).
+//   16x16 tiles  (v_mfma_f32_16x16x32_bf16, _16x16x16_bf16, _16x16x4_f32)
+//       accumulator: lane l holds column l%16, register r holds row 4(l/16) + r.
+//   Operands: lane l holds A[row = l%M][k in kset(l)] and B[k in kset(l)][col = l%N].
+// A contraction only needs A and B to agree on kset, so a kernel may pick any
+// k-assignment per lane group.  Two are used:
+//   * contiguous: kset = 8*(l/32) + 0..7 (32x32) -- one 16-byte LDS read;
+//   * acc-compatible: kset = {4g+0..3, 8+4g+0..3}, g = l/32, within each
+//     16-wide k step -- exactly the rows an accumulator lane already holds, so
+//     an fp32 accumulator converts in registers into the next MFMA's B operand
+//     (as itself) or A operand (as its transpose) with no LDS round trip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CHUNK = 64;     // tokens per chunk
+constexpr int SUB = 16;       // tokens per gate sub-block (factorisation reference span)
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---------------------------------------------------------------- element IO
+template <typename ET> struct Elem;
+template <> struct Elem<bf16> {
+    static __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+    static __device__ __forceinline__ bf16 from_f(float x) { return (bf16)x; }
+};
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float to_f(float x) { return x; }
+    static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+
+// 4 consecutive elements, loaded/stored as one 8-byte (bf16) or 16-byte (fp32) access.
+template <typename ET> struct Vec4;
+template <> struct Vec4<bf16> {
+    typedef uint2 raw;
+    static __device__ __forceinline__ raw load(const bf16 *p) { return *(const uint2 *)p; }
+    static __device__ __forceinline__ void store(bf16 *p, raw v) { *(uint2 *)p = v; }
+    static __device__ __forceinline__ void unpack(raw v, float *f) {
+        f[0] = __builtin_bit_cast(float, v.x << 16);
+        f[1] = __builtin_bit_cast(float, v.x & 0xffff0000u);
+        f[2] = __builtin_bit_cast(float, v.y << 16);
+        f[3] = __builtin_bit_cast(float, v.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ raw pack(const float *f) {
+        bf16x4 b;
+        b[0] = (bf16)f[0]; b[1] = (bf16)f[1]; b[2] = (bf16)f[2]; b[3] = (bf16)f[3];
+        return __builtin_bit_cast(uint2, b);
+    }
+    static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
+};
+template <> struct Vec4<float> {
+    typedef float4 raw;
+    static __device__ __forceinline__ raw load(const float *p) { return *(const float4 *)p; }
+    static __device__ __forceinline__ void store(float *p, raw v) { *(float4 *)p = v; }
+    static __device__ __forceinline__ void unpack(raw v, float *f) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+    static __device__ __forceinline__ raw pack(const float *f) { return make_float4(f[0], f[1], f[2], f[3]); }
+    static __device__ __forceinline__ raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
+// ------------------------------------------------------------- fragments
+// An 8-value operand fragment: for bf16 one MFMA (k = 16 / 32 wide), for fp32
+// eight MFMAs, MFMA m consuming value m of every lane.
+template <typename ET> struct Frag8;
+template <> struct Frag8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void set(const float *f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)f[e];
+    }
+    // 8 contiguous elements
+    __device__ __forceinline__ void load8(const bf16 *p) { v = *(const bf16x8 *)p; }
+    // elements p[0..3] then p2[0..3]
+    __device__ __forceinline__ void load44(const bf16 *p, const bf16 *p2) {
+        uint2 a = *(const uint2 *)p, b = *(const uint2 *)p2;
+        uint4 u = make_uint4(a.x, a.y, b.x, b.y);
+        v = __builtin_bit_cast(bf16x8, u);
+    }
+};
+template <> struct Frag8<float> {
+    float v[8];
+    __device__ __forceinline__ void set(const float *f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = f[e];
+    }
+    __device__ __forceinline__ void load8(const float *p) {
+        float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    __device__ __forceinline__ void load44(const float *p, const float *p2) {
+        float4 a = *(const float4 *)p, b = *(const float4 *)p2;
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+// C(32x32) += A(32 x 16) * B(16 x 32)
+__device__ __forceinline__ void mma32(f32x16 &c, const Frag8<bf16> &a, const Frag8<bf16> &b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16 &c, const Frag8<float> &a, const Frag8<float> &b) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[m], b.v[m], c, 0, 0, 0);
+}
+// C(16x16) += A(16 x 32) * B(32 x 16)
+__device__ __forceinline__ void mma16(f32x4 &c, const Frag8<bf16> &a, const Frag8<bf16> &b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4 &c, const Frag8<float> &a, const Frag8<float> &b) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[m], b.v[m], c, 0, 0, 0);
+}
+
+// 4-value fragments for 16x16 tiles with a 16-wide k (kset = 4*(l/16) + 0..3),
+// matching the 16x16 accumulator rows of a lane.
+template <typename ET> struct Frag4;
+template <> struct Frag4<bf16> {
+    s16x4 v;
+    __device__ __forceinline__ void set(const float *f) {
+        bf16x4 b;
+        b[0] = (bf16)f[0]; b[1] = (bf16)f[1]; b[2] = (bf16)f[2]; b[3] = (bf16)f[3];
+        v = __builtin_bit_cast(s16x4, b);
+    }
+    __device__ __forceinline__ void load4(const bf16 *p) { v = __builtin_bit_cast(s16x4, *(const uint2 *)p); }
+};
+template <> struct Frag4<float> {
+    float v[4];
+    __device__ __forceinline__ void set(const float *f) { v[0] = f[0]; v[1] = f[1]; v[2] = f[2]; v[3] = f[3]; }
+    __device__ __forceinline__ void load4(const float *p) {
+        float4 a = *(const float4 *)p;
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    }
+};
+__device__ __forceinline__ void mma16k16(f32x4 &c, const Frag4<bf16> &a, const Frag4<bf16> &b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16k16(f32x4 &c, const Frag4<float> &a, const Frag4<float> &b) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[m], b.v[m], c, 0, 0, 0);
+}
+
+// ------------------------------------------------------- kernel parameters
+// Roles of the chunk kernel.
+enum Role : int32_t {
+    ROLE_OUT = 0,      // one chain per workgroup: start state -> outputs + final state
+    ROLE_SEG_M = 1,    // segment operator M: V = 0, start state = I, no outputs
+    ROLE_SEG_C = 2,    // segment offset C: start state = 0, no outputs
+    ROLE_SEG_OUT = 3   // one segment: start state from workspace -> outputs (+ final state)
+};
+
+struct ChunkParams {
+    const void *q, *k, *v;     // ET
+    const float *g;            // raw log decays, or in-chunk cumsums (g_is_gamma)
+    const float *beta;
+    const float *s0;           // initial state or NULL
+    void *o;                   // ET
+    float *sT;                 // final state or NULL
+    const int32_t *cu;         // NULL: dense layout
+    float *ws_maps;            // [chain][seg][2][D][D] segment operators (M, C)
+    const float *ws_start;     // [chain][seg][D][D] segment start states
+    // strides in elements: batch, token, head
+    int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, g_sb, g_st, g_sh;
+    int64_t b_sb, b_st, b_sh, o_sb, o_st, o_sh;
+    int64_t s0_sn, s0_sh, s0_sr, sT_sn, sT_sh, sT_sr;   // state: sequence, head, row
+    int32_t N, H, T;           // T: tokens per sequence in the dense layout
+    int32_t nseg;
+    int32_t role;
+    int32_t g_is_gamma;
+    int32_t stall_wave;        // wave index to stall, or -1
+    int32_t stall_iters;       // s_sleep(127) repetitions per stall
+};
+
+struct PrepParams {
+    const float *g;
+    float *gamma;
+    const int32_t *cu;
+    int64_t g_sb, g_st, g_sh, y_sb, y_st, y_sh;
+    int32_t N, H, T, D;
+    int32_t chunks_per_seq;    // dense layout: ceil(T / 64); packed: unused
+};
+
+struct CombineParams {
+    const float *maps;         // [chain][seg][2][D][D]
+    float *start;              // [chain][seg][D][D]
+    const float *s0;
+    int64_t s0_sn, s0_sh, s0_sr;
+    int32_t N, H, nseg;
+};
+
+// Sequence n's token range in the dense ([B,T,...]) or packed (cu_seqlens) layout.
+__device__ __forceinline__ void seq_range(const int32_t *cu, int n, int T, int64_t &t0, int &len, int64_t &bofs_sel) {
+    if (cu) {
+        t0 = cu[n];
+        len = cu[n + 1] - cu[n];
+        bofs_sel = 0;
+    } else {
+        t0 = 0;
+        len = T;
+        bofs_sel = n;
+    }
+}
+
+}  // namespace kda

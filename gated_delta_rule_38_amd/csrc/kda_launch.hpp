@@ -1,0 +1,13 @@
+// Host-side launchers of the gfx950 KDA kernels (defined in the .hip files).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "kda_device.hpp"
+
+namespace kda {
+// CHUNK kernel, one workgroup per chain / segment (x2 for the segment-build roles).
+hipError_t launch_chunk(const ChunkParams &p, int D, bool fp32, int grid, bool stall, hipStream_t st);
+// PREP kernel over `nvc` virtual chunks x H heads.
+hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st);
+// COMBINE kernel over chains x D/32 value slabs.
+hipError_t launch_combine(const CombineParams &p, int D, int chains, hipStream_t st);
+}  // namespace kda

@@ -1,0 +1,73 @@
+// PREP kernel: the in-chunk inclusive cumulative sum of the log decays g.
+//
+// Chunks are 64 tokens and restart at every sequence start, so a chunk never
+// straddles two sequences -- the "gap-safe virtual chunk mapping" of the
+// cudnn-frontend Hopper KDA prefill PR (#1056, walkthrough).  Virtual chunk v
+// maps to (sequence n, chunk j of n) through the running count of
+// ceil(len_n / 64); the packed layout's grid is the host-known bound
+// ceil(T_tot / 64) + N and the surplus workgroups exit at once.  One thread per
+// key channel adds the chunk's g values in token order in fp32, the same
+// sequential order the chunk kernel's fused scan uses, so both produce the same
+// bits.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+__global__ __launch_bounds__(128) void prep_kernel(const PrepParams p)
+{
+    const int v = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, nt = blockDim.x;
+    __shared__ int s_scan[128];
+    __shared__ int s_found[2];
+    int n = -1, j = 0;
+    if (!p.cu) {
+        n = v / p.chunks_per_seq;
+        j = v % p.chunks_per_seq;
+        if (n >= p.N) return;
+    } else {
+        if (tid == 0) { s_found[0] = -1; s_found[1] = 0; }
+        __syncthreads();
+        int carry = 0;
+        for (int base = 0; base < p.N; base += nt) {
+            const int s = base + tid;
+            const int cnt = (s < p.N) ? (p.cu[s + 1] - p.cu[s] + CHUNK - 1) / CHUNK : 0;
+            s_scan[tid] = cnt;
+            __syncthreads();
+            for (int off = 1; off < nt; off <<= 1) {         // inclusive Hillis-Steele scan
+                const int add = (tid >= off) ? s_scan[tid - off] : 0;
+                __syncthreads();
+                s_scan[tid] += add;
+                __syncthreads();
+            }
+            const int incl = carry + s_scan[tid], excl = incl - cnt;
+            if (s < p.N && v >= excl && v < incl) { s_found[0] = s; s_found[1] = v - excl; }
+            carry += s_scan[nt - 1];
+            __syncthreads();
+        }
+        __syncthreads();
+        n = s_found[0];
+        j = s_found[1];
+        if (n < 0) return;
+    }
+    if (tid >= p.D) return;
+    int64_t t0, bsel;
+    int len;
+    seq_range(p.cu, n, p.T, t0, len, bsel);
+    const int tok0 = j * CHUNK, L = min(CHUNK, len - tok0);
+    const float *src = p.g + bsel * p.g_sb + h * p.g_sh + (t0 + tok0) * p.g_st + tid;
+    float *dst = p.gamma + bsel * p.y_sb + h * p.y_sh + (t0 + tok0) * p.y_st + tid;
+    float acc = 0.f;
+    for (int i = 0; i < L; ++i) {
+        acc = acc + src[(int64_t)i * p.g_st];
+        dst[(int64_t)i * p.y_st] = acc;
+    }
+}
+
+hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st)
+{
+    if (nvc <= 0 || p.H <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prep_kernel, dim3(nvc, p.H), dim3(128), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

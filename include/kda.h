@@ -1,0 +1,155 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention chunked prefill.
+ *
+ * The operation (the reading of the pages, which name the method but never
+ * print its equations; see the TensorRT-LLM KDA prefill fix PR #19826 and the
+ * cudnn-frontend Hopper KDA prefill PR #1056): for every sequence n and head h
+ * independently, over the sequence's tokens t in order,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * S is a d_k x d_v fp32 matrix (row = key channel, column = value channel),
+ * S_{-1} = initial_state (zeros when NULL) and final_state = S after the last
+ * token.  g is the per-token, per-channel natural-log decay; the kernels are
+ * guaranteed on g in [-5, 0] (the production gate_lower_bound of the
+ * cudnn-frontend PR's correctness section) -- values below -5 may overflow
+ * the in-chunk gate factorisation.  beta is the value in (0, 1) (no sigmoid
+ * is applied).  No scale is applied to q.  The kernels compute the 64-token
+ * chunked WY/UT form of this recurrence (TensorRT-LLM PR #19960 names the
+ * "WY-form chunk"; "v64" in the cudnn-frontend kernel name gives the chunk).
+ *
+ * Tensors (all pointers are DEVICE memory owned by the caller; the library
+ * never frees or retains them):
+ *   dense  (cu_seqlens == NULL): q, k, g [B, T, H, K]; v, out [B, T, H, V];
+ *                                beta [B, T, H]; states [B, H, K, V]
+ *   packed (cu_seqlens != NULL): q, k, g [T_tot, H, K] (or 4-D with B == 1);
+ *                                v, out [T_tot, H, V]; beta [T_tot, H];
+ *                                cu_seqlens int32 [N + 1] with cu[0] = 0,
+ *                                non-decreasing, cu[N] = T_tot (device memory,
+ *                                NOT checked on the host); states [N, H, K, V]
+ *   K == V, K in {64, 128}; H >= 1; T >= 0; zero-length sequences allowed
+ *   (no output rows; final_state == initial_state bit for bit).
+ * Dtypes: q, k, v, out all KDA_BF16, or all KDA_F32 (the fp32 debug mode,
+ *   K == 64 only); g, beta, initial_state, final_state KDA_F32.
+ * Strides are in ELEMENTS; every tensor needs a unit last-dimension stride and
+ *   all other strides are honoured (row-padded views give the same bits as
+ *   contiguous tensors).
+ * Aliasing: out may not overlap any input; final_state may be exactly
+ *   initial_state (in-place update) but may not partially overlap it.
+ *
+ * Errors: every check runs on the host before anything is enqueued.  On any
+ * error nothing is launched, outputs are untouched and kda_last_error() holds
+ * a thread-local message.  KDA_ERR_HIP reports a HIP runtime failure (the
+ * message carries hipGetErrorString).
+ *
+ * Asynchrony: calls enqueue on `stream` (a hipStream_t; NULL is the null
+ * stream) and return without synchronising or reading device data back.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer or descriptor is NULL            */
+    KDA_ERR_SHAPE = 2,       /* rank / extent mismatch or unsupported head size     */
+    KDA_ERR_DTYPE = 3,       /* dtype not allowed for that argument                 */
+    KDA_ERR_LAYOUT = 4,      /* last-dimension stride != 1 or negative stride       */
+    KDA_ERR_ALIAS = 5,       /* forbidden overlap between outputs and inputs        */
+    KDA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement         */
+    KDA_ERR_WORKSPACE = 7,   /* workspace too small or allocation failed            */
+    KDA_ERR_HIP = 8          /* HIP runtime error while enqueueing                  */
+} kda_status_t;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1, KDA_I32 = 2 } kda_dtype_t;
+
+/* A strided view of device memory.  shape/stride entries past ndim are ignored;
+ * strides count elements, not bytes. */
+typedef struct {
+    void *data;
+    int32_t dtype; /* kda_dtype_t */
+    int32_t ndim;
+    int64_t shape[4];
+    int64_t stride[4];
+} kda_tensor_t;
+
+/* Planner and test knobs.  A zero-filled struct (or NULL) means "automatic". */
+typedef struct {
+    int32_t nseg;          /* segments per (sequence, head) chain; 0 = planner's choice, 1..64 forces */
+    int32_t prep;          /* 0 = planner; 1 = standalone PREP kernel; 2 = in-chunk (fused) gate scan */
+    int32_t stall_wave;    /* test hook: -1/0 = none; w+1 stalls wave w at every LDS hand-off        */
+    int32_t stall_cycles;  /* length of each injected stall, in s_sleep units of 64 cycles           */
+} kda_options_t;
+
+/*
+ * kda_prefill -- the KDA chunked prefill with a library-cached workspace.
+ * q, k, v, g, beta: inputs as above.  initial_state: NULL for zeros.
+ * cu_seqlens: NULL for the dense layout.  out: written for every valid token.
+ * final_state: NULL to skip.  stream: hipStream_t.
+ * Uses (and grows on demand) a per-device workspace cached by the library; the
+ * first call for a new size may call hipMalloc, so this entry point is not
+ * meant for graph capture -- use kda_prefill_ws there.
+ */
+kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                         const kda_tensor_t *g, const kda_tensor_t *beta,
+                         const kda_tensor_t *initial_state, const kda_tensor_t *cu_seqlens,
+                         kda_tensor_t *out, kda_tensor_t *final_state, void *stream);
+
+/* Bytes of device workspace kda_prefill_ws needs for these descriptors and
+ * options (0 when the plan is a single chunk-kernel launch). */
+kda_status_t kda_prefill_workspace_size(const kda_tensor_t *q, const kda_tensor_t *k,
+                                        const kda_tensor_t *v, const kda_tensor_t *g,
+                                        const kda_tensor_t *beta,
+                                        const kda_tensor_t *initial_state,
+                                        const kda_tensor_t *cu_seqlens, const kda_tensor_t *out,
+                                        const kda_tensor_t *final_state,
+                                        const kda_options_t *opts, size_t *bytes);
+
+/* kda_prefill with options and a caller-owned device workspace of at least
+ * kda_prefill_workspace_size() bytes (256-byte aligned).  Allocates nothing and
+ * never synchronises, so it can be captured into a HIP graph. */
+kda_status_t kda_prefill_ws(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                            const kda_tensor_t *g, const kda_tensor_t *beta,
+                            const kda_tensor_t *initial_state, const kda_tensor_t *cu_seqlens,
+                            kda_tensor_t *out, kda_tensor_t *final_state,
+                            const kda_options_t *opts, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * kda_prep -- the standalone PREP kernel: the in-chunk inclusive cumulative sum
+ * of g over 64-token chunks that restart at every sequence start (the
+ * "gap-safe virtual chunk mapping" of the cudnn-frontend PR's walkthrough: a
+ * chunk never straddles two sequences).  gamma has g's shape and dtype (fp32),
+ * must not overlap g, and receives for token t of chunk [t0, t0 + L):
+ *     gamma[t] = (((g[t0] + g[t0+1]) + ...) + g[t])   (fp32 adds in token order).
+ */
+kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, kda_tensor_t *gamma,
+                      void *stream);
+
+/* Frees the workspace cached by kda_prefill on every device. */
+void kda_release_cached_workspace(void);
+
+/* Kernel timing for measurement: when enabled, every kernel the library
+ * enqueues is bracketed by hipEvents on its stream.  kda_profile_read()
+ * synchronises those events, returns the summed milliseconds and launch count
+ * of kernels whose name contains `kernel` (e.g. "chunk"), and clears them. */
+void kda_profile_enable(int on);
+kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *launches);
+
+const char *kda_status_string(kda_status_t status);
+const char *kda_last_error(void);
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

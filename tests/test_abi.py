@@ -1,0 +1,191 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, and the host-side validator returns the documented
+status codes (nothing is launched on an error, so these run on any host).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_38_amd as kda
+from gated_delta_rule_38_amd import KdaTensor, KDA_BF16, KDA_F32, KDA_I32
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_38_amd import build
+        build.build(verbose=False)
+    return kda.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(kda.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(5) == b"KDA_ERR_ALIAS"
+    assert lib.kda_status_string(8) == b"KDA_ERR_HIP"
+
+
+FAKE = 1 << 40   # a non-NULL, 256-aligned address; never dereferenced on the error paths
+
+
+def desc(shape, dtype=KDA_BF16, base=FAKE, strides=None):
+    d = KdaTensor()
+    d.data = base
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def packed_set(T=100, H=2, D=128, N=3, dt=KDA_BF16):
+    gap = 1 << 32
+    return dict(q=desc([T, H, D], dt, FAKE), k=desc([T, H, D], dt, FAKE + gap),
+                v=desc([T, H, D], dt, FAKE + 2 * gap), g=desc([T, H, D], KDA_F32, FAKE + 3 * gap),
+                beta=desc([T, H], KDA_F32, FAKE + 4 * gap), s0=desc([N, H, D, D], KDA_F32, FAKE + 5 * gap),
+                cu=desc([N + 1], KDA_I32, FAKE + 6 * gap), out=desc([T, H, D], dt, FAKE + 7 * gap),
+                sT=desc([N, H, D, D], KDA_F32, FAKE + 8 * gap))
+
+
+def call_prefill(lib, s):
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    return lib.kda_prefill(r(s["q"]), r(s["k"]), r(s["v"]), r(s["g"]), r(s["beta"]), r(s["s0"]),
+                           r(s["cu"]), r(s["out"]), r(s["sT"]), None)
+
+
+def test_null_descriptor(lib):
+    s = packed_set()
+    s["q"] = None
+    assert call_prefill(lib, s) == 1
+    assert b"q" in lib.kda_last_error()
+
+
+def test_dtype_mismatch(lib):
+    s = packed_set()
+    s["k"] = desc([100, 2, 128], KDA_F32, s["k"].data)
+    assert call_prefill(lib, s) == 3
+    s = packed_set()
+    s["g"] = desc([100, 2, 128], KDA_BF16, s["g"].data)
+    assert call_prefill(lib, s) == 3
+    s = packed_set()
+    s["cu"] = desc([4], KDA_F32, s["cu"].data)
+    assert call_prefill(lib, s) == 3
+
+
+def test_shape_errors(lib):
+    s = packed_set()
+    s["v"] = desc([100, 2, 64], KDA_BF16, s["v"].data)
+    assert call_prefill(lib, s) == 2
+    s = packed_set()
+    s["beta"] = desc([99, 2], KDA_F32, s["beta"].data)
+    assert call_prefill(lib, s) == 2
+    s = packed_set()
+    s["s0"] = desc([2, 2, 128, 128], KDA_F32, s["s0"].data)   # N mismatch
+    assert call_prefill(lib, s) == 2
+
+
+def test_unsupported_head_size_and_fp32_d128(lib):
+    s = packed_set(D=96)
+    assert call_prefill(lib, s) == 6
+    s = packed_set(D=128, dt=KDA_F32)
+    assert call_prefill(lib, s) == 6
+
+
+def test_layout_errors(lib):
+    s = packed_set()
+    s["q"] = desc([100, 2, 128], KDA_BF16, s["q"].data, strides=[256, 128, 2])
+    assert call_prefill(lib, s) == 4
+    s = packed_set()
+    s["q"] = desc([100, 2, 128], KDA_BF16, s["q"].data, strides=[256, 129, 1])   # misaligned rows
+    assert call_prefill(lib, s) == 4
+
+
+def test_alias_errors(lib):
+    s = packed_set()
+    s["out"] = desc([100, 2, 128], KDA_BF16, s["v"].data + 64)   # overlaps v
+    assert call_prefill(lib, s) == 5
+    s = packed_set()
+    s["sT"] = desc([3, 2, 128, 128], KDA_F32, s["s0"].data + 1024)   # partial overlap
+    assert call_prefill(lib, s) == 5
+
+
+def test_row_padded_views_validate(lib):
+    """Row-padded strides (the cudnn-frontend review's [33, 2, 256][..., :128]
+    probe) are legal; the workspace query walks the whole validator + planner."""
+    s = packed_set(T=33, H=2, D=128, N=3)
+    s["q"] = desc([33, 2, 128], KDA_BF16, s["q"].data, strides=[512, 256, 1])
+    s["s0"] = desc([3, 2, 128, 128], KDA_F32, s["s0"].data, strides=[2 * 128 * 256, 128 * 256, 256, 1])
+    r = lambda d: ctypes.byref(d)
+    n = ctypes.c_size_t(7)
+    opts = kda.options(nseg=1)
+    st = lib.kda_prefill_workspace_size(r(s["q"]), r(s["k"]), r(s["v"]), r(s["g"]), r(s["beta"]), r(s["s0"]),
+                                        r(s["cu"]), r(s["out"]), r(s["sT"]), ctypes.byref(opts), ctypes.byref(n))
+    assert st == 0, lib.kda_last_error()
+    assert n.value == 0
+
+
+def test_in_place_state_allowed(lib):
+    s = packed_set()
+    s["sT"] = desc([3, 2, 128, 128], KDA_F32, s["s0"].data)
+    r = lambda d: ctypes.byref(d)
+    n = ctypes.c_size_t(0)
+    opts = kda.options(nseg=1)
+    st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                        ctypes.byref(opts), ctypes.byref(n))
+    assert st == 0, lib.kda_last_error()
+
+
+def test_workspace_size_of_segmented_plan(lib):
+    """Forced nseg = 8 on B=2, H=16, T=4096, d=128: Gamma (fp32, one per
+    token-head-channel) + (M, C) per segment + start state per segment."""
+    B, T, H, D = 2, 4096, 16, 128
+    gap = 1 << 34
+    s = dict(q=desc([B, T, H, D]), k=desc([B, T, H, D], base=FAKE + gap), v=desc([B, T, H, D], base=FAKE + 2 * gap),
+             g=desc([B, T, H, D], KDA_F32, FAKE + 3 * gap), beta=desc([B, T, H], KDA_F32, FAKE + 4 * gap),
+             s0=None, cu=None, out=desc([B, T, H, D], base=FAKE + 5 * gap), sT=None)
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    n = ctypes.c_size_t(0)
+    opts = kda.options(nseg=8)
+    st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                        ctypes.byref(opts), ctypes.byref(n))
+    assert st == 0, lib.kda_last_error()
+    chains, dd = B * H, D * D * 4
+    want = B * T * H * D * 4 + chains * 8 * 2 * dd + chains * 8 * dd
+    assert n.value == want
+    opts = kda.options(nseg=1, prep=2)
+    st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                        ctypes.byref(opts), ctypes.byref(n))
+    assert st == 0 and n.value == 0     # single segment with the in-chunk scan: no workspace
+
+
+def test_python_binding_refuses_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    x = torch.zeros(4, 1, 64)
+    with pytest.raises(RuntimeError):
+        kda.prefill(x, x, x, x, torch.zeros(4, 1), cu_seqlens=torch.tensor([0, 4], dtype=torch.int32))

@@ -1,0 +1,336 @@
+"""GPU parity of the HIP KDA prefill (called through the C ABI) against the
+float64 oracle, plus the bit-stability properties the pages ask for.
+
+Tolerances (whole-tensor relative L2, outputs and final states separately):
+5e-3 with bf16 q/k/v, 1e-4 in the fp32 debug mode.  Small cases compare every
+element with the oracle; the full-size workloads compare every element of a
+seeded sample of (sequence, head) chains that the oracle runs one by one, in
+the same launch configuration the bench times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 5e-3, "f32": 1e-4}
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_38_amd as k
+    k.load_library()
+    return k
+
+
+def gen(w, gate=None):
+    return workloads.make_inputs(w, device="cuda", gate=gate)
+
+
+def run(kda, x, **kw):
+    return kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"], **kw)
+
+
+def chain_slice(x, n, h):
+    """Host float64-ready copies of chain (n, h)'s inputs, packed [L, 1, D]."""
+    if x["cu_seqlens"] is None:
+        sel = lambda t: t[n, :, h:h + 1]
+        bsel = lambda t: t[n, :, h:h + 1]
+    else:
+        cu = x["cu_seqlens"].cpu()
+        a, b = int(cu[n]), int(cu[n + 1])
+        sel = lambda t: t[a:b, h:h + 1]
+        bsel = sel
+    s0 = None if x["initial_state"] is None else x["initial_state"][n:n + 1, h:h + 1].cpu()
+    return (sel(x["q"]).cpu(), sel(x["k"]).cpu(), sel(x["v"]).cpu(), sel(x["g"]).cpu(), bsel(x["beta"]).cpu(), s0)
+
+
+def out_slice(x, out, n, h):
+    if x["cu_seqlens"] is None:
+        return out[n, :, h:h + 1]
+    cu = x["cu_seqlens"].cpu()
+    return out[int(cu[n]):int(cu[n + 1]), h:h + 1]
+
+
+def check_chains(x, out, sT, chains, tol):
+    worst = 0.0
+    for n, h in chains:
+        q, k, v, g, b, s0 = chain_slice(x, n, h)
+        L = q.shape[0]
+        o_ref, s_ref = oracle.run_c(q, k, v, g, b, s0, np.array([0, L]))
+        o_gpu = out_slice(x, out, n, h).float().cpu().numpy().reshape(o_ref.shape)
+        s_gpu = sT[n:n + 1, h:h + 1].cpu().numpy()
+        assert np.isfinite(o_gpu).all() and np.isfinite(s_gpu).all(), (n, h)
+        eo = oracle.rel_l2(o_gpu, o_ref) if L else 0.0
+        es = oracle.rel_l2(s_gpu, s_ref)
+        worst = max(worst, eo, es)
+        assert eo <= tol and es <= tol, f"chain {(n, h)}: rel-L2 out {eo:.3e} state {es:.3e}"
+    return worst
+
+
+def check_full(x, out, sT, tol):
+    o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["g"].cpu(), x["beta"].cpu(),
+                                None if x["initial_state"] is None else x["initial_state"].cpu(),
+                                None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu())
+    o_gpu = out.float().cpu().numpy().reshape(o_ref.shape)
+    s_gpu = sT.cpu().numpy()
+    assert np.isfinite(o_gpu).all() and np.isfinite(s_gpu).all()
+    eo, es = oracle.rel_l2(o_gpu, o_ref), oracle.rel_l2(s_gpu, s_ref)
+    assert eo <= tol and es <= tol, f"rel-L2 out {eo:.3e} state {es:.3e}"
+    return eo, es
+
+
+# ------------------------------------------------------------ parity ----
+
+def test_tiny_fp32_debug_mode(kda):
+    w = workloads.WORKLOADS["tiny"]
+    say("tiny fp32", w.describe())
+    x = gen(w)
+    out, sT = run(kda, x)
+    eo, es = check_full(x, out, sT, TOL["f32"])
+    say(f"tiny rel-L2 out {eo:.2e} state {es:.2e}")
+
+
+EDGE = [
+    ([17, 0, 16], 2, 128), ([1025, 0, 31], 2, 128), ([1024], 4, 128), ([1], 2, 128), ([64], 2, 128),
+    ([63, 65, 128, 1, 0], 3, 128), ([300, 5], 2, 64), ([0], 2, 128), ([0, 0], 1, 64),
+]
+
+
+@pytest.mark.parametrize("lengths,H,D", EDGE)
+def test_edge_shapes_bf16(kda, lengths, H, D):
+    w = workloads.custom(lengths, H=H, D=D, dtype="bf16", dense=False, seed=3)
+    say("edge", lengths, H, D)
+    x = gen(w)
+    out, sT = run(kda, x)
+    check_full(x, out, sT, TOL["bf16"])
+
+
+@pytest.mark.parametrize("lengths,H", [([130, 7], 2), ([64, 1, 200], 1)])
+def test_edge_shapes_fp32(kda, lengths, H):
+    w = workloads.custom(lengths, H=H, D=64, dtype="f32", dense=False, seed=4)
+    say("edge fp32", lengths, H)
+    x = gen(w)
+    out, sT = run(kda, x)
+    check_full(x, out, sT, TOL["f32"])
+
+
+def test_zero_length_keeps_initial_state_bits(kda):
+    w = workloads.custom([0, 40, 0], H=2, D=128, seed=5)
+    x = gen(w)
+    out, sT = run(kda, x)
+    s0 = x["initial_state"]
+    assert torch_equal(sT[0], s0[0]) and torch_equal(sT[2], s0[2])
+
+
+@pytest.mark.parametrize("gate", ["floor", "zero"])
+def test_gate_extremes(kda, gate):
+    """Every g at the -5 floor (a chunk-wide exp(-Gamma) would overflow) and g = 0."""
+    w = workloads.custom([200, 64, 33], H=2, D=128, seed=6)
+    say("gate", gate)
+    x = gen(w, gate=gate)
+    out, sT = run(kda, x)
+    check_full(x, out, sT, TOL["bf16"])
+
+
+def _sample(w, count, seed=0):
+    rng = np.random.default_rng(seed)
+    chains = {(w.n_seq - 1, w.H - 1), (0, 0)}
+    while len(chains) < count:
+        chains.add((int(rng.integers(w.n_seq)), int(rng.integers(w.H))))
+    return sorted(chains)
+
+
+@pytest.mark.parametrize("name,count", [("eqlen", 6), ("varlen", 6), ("varlen_padded", 4), ("long", 1),
+                                        ("large", 3)])
+def test_workload_sampled_chains(kda, name, count):
+    import torch
+    w = workloads.WORKLOADS[name]
+    say("workload", w.describe())
+    x = gen(w)
+    out, sT = run(kda, x)
+    torch.cuda.synchronize()
+    worst = check_chains(x, out, sT, _sample(w, count), TOL[w.dtype])
+    say(f"{name}: worst sampled rel-L2 {worst:.2e}")
+    del x, out, sT
+    torch.cuda.empty_cache()
+
+
+# -------------------------------------------------- bit-stability ----
+
+def torch_equal(a, b):
+    import torch
+    return bool(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)))
+
+
+def test_repeat_runs_bitwise(kda):
+    w = workloads.custom([1000, 64, 300], H=4, D=128, seed=7)
+    x = gen(w)
+    o0, s0 = run(kda, x)
+    for _ in range(9):
+        o1, s1 = run(kda, x)
+        assert torch_equal(o0, o1) and torch_equal(s0, s1)
+
+
+@pytest.mark.parametrize("layout", ["padded_eqlen", "varlen"])
+@pytest.mark.parametrize("wave", [0, 1, 2, 3])
+def test_stalled_wave_gives_same_bits(kda, layout, wave):
+    """A copy of the kernel with one wave stalled ~20 us after every barrier must
+    reproduce the unstalled bits (the warp-timing test of TensorRT-LLM PR #19826)."""
+    if layout == "padded_eqlen":
+        w = workloads.custom([200] * 3, H=2, D=128, dense=True, seed=8)
+    else:
+        w = workloads.custom([130, 1, 77, 64], H=2, D=128, seed=8)
+    x = gen(w)
+    say("stall", layout, "wave", wave)
+    o0, s0 = run(kda, x, nseg=1)
+    o1, s1 = run(kda, x, nseg=1, stall_wave=wave, stall_cycles=127 * 6)
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+    o2, s2 = run(kda, x, nseg=3)
+    o3, s3 = run(kda, x, nseg=3, stall_wave=wave, stall_cycles=127 * 6)
+    assert torch_equal(o2, o3) and torch_equal(s2, s3)
+
+
+def test_poisoned_outputs_and_workspace(kda):
+    import torch
+    w = workloads.custom([333, 64, 5], H=3, D=128, seed=9)
+    x = gen(w)
+    o0, s0 = run(kda, x, nseg=2)
+    out = torch.full_like(o0, float("nan"))
+    fin = torch.full_like(s0, float("nan"))
+    ws_bytes = kda.workspace_size(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"],
+                                  nseg=2)
+    ws = torch.full((ws_bytes // 4 + 64,), float("nan"), device="cuda")
+    o1, s1 = run(kda, x, out=out, final_state=fin, nseg=2, workspace=ws.view(torch.uint8))
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+
+
+def test_row_padded_views_same_bits(kda):
+    """Q backed by [T, H, 256] viewed [..., :128] and the initial state with row
+    stride 256 (the strided probe of the cudnn-frontend PR review)."""
+    import torch
+    w = workloads.custom([17, 0, 16], H=2, D=128, seed=10)
+    x = gen(w)
+    o0, s0 = run(kda, x)
+    qb = torch.zeros(x["q"].shape[0], 2, 256, dtype=x["q"].dtype, device="cuda")
+    qb[..., :128] = x["q"]
+    sb = torch.zeros(3, 2, 128, 256, device="cuda")
+    sb[..., :128] = x["initial_state"]
+    y = dict(x, q=qb[..., :128], initial_state=sb[..., :128])
+    o1, s1 = run(kda, y)
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+
+
+def test_dense_equals_packed(kda):
+    w = workloads.custom([200] * 3, H=2, D=128, dense=True, seed=11)
+    x = gen(w)
+    o0, s0 = run(kda, x)
+    y = {kk: (workloads.to_packed(t) if kk in ("q", "k", "v", "g", "beta") else t) for kk, t in x.items()}
+    import torch
+    y["cu_seqlens"] = torch.tensor([0, 200, 400, 600], dtype=torch.int32, device="cuda")
+    o1, s1 = run(kda, y)
+    assert torch_equal(workloads.to_packed(o0), o1) and torch_equal(s0, s1)
+
+
+@pytest.mark.parametrize("nseg", [1, 2, 4, 8])
+def test_forced_segments_match_oracle(kda, nseg):
+    w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=12)
+    x = gen(w)
+    say("nseg", nseg)
+    out, sT = run(kda, x, nseg=nseg)
+    check_full(x, out, sT, TOL["bf16"])
+
+
+def test_standalone_prep_equals_fused_scan(kda):
+    w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=13)
+    x = gen(w)
+    o1, s1 = run(kda, x, nseg=1, prep=1)
+    o2, s2 = run(kda, x, nseg=1, prep=2)
+    assert torch_equal(o1, o2) and torch_equal(s1, s2)
+
+
+def test_in_place_state(kda):
+    import torch
+    w = workloads.custom([150, 20], H=2, D=128, seed=14)
+    x = gen(w)
+    o0, s0 = run(kda, x)
+    st = x["initial_state"].clone()
+    y = dict(x, initial_state=st)
+    o1, s1 = run(kda, y, final_state=st)
+    assert s1.data_ptr() == st.data_ptr()
+    assert torch_equal(o0, o1) and torch_equal(s0, st)
+
+
+@pytest.mark.parametrize("dense", [True, False])
+def test_prep_kernel_bit_exact(kda, dense):
+    """PREP output equals a float32 sequential cumsum restarted every 64 tokens
+    of every sequence."""
+    import torch
+    if dense:
+        w = workloads.custom([130] * 2, H=3, D=128, dense=True, seed=15)
+    else:
+        w = workloads.custom([130, 0, 64, 1, 65], H=3, D=128, seed=15)
+    x = gen(w)
+    gam = kda.prep(x["g"], x["cu_seqlens"])
+    g = x["g"].cpu().numpy()
+    got = gam.cpu().numpy()
+    if dense:
+        g = g.reshape(-1, *g.shape[2:])
+        got = got.reshape(-1, *got.shape[2:])
+        cu = np.arange(3) * 130
+    else:
+        cu = x["cu_seqlens"].cpu().numpy()
+    want = np.zeros_like(g)
+    for n in range(len(cu) - 1):
+        for c0 in range(cu[n], cu[n + 1], 64):
+            acc = np.zeros(g.shape[1:], dtype=np.float32)
+            for t in range(c0, min(c0 + 64, cu[n + 1])):
+                acc = (acc + g[t]).astype(np.float32)
+                want[t] = acc
+    assert np.array_equal(want.view(np.int32), got.view(np.int32))
+
+
+def test_graph_replay_with_changed_q(kda):
+    """kda_prefill_ws captured in a HIP graph; q changes between replays and
+    each replay must equal a fresh eager call bit for bit."""
+    import torch
+    w = workloads.custom([300, 77], H=2, D=128, seed=16)
+    x = gen(w)
+    ws_bytes = kda.workspace_size(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"],
+                                  nseg=2)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device="cuda")
+    qbuf = x["q"].clone()
+    out = torch.empty_like(x["v"])
+    fin = torch.empty_like(x["initial_state"])
+    y = dict(x, q=qbuf)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(kda, y, out=out, final_state=fin, nseg=2, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(kda, y, out=out, final_state=fin, nseg=2, workspace=ws)
+    gen_ = torch.Generator(device="cuda")
+    for rep in range(4):
+        gen_.manual_seed(100 + rep)
+        newq = torch.randn(qbuf.shape, generator=gen_, device="cuda")
+        newq = (newq / newq.norm(dim=-1, keepdim=True)).to(qbuf.dtype)
+        qbuf.copy_(newq)
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref, s_ref = run(kda, dict(x, q=newq.clone()), nseg=2)
+        torch.cuda.synchronize()
+        assert torch_equal(out, o_ref) and torch_equal(fin, s_ref), f"replay {rep}"
