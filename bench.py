@@ -1,0 +1,224 @@
+"""KDA chunked-prefill benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config varlen|large|eqlen|long|varlen_padded|tiny]
+
+One step is one kda_prefill call over the whole workload (every kernel of the
+hot path), with inputs already resident in HBM.  Prints ONE JSON line:
+throughput in tokens/s, the roofline of the dominant kernel (its duration from
+HIP events recorded by the library on the launch stream over the timed region),
+and the float64 oracle timed on the host cores on a bounded sample of the same
+workload.  Correctness is checked against the oracle on sampled chains before
+anything is timed.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/sec at H=32,d=128 bf16; MFMA util % and HBM GB/s"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic(w):
+    """Bytes and flops the method itself must move / compute for workload w:
+    per token-head q, k, v, out (D elements each in the I/O dtype), g (D fp32),
+    beta (one fp32); per chain the initial and final fp32 D x D states.
+    Flops per token-head: the three dense state contractions (6 D^2) plus the
+    triangular in-chunk work (A, P, Ut, W, P U: 64 * 5 D)."""
+    es = 2 if w.dtype == "bf16" else 4
+    D, H = w.D, w.H
+    th = w.tokens * H
+    chains = w.n_seq * H
+    per_th = 4 * D * es + D * 4 + 4
+    bytes_ = th * per_th + chains * 2 * D * D * 4
+    flops = th * (6 * D * D + 64 * 5 * D)
+    return bytes_, flops, per_th
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("kda_chunk.hip", "kda_device.hpp"):
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(config, launches_per_step):
+    """HBM bytes per launch of the chunk kernel from the committed rocprofv3
+    PMC summary, or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w, budget_s):
+    """The float64 oracle (C, OpenMP over chains) on a bounded sample of the
+    workload's chains; returns tokens/s scaled to the whole workload's H."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
+    # ~1.5 GFLOP/s per core for the scalar fp64 loop: pick chains worth ~budget_s
+    per_th = 7.0 * w.D * w.D
+    target_th = budget_s * threads * 1.5e9 / per_th
+    rng = np.random.default_rng(0)
+    order = [(n, h) for n in range(w.n_seq) for h in range(w.H)]
+    rng.shuffle(order)
+    picked, th = [], 0
+    for n, h in order:
+        if th >= target_th:
+            break
+        picked.append((n, h))
+        th += w.lengths[n]
+    # gather the picked chains as one packed problem with H = 1
+    import torch
+    qs, ks, vs, gs, bs, ss, lens = [], [], [], [], [], [], []
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu()
+    for n, h in picked:
+        if cu is None:
+            sl = lambda t: t[n, :, h]
+        else:
+            a, b = int(cu[n]), int(cu[n + 1])
+            sl = lambda t: t[a:b, h]
+        qs.append(sl(x["q"]).cpu()); ks.append(sl(x["k"]).cpu()); vs.append(sl(x["v"]).cpu())
+        gs.append(sl(x["g"]).cpu()); bs.append(sl(x["beta"]).cpu())
+        ss.append(x["initial_state"][n, h].cpu() if x["initial_state"] is not None else torch.zeros(w.D, w.D))
+        lens.append(w.lengths[n])
+    cat = lambda lst: torch.cat(lst)[:, None]
+    s0 = torch.stack(ss)[:, None]
+    cuh = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    args = (cat(qs), cat(ks), cat(vs), cat(gs), cat(bs), s0)
+    t = time.perf_counter()
+    _, _, used = oracle.run_c(*args, cuh, threads=threads, return_threads=True)
+    dt = time.perf_counter() - t
+    token_heads = int(sum(lens))
+    return {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{len(picked)} of {w.n_seq * w.H} (sequence, head) chains, {token_heads} token-heads, "
+                      f"float64 C recurrence, {dt:.1f} s; tokens/s = token-heads / H / seconds"}
+
+
+def correctness_gate(kda, x, w, out, fin):
+    import numpy as np
+    import oracle
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu()
+    worst = 0.0
+    for n, h in [(0, 0), (w.n_seq - 1, w.H - 1)]:
+        if cu is None:
+            sl, osl = (lambda t: t[n, :, h:h + 1]), (lambda t: t[n, :, h:h + 1])
+        else:
+            a, b = int(cu[n]), int(cu[n + 1])
+            sl = osl = (lambda t: t[a:b, h:h + 1])
+        s0 = None if x["initial_state"] is None else x["initial_state"][n:n + 1, h:h + 1].cpu()
+        q = sl(x["q"]).cpu()
+        o_ref, s_ref = oracle.run_c(q, sl(x["k"]).cpu(), sl(x["v"]).cpu(), sl(x["g"]).cpu(), sl(x["beta"]).cpu(),
+                                    s0, np.array([0, q.shape[0]]))
+        eo = oracle.rel_l2(osl(out).float().cpu().numpy().reshape(o_ref.shape), o_ref)
+        es = oracle.rel_l2(fin[n:n + 1, h:h + 1].cpu().numpy(), s_ref)
+        worst = max(worst, eo, es)
+    tol = 5e-3 if w.dtype == "bf16" else 1e-4
+    if not worst <= tol:
+        raise SystemExit(f"correctness gate failed: sampled rel-L2 {worst:.3e} > {tol}")
+    return worst
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="varlen")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="instead of the bench, copy this many MiB device-to-device 5 times (PMC calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_38_amd as kda
+    import workloads
+    kda.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs the GPU")
+    dev = torch.device("cuda:0")
+
+    if a.copy_calib:
+        n = a.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_each_way": n * 4, "copies": 5}))
+        return
+
+    w = workloads.WORKLOADS[a.config]
+    x = workloads.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    step = lambda: kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"],
+                               out=out, final_state=fin)
+    out = torch.empty_like(x["v"])
+    fin = torch.empty((w.n_seq, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    step()
+    torch.cuda.synchronize()
+    gate = correctness_gate(kda, x, w, out, fin)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    kda.profile_read()            # drop anything recorded so far
+    kda.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kda.profile_enable(False)
+    chunk_ms, chunk_n = kda.profile_read("kda_chunk")
+    elapsed = t1 - t0
+    ms_step = elapsed / a.steps * 1e3
+    tokens_s = w.tokens * a.steps / elapsed
+
+    bytes_, flops, per_th = algorithmic(w)
+    launches_per_step = max(1, chunk_n // a.steps)
+    kern_ms = chunk_ms / max(1, chunk_n)                 # average chunk-kernel launch
+    # algorithmic bytes of one chunk-kernel launch: the single-segment plan does
+    # the whole workload in one launch
+    bytes_launch = bytes_ / launches_per_step
+    achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
+    tr = traffic_from_profile(a.config, launches_per_step)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    tflops = flops / launches_per_step / (kern_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; see workloads.py)",
+        "config": w.describe(),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": tr},
+        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
+                 "flops_per_launch": flops / launches_per_step},
+        "kernel": {"name": "kda_chunk", "avg_ms": kern_ms, "launches_per_step": launches_per_step,
+                   "algorithmic_bytes_per_launch": bytes_launch, "bytes_per_token_head": per_th,
+                   "kernel_source_sha": source_sha()},
+        "correctness": {"sampled_rel_l2_max": gate},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, w, a.cpu_budget)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -34,7 +34,7 @@ class KdaTensor(ctypes.Structure):
 
 class KdaOptions(ctypes.Structure):
     _fields_ = [("nseg", ctypes.c_int32), ("prep", ctypes.c_int32),
-                ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32)]
+                ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -63,7 +63,7 @@ def load_library(path: str = LIB_PATH):
     lib.kda_prefill_ws.restype = ctypes.c_int
     lib.kda_prefill_workspace_size.argtypes = [T, T, T, T, T, T, T, T, T, O, ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_prefill_workspace_size.restype = ctypes.c_int
-    lib.kda_prep.argtypes = [T, T, T, V]
+    lib.kda_prep.argtypes = [T, T, ctypes.c_int32, T, V]
     lib.kda_prep.restype = ctypes.c_int
     lib.kda_release_cached_workspace.argtypes = []
     lib.kda_release_cached_workspace.restype = None
@@ -124,9 +124,9 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be on the GPU")
 
 
-def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0) -> KdaOptions:
+def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0, variant: int = 0) -> KdaOptions:
     o = KdaOptions()
-    o.nseg, o.prep = nseg, prep
+    o.nseg, o.prep, o.variant = nseg, prep, variant
     o.stall_wave = stall_wave + 1 if stall_wave >= 0 else 0
     o.stall_cycles = stall_cycles
     return o
@@ -144,19 +144,19 @@ def _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, want_final
 
 
 def workspace_size(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
-                   nseg: int = 0, prep: int = 0) -> int:
+                   nseg: int = 0, prep: int = 0, variant: int = 0) -> int:
     lib = load_library()
     out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, False)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     n = ctypes.c_size_t(0)
-    _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(options(nseg, prep)),
+    _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(options(nseg, prep, variant=variant)),
                                           ctypes.byref(n)))
     return n.value
 
 
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
             output_final_state: bool = True, nseg: int = 0, prep: int = 0, stall_wave: int = -1,
-            stall_cycles: int = 0, workspace=None, stream=None) -> Tuple:
+            stall_cycles: int = 0, variant: int = 0, workspace=None, stream=None) -> Tuple:
     """KDA chunked prefill.  Returns (out, final_state).
 
     Dense layout: q, k, g [B, T, H, K], v [B, T, H, V], beta [B, T, H].
@@ -172,11 +172,11 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, output_final_state)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    plain = nseg == 0 and prep == 0 and stall_wave < 0 and workspace is None
+    plain = nseg == 0 and prep == 0 and stall_wave < 0 and variant == 0 and workspace is None
     if plain:
         _check(lib.kda_prefill(*[_ptr(d) for d in ds], ctypes.c_void_p(st)))
         return out, final_state
-    opts = options(nseg, prep, stall_wave, stall_cycles)
+    opts = options(nseg, prep, stall_wave, stall_cycles, variant)
     need = ctypes.c_size_t(0)
     _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value:
@@ -191,8 +191,8 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     return out, final_state
 
 
-def prep(g, cu_seqlens=None, gamma=None, stream=None):
-    """Standalone PREP kernel: in-chunk (64-token) inclusive cumsum of g."""
+def prep(g, cu_seqlens=None, gamma=None, chunk: int = 64, stream=None):
+    """Standalone PREP kernel: in-chunk (``chunk`` = 32 or 64 tokens) inclusive cumsum of g."""
     import torch
     lib = load_library()
     _require_gpu(g, cu_seqlens, gamma)
@@ -200,7 +200,8 @@ def prep(g, cu_seqlens=None, gamma=None, stream=None):
         gamma = torch.empty_like(g)
     st = torch.cuda.current_stream(g.device).cuda_stream if stream is None else stream
     dc = describe(cu_seqlens) if cu_seqlens is not None else None
-    _check(lib.kda_prep(ctypes.byref(describe(g)), _ptr(dc), ctypes.byref(describe(gamma)), ctypes.c_void_p(st)))
+    _check(lib.kda_prep(ctypes.byref(describe(g)), _ptr(dc), ctypes.c_int32(chunk), ctypes.byref(describe(gamma)),
+                        ctypes.c_void_p(st)))
     return gamma
 
 

@@ -235,6 +235,8 @@ kda_status_t validate(const kda_tensor_t *q, const kda_tensor_t *k, const kda_te
 // ------------------------------------------------------------------ plan
 struct Plan {
     int nseg = 1;
+    bool pipe = false;          // pipelined 32-token kernel (d = 128, bf16)
+    int chunk = 64;
     bool standalone_prep = false;
     size_t off_gamma = 0, off_maps = 0, off_start = 0, bytes = 0;
 };
@@ -252,7 +254,13 @@ int device_cus()
 kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
 {
     const int64_t chains = P.N * P.H;
-    const int64_t max_chunks = P.dense ? (P.T + 63) / 64 : (P.Ttot + 63) / 64;
+    const int variant = o ? o->variant : 0;
+    if (variant < 0 || variant > 2) return fail(KDA_ERR_UNSUPPORTED, "kernel variant %d", variant);
+    const bool pipe_ok = P.D == 128 && !P.fp32;
+    if (variant == 2 && !pipe_ok) return fail(KDA_ERR_UNSUPPORTED, "the pipelined kernel needs head size 128 and bf16");
+    pl.pipe = pipe_ok && variant != 1;
+    pl.chunk = pl.pipe ? 32 : 64;
+    const int64_t max_chunks = P.dense ? (P.T + pl.chunk - 1) / pl.chunk : (P.Ttot + pl.chunk - 1) / pl.chunk;
     if (o && o->nseg > 0) {
         if (o->nseg > 64) return fail(KDA_ERR_UNSUPPORTED, "nseg %d > 64", o->nseg);
         pl.nseg = o->nseg;
@@ -261,7 +269,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
         int64_t nseg = 1;
         if (chains > 0 && chains < cus) {
             nseg = std::min<int64_t>(cus / chains, 32);
-            nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, max_chunks / 4));   // >= ~4 chunks per segment
+            nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, max_chunks / 8));   // >= ~8 chunks per segment
         }
         pl.nseg = (int)std::max<int64_t>(1, nseg);
     }
@@ -343,6 +351,9 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     const bool stall = cp.stall_wave >= 0 && cp.stall_iters > 0;
     const int D = (int)P.D;
     hipError_t e;
+    auto chunk = [&](int grid) {
+        return pl.pipe ? kda::launch_chunk_pipe(cp, grid, stall, st) : kda::launch_chunk(cp, D, P.fp32, grid, stall, st);
+    };
 
     if (pl.standalone_prep) {
         kda::PrepParams pp{};
@@ -352,8 +363,9 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
         // workspace Gamma: contiguous [B*T or Ttot, H, D]
         pp.y_st = P.H * P.D; pp.y_sh = P.D; pp.y_sb = P.dense ? P.T * P.H * P.D : 0;
         pp.N = (int32_t)P.N; pp.H = (int32_t)P.H; pp.T = (int32_t)P.T; pp.D = D;
-        pp.chunks_per_seq = P.dense ? (int32_t)((P.T + 63) / 64) : 0;
-        const int64_t nvc = P.dense ? P.B * ((P.T + 63) / 64) : (P.Ttot + 63) / 64 + P.N;
+        pp.chunk = pl.chunk;
+        pp.chunks_per_seq = P.dense ? (int32_t)((P.T + pl.chunk - 1) / pl.chunk) : 0;
+        const int64_t nvc = P.dense ? P.B * pp.chunks_per_seq : (P.Ttot + pl.chunk - 1) / pl.chunk + P.N;
         if ((e = timed("kda_prep", st, [&] { return kda::launch_prep(pp, (int)nvc, st); })) != hipSuccess)
             return hip_fail(e, "PREP launch");
         cp.g = gam;
@@ -362,7 +374,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     }
     if (pl.nseg == 1) {
         cp.role = kda::ROLE_OUT;
-        if ((e = timed("kda_chunk", st, [&] { return kda::launch_chunk(cp, D, P.fp32, (int)chains, stall, st); })) != hipSuccess)
+        if ((e = timed("kda_chunk", st, [&] { return chunk((int)chains); })) != hipSuccess)
             return hip_fail(e, "chunk launch");
         return KDA_OK;
     }
@@ -370,7 +382,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     cp.ws_start = (const float *)(wsb + pl.off_start);
     cp.role = kda::ROLE_SEG_M;   // the launch covers both M and C roles
     if ((e = timed("kda_chunk_segbuild", st, [&] {
-             return kda::launch_chunk(cp, D, P.fp32, (int)(chains * pl.nseg * 2), stall, st);
+             return chunk((int)(chains * pl.nseg * 2));
          })) != hipSuccess)
         return hip_fail(e, "segment-build launch");
     kda::CombineParams mp{};
@@ -381,7 +393,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
         return hip_fail(e, "combine launch");
     cp.role = kda::ROLE_SEG_OUT;
     if ((e = timed("kda_chunk_segout", st, [&] {
-             return kda::launch_chunk(cp, D, P.fp32, (int)(chains * pl.nseg), stall, st);
+             return chunk((int)(chains * pl.nseg));
          })) != hipSuccess)
         return hip_fail(e, "segment-output launch");
     return KDA_OK;
@@ -463,9 +475,11 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
     return run(P, pl, nullptr, ws, pl.bytes, (hipStream_t)stream);
 }
 
-kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, kda_tensor_t *gamma, void *stream)
+kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int32_t chunk, kda_tensor_t *gamma,
+                      void *stream)
 {
     kda_status_t st;
+    if (chunk != 32 && chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk length %d not in {32, 64}", chunk);
     if ((st = check_basic(g, "g", false)) || (st = check_basic(gamma, "gamma", false)) ||
         (st = check_basic(cu_seqlens, "cu_seqlens", true)))
         return st;
@@ -497,9 +511,10 @@ kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, kda
     pp.g_sb = tg.sb; pp.g_st = tg.st; pp.g_sh = tg.sh;
     pp.y_sb = ty.sb; pp.y_st = ty.st; pp.y_sh = ty.sh;
     pp.N = (int32_t)P.N; pp.H = (int32_t)P.H; pp.T = (int32_t)P.T; pp.D = (int32_t)P.D;
-    pp.chunks_per_seq = P.dense ? (int32_t)((P.T + 63) / 64) : 0;
+    pp.chunk = chunk;
+    pp.chunks_per_seq = P.dense ? (int32_t)((P.T + chunk - 1) / chunk) : 0;
     if (P.N == 0 || (P.dense && P.T == 0)) return KDA_OK;
-    const int64_t nvc = P.dense ? P.B * ((P.T + 63) / 64) : (P.Ttot + 63) / 64 + P.N;
+    const int64_t nvc = P.dense ? P.B * pp.chunks_per_seq : (P.Ttot + chunk - 1) / chunk + P.N;
     hipError_t e = timed("kda_prep", (hipStream_t)stream, [&] { return kda::launch_prep(pp, (int)nvc, (hipStream_t)stream); });
     return e == hipSuccess ? KDA_OK : hip_fail(e, "PREP launch");
 }

@@ -48,16 +48,19 @@ template <int D, typename ET> struct ChunkCfg {
     static constexpr int G_LD = D + 4;         // Gamma, fp32 [64][D]
     static constexpr int H_LD = HALF + PH;     // X, Y, Z, Kb  [rows][HALF]
     static constexpr int QT_LD = D + 4;        // Qt, W [64][D]
-    static constexpr int TT_LD = CHUNK + 4;    // Kh^T, (beta Kt)^T, (beta V)^T [D][64]
-    static constexpr int SQ_LD = CHUNK + 4;    // A, P, T [64][64]
-    static constexpr int AD_BS = 16 * 17 + 1;  // fp32 diagonal blocks of A (bf16 mode)
+    static constexpr int TT_LD = CHUNK + 4;    // Kh^T [D][64], read 8 bytes per lane
+    static constexpr int TW_LD = CHUNK + PH;   // (beta Kt)^T, (beta V)^T [D][64], read 16 bytes per lane
+    static constexpr int SQ_LD = CHUNK + 4;    // A, P [64][64]
+    static constexpr int TQ_LD = CHUNK + PH;   // T [64][64], read 16 bytes per lane
+    static constexpr int AD_LD = 20;           // fp32 diagonal blocks of A (bf16 mode): rows 16-byte aligned
+    static constexpr int AD_BS = 16 * AD_LD + 4;
     static constexpr int TD_LD = 16 + 4;       // transposed diagonal blocks of T
     static constexpr int KB_ROWS = 96;         // K-bar blocks 0..2 + three scaled copies
     // region G: Gamma, later A (+ fp32 diagonal), T, T-diag^T
     static constexpr int SZ_GAM = CHUNK * G_LD * 4;
     static constexpr int SZ_A = CHUNK * SQ_LD * ES;
     static constexpr int SZ_AD = (ES == 2) ? 4 * AD_BS * 4 : 0;
-    static constexpr int SZ_T = CHUNK * SQ_LD * ES;
+    static constexpr int SZ_T = CHUNK * TQ_LD * ES;
     static constexpr int SZ_TD = 4 * 16 * TD_LD * ES;
     static constexpr int SZ_G2 = SZ_A + SZ_AD + SZ_T + SZ_TD;
     static constexpr int SZ_G = ((SZ_GAM > SZ_G2 ? SZ_GAM : SZ_G2) + 15) / 16 * 16;
@@ -69,7 +72,8 @@ template <int D, typename ET> struct ChunkCfg {
     // region E: Qt, Kh^T, (beta Kt)^T, (beta V)^T
     static constexpr int SZ_QT = CHUNK * QT_LD * ES;
     static constexpr int SZ_TT = D * TT_LD * ES;
-    static constexpr int SZ_E = (SZ_QT + 3 * SZ_TT + 15) / 16 * 16;
+    static constexpr int SZ_TW = D * TW_LD * ES;
+    static constexpr int SZ_E = (SZ_QT + SZ_TT + 2 * SZ_TW + 15) / 16 * 16;
     static constexpr int NSC = 16;             // per-channel scale rows
     static constexpr int SZ_SC = NSC * D * 4;
     static constexpr int OFF_G = 0, OFF_H = SZ_G, OFF_E = OFF_H + SZ_H, OFF_SC = OFF_E + SZ_E;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
     using EL = Elem<ET>;
     constexpr int NW = Cf::NW, HALF = Cf::HALF, CG = Cf::CG;
     constexpr int G_LD = Cf::G_LD, H_LD = Cf::H_LD, QT_LD = Cf::QT_LD, TT_LD = Cf::TT_LD,
-                  SQ_LD = Cf::SQ_LD;
+                  SQ_LD = Cf::SQ_LD, TW_LD = Cf::TW_LD, TQ_LD = Cf::TQ_LD;
     constexpr int NMT = D / 32;            // 32-row tiles of the state
     constexpr int NITEM = 20 / NW;         // A/P sub-tiles per wave
 
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
     ET *sQt = (ET *)(smem + Cf::OFF_E);
     ET *sKhT = sQt + CHUNK * QT_LD;
     ET *sKtT = sKhT + D * TT_LD;
-    ET *sVT = sKtT + D * TT_LD;
+    ET *sVT = sKtT + D * Cf::TW_LD;
     float *sSc = (float *)(smem + Cf::OFF_SC);
     float *sBeta = (float *)(smem + Cf::OFF_BETA);
 
@@ -169,46 +173,51 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
         } else if (role == ROLE_SEG_OUT) {
             src = p.ws_start + ((int64_t)chain * p.nseg + seg) * D * D;
         }
+        const float one = (role == ROLE_SEG_M) ? 1.f : 0.f;
+        if (src) {                  // one straight-line block of loads
 #pragma unroll
-        for (int m = 0; m < NMT; ++m)
+            for (int m = 0; m < NMT; ++m)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 32 * m + 8 * q + 4 * g2 + r;
-                    float x = 0.f;
-                    if (src) x = src[row * rs + vcol];
-                    else if (role == ROLE_SEG_M) x = (row == vcol) ? 1.f : 0.f;
-                    S[m][4 * q + r] = x;
-                }
+                    for (int r = 0; r < 4; ++r) S[m][4 * q + r] = src[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol];
+        } else {
+#pragma unroll
+            for (int m = 0; m < NMT; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[m][4 * q + r] = (32 * m + 8 * q + 4 * g2 + r == vcol) ? one : 0.f;
+        }
     }
 
     // ------------------------------------------------ register prefetch
     typename V4::raw rq[2][4], rk[2][4], rv[2][4];
     float4 rg[2][4];
     float rbeta = 0.f;
+    // Loads are unconditional from clamped, always in-bounds addresses (tail rows
+    // re-read the chunk's last token) so no load sits in a branch whose merge would
+    // force a wait; tail rows are zeroed where the data is used.
     auto load_g = [&](int c) {
-        const int tok0 = c * CHUNK, L = min(CHUNK, len - tok0);
+        const int tok0 = c * CHUNK, Lm1 = min(CHUNK, len - tok0) - 1;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 4 * tg + r, ch = hh * HALF + 4 * cg;
-                rg[hh][r] = (i < L) ? *(const float4 *)(gb + (int64_t)(tok0 + i) * p.g_st + ch)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int ch = hh * HALF + 4 * cg;
+                rg[hh][r] = *(const float4 *)(gb + (int64_t)(tok0 + min(4 * tg + r, Lm1)) * p.g_st + ch);
             }
-        if (tid < CHUNK) rbeta = (tid < L) ? bb[(int64_t)(tok0 + tid) * p.b_st] : 0.f;
+        if (tid < CHUNK) rbeta = bb[(int64_t)(tok0 + min(tid, Lm1)) * p.b_st];
     };
     auto load_qkv = [&](int c, int hh) {
-        const int tok0 = c * CHUNK, L = min(CHUNK, len - tok0);
+        const int tok0 = c * CHUNK, Lm1 = min(CHUNK, len - tok0) - 1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 4 * tg + r, ch = hh * HALF + 4 * cg;
-            const bool ok = i < L;
-            const int64_t tk = tok0 + i;
-            rq[hh][r] = (ok && has_out) ? V4::load(qb + tk * p.q_st + ch) : V4::zero();
-            rk[hh][r] = ok ? V4::load(kb + tk * p.k_st + ch) : V4::zero();
-            rv[hh][r] = (ok && has_v) ? V4::load(vb + tk * p.v_st + ch) : V4::zero();
+            const int ch = hh * HALF + 4 * cg;
+            const int64_t tk = tok0 + min(4 * tg + r, Lm1);
+            rq[hh][r] = V4::load(qb + tk * p.q_st + ch);
+            rk[hh][r] = V4::load(kb + tk * p.k_st + ch);
+            rv[hh][r] = V4::load(vb + tk * p.v_st + ch);
         }
     };
     if (c_begin < c_end) {
@@ -230,22 +239,29 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                *(float4 *)(sG + (4 * tg + r) * G_LD + hh * HALF + 4 * cg) = rg[hh][r];
-        if (tid < CHUNK) sBeta[tid] = rbeta;
+                *(float4 *)(sG + (4 * tg + r) * G_LD + hh * HALF + 4 * cg) =
+                    (4 * tg + r < L) ? rg[hh][r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < CHUNK) sBeta[tid] = (tid < L) ? rbeta : 0.f;
         if (c + 1 < c_end) load_g(c + 1);
         sync();
 
         // ---------------- stage 2: in-chunk gate scan (PREP's device step) + scales
         if (tid < D) {
-            float acc = 0.f, gend[4];
-#pragma unroll 8
+            // one thread per key channel: the column into registers, the 64 adds in
+            // token order (fp32, sequential), the column back
+            float col[CHUNK], gend[4];
+#pragma unroll
+            for (int i = 0; i < CHUNK; ++i) col[i] = sG[i * G_LD + tid];
+            float acc = 0.f;
+#pragma unroll
             for (int i = 0; i < CHUNK; ++i) {
-                const float x = sG[i * G_LD + tid];
-                if (p.g_is_gamma) acc = (i < L) ? x : acc;   // tail rows hold Gamma_{L-1}
-                else acc = acc + x;                          // sequential fp32 order
-                sG[i * G_LD + tid] = acc;
+                if (p.g_is_gamma) acc = (i < L) ? col[i] : acc;   // tail rows hold Gamma_{L-1}
+                else acc = acc + col[i];
+                col[i] = acc;
                 if ((i & 15) == 15) gend[i >> 4] = acc;
             }
+#pragma unroll
+            for (int i = 0; i < CHUNK; ++i) sG[i * G_LD + tid] = col[i];
             const float GL = gend[3];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -293,6 +309,14 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                     V4::unpack(rq[hh][r], qf);
                     V4::unpack(rk[hh][r], kf);
                     V4::unpack(rv[hh][r], vf);
+                    if (i >= L || !has_v) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) vf[e] = 0.f;
+                    }
+                    if (i >= L) {                       // tail rows: no token
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { qf[e] = 0.f; kf[e] = 0.f; }
+                    }
                     float X[4], Y[4], Z[4], Kb[4], Qt[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -333,10 +357,10 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                     const float a0[4] = {kh[0][e], kh[1][e], kh[2][e], kh[3][e]};
                     const float a1[4] = {bkt[0][e], bkt[1][e], bkt[2][e], bkt[3][e]};
                     V4::store(sKhT + (ch + e) * TT_LD + 4 * tg, V4::pack(a0));
-                    V4::store(sKtT + (ch + e) * TT_LD + 4 * tg, V4::pack(a1));
+                    V4::store(sKtT + (ch + e) * TW_LD + 4 * tg, V4::pack(a1));
                     if (has_v) {
                         const float a2[4] = {bv[0][e], bv[1][e], bv[2][e], bv[3][e]};
-                        V4::store(sVT + (ch + e) * TT_LD + 4 * tg, V4::pack(a2));
+                        V4::store(sVT + (ch + e) * TW_LD + 4 * tg, V4::pack(a2));
                     }
                 }
             }
@@ -381,8 +405,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                 for (int r = 0; r < 4; ++r) vals[r] = (j0 + r < i) ? apacc[it][r] * bi : 0.f;
                 if (ib == jb) {
                     if constexpr (Cf::ES == 2) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sAd[ib * Cf::AD_BS + l16 * 17 + 4 * g4 + r] = vals[r];
+                        *(float4 *)(sAd + ib * Cf::AD_BS + l16 * Cf::AD_LD + 4 * g4) = make_float4(vals[0], vals[1], vals[2], vals[3]);
                     } else {
                         V4::store(sA + i * SQ_LD + j0, V4::pack(vals));
                     }
@@ -400,29 +423,39 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
             const int bsel2 = tid >> 6, rem = tid & 63;
             const int ib = 2 * bsel2, i = 16 * ib + (rem >> 2), j = 16 * (ib + 1) + 4 * (rem & 3);
             if (has_out) V4::store(sP + i * SQ_LD + j, V4::zero());
-            V4::store(sT + i * SQ_LD + j, V4::zero());
+            V4::store(sT + i * TQ_LD + j, V4::zero());
         }
         sync();
 
         // ---------------- stage 6: T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution
-        if (wave == 0) {
-            const int b = g4, col = l16;
+        {
+            // block b of this lane: D = 128 gives one block per wave, D = 64 two per wave
+            constexpr int PER = 4 / NW;
+            const int b = wave + NW * (g4 % PER), col = l16;
             const float *Ab;
             int ld;
-            if constexpr (Cf::ES == 2) { Ab = sAd + b * Cf::AD_BS; ld = 17; }
+            if constexpr (Cf::ES == 2) { Ab = sAd + b * Cf::AD_BS; ld = Cf::AD_LD; }
             else { Ab = (const float *)sA + (16 * b) * SQ_LD + 16 * b; ld = SQ_LD; }
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                float arow[16];
+#pragma unroll
+                for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
+                    const float4 a4 = *(const float4 *)(Ab + i * ld + 4 * j4);
+                    arow[4 * j4] = a4.x; arow[4 * j4 + 1] = a4.y; arow[4 * j4 + 2] = a4.z; arow[4 * j4 + 3] = a4.w;
+                }
                 float s = (i == col) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) s = fmaf(-Ab[i * ld + j], x[j], s);
+                for (int j = 0; j < i; ++j) s = fmaf(-arow[j], x[j], s);
                 x[i] = s;
             }
+            if (g4 < PER) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sT[(16 * b + i) * SQ_LD + 16 * b + col] = EL::from_f(x[i]);
-                sTdT[(16 * b + col) * Cf::TD_LD + i] = EL::from_f(x[i]);
+                for (int i = 0; i < 16; ++i) {
+                    sT[(16 * b + i) * TQ_LD + 16 * b + col] = EL::from_f(x[i]);
+                    sTdT[(16 * b + col) * Cf::TD_LD + i] = EL::from_f(x[i]);
+                }
             }
         }
         sync();
@@ -446,7 +479,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                     mma16k16(Y, fa, fb);
                 }
                 Frag4<ET> fa2, fy;
-                fa2.load4(sT + (16 * i + l16) * SQ_LD + 16 * i + 4 * g4);
+                fa2.load4(sT + (16 * i + l16) * TQ_LD + 16 * i + 4 * g4);
                 const float y4[4] = {Y[0], Y[1], Y[2], Y[3]};
                 fy.set(y4);
                 f32x4 Tij = {0.f, 0.f, 0.f, 0.f};
@@ -454,7 +487,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     Tij[r] = -Tij[r];
-                    sT[(16 * i + 4 * g4 + r) * SQ_LD + 16 * jc + l16] = EL::from_f(Tij[r]);
+                    sT[(16 * i + 4 * g4 + r) * TQ_LD + 16 * jc + l16] = EL::from_f(Tij[r]);
                 }
                 Tp[i] = Tij;
             }
@@ -471,8 +504,8 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                 for (int s = 0; s < 4; ++s) {
                     if (nt == 0 && s >= 2) continue;
                     Frag8<ET> fa, fb;
-                    fa.load8(sKtT + (32 * wave + l32) * TT_LD + 16 * s + 8 * g2);
-                    fb.load8(sT + (32 * nt + l32) * SQ_LD + 16 * s + 8 * g2);
+                    fa.load8(sKtT + (32 * wave + l32) * TW_LD + 16 * s + 8 * g2);
+                    fb.load8(sT + (32 * nt + l32) * TQ_LD + 16 * s + 8 * g2);
                     mma32(acc, fa, fb);
                 }
 #pragma unroll
@@ -489,8 +522,8 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                 for (int s = 0; s < 4; ++s) {
                     if (mt == 0 && s >= 2) continue;
                     Frag8<ET> fa, fb;
-                    fa.load8(sT + (32 * mt + l32) * SQ_LD + 16 * s + 8 * g2);
-                    fb.load8(sVT + (32 * wave + l32) * TT_LD + 16 * s + 8 * g2);
+                    fa.load8(sT + (32 * mt + l32) * TQ_LD + 16 * s + 8 * g2);
+                    fb.load8(sVT + (32 * wave + l32) * TW_LD + 16 * s + 8 * g2);
                     mma32(U[mt], fa, fb);
                 }
             }

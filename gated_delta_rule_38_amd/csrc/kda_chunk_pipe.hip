@@ -1,0 +1,612 @@
+// Pipelined CHUNK kernel for d_k = d_v = 128, bf16: the production path.
+//
+// Same mathematics as kda_chunk.hip (the WY/UT chunk form of the gated delta
+// rule; see the comment there), with 32-token chunks and the work of a chain
+// split between two wave roles of one 512-thread workgroup:
+//   * 4 consumer waves own the fp32 128x128 state -- wave w keeps value columns
+//     [32w, 32w+32) in MFMA accumulators for the whole chain -- and run the
+//     state path of chunk c:
+//         R = V - Kt S,   U = (T diag(beta)) R,   O = Qt S + P U,
+//         S <- Diag(e^{G_L}) S + Kh^T U
+//     (U = T diag(beta) (V - Kt S) is the UT form's U = Ut - W S with
+//     Ut = T diag(beta) V and W = T diag(beta) Kt folded together, so W is
+//     never formed);
+//   * 4 producer waves meanwhile build the state-independent operators of the
+//     next chunk: the in-chunk gate scan, the gate-factored operands, A and P on
+//     16x16 MFMA tiles and T diag(beta) with T = (I + A)^-1.
+// The roles meet in a double buffer in LDS.  Step t: the producers build chunk
+// t into buffer t%2 while the consumers run chunk t-1 from buffer (t-1)%2.
+// Every wave executes the same three workgroup barriers per step; no buffer is
+// written before the barrier that ends the last read of its previous contents
+// (the reader/writer ordering TensorRT-LLM PR #19826 had to add to its fused
+// prefill between a chunk's readers and the next chunk's writers).  A VALU-heavy
+// producer wave and an MFMA-heavy consumer wave share each SIMD.
+//
+//   interval 1: producers -- gate-factored operands of chunk t; q, k, v of t+1 requested
+//               consumers -- R and U of chunk t-1
+//   interval 2: producers -- A, P of chunk t
+//               consumers -- O of chunk t-1 (stored)
+//   interval 3: producer wave 0 -- T diag(beta) of chunk t
+//               producer waves 2, 3 -- gate scan of chunk t+1; g of t+2 requested
+//               consumers -- state update of chunk t-1
+//
+// 32-token chunks hold two 16-token gate sub-blocks: diagonal sub-blocks factor
+// the decay through the block start (factors within [e^-80, e^80] for g >= -5),
+// the off-diagonal one through the last token of block 0 (factors <= 1).
+#include <type_traits>
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace pipe {
+
+constexpr int C = 32;           // tokens per chunk
+constexpr int D = 128;
+constexpr int NT = 512;         // 4 consumer + 4 producer waves
+// leading dimensions (elements); padding matches each tile's read width
+constexpr int W_LD = D + 4;     // Qt, -Kt [32][128] bf16, 8-byte reads
+constexpr int KH_LD = C + 4;    // Kh^T, V^T [128][32] bf16, 8-byte reads
+constexpr int P_LD = C + 4;     // P, T diag(beta) [32][32] bf16, 8-byte reads
+constexpr int G_LD = D + 4;     // Gamma * log2(e) [32][128] fp32
+constexpr int X_LD = D + 8;     // X, Y, Z, Kb [rows][128] bf16, 16-byte reads
+constexpr int A_LD = 16 + 4;    // 16x16 blocks: A10 (bf16), A diagonal (fp32), T diagonal^T (fp32)
+// one operand buffer (bytes)
+constexpr int B_QT = 0;
+constexpr int B_KT = B_QT + C * W_LD * 2;
+constexpr int B_KH = B_KT + C * W_LD * 2;
+constexpr int B_VT = B_KH + D * KH_LD * 2;
+constexpr int B_P = B_VT + D * KH_LD * 2;
+constexpr int B_T = B_P + C * P_LD * 2;
+constexpr int B_SIZE = B_T + C * P_LD * 2;
+// producer scratch
+constexpr int S_G = 2 * B_SIZE;
+constexpr int S_X = S_G + C * G_LD * 4;
+constexpr int S_Y = S_X + C * X_LD * 2;
+constexpr int S_Z = S_Y + C * X_LD * 2;
+constexpr int S_KB = S_Z + C * X_LD * 2;
+constexpr int S_A10 = S_KB + 16 * X_LD * 2;
+constexpr int S_AD = S_A10 + 16 * A_LD * 2;
+constexpr int S_TD = S_AD + 2 * 16 * A_LD * 4;
+constexpr int S_T22 = S_TD + 16 * A_LD * 4;
+constexpr int S_SC = S_T22 + 2 * 8 * 8 * 4;
+constexpr int S_DEC = S_SC + 2 * D * 4;       // chunk decays e^{G_L}: a ring of 3 chunks
+constexpr int S_BETA = S_DEC + 3 * D * 4;     // beta: a ring of 2 chunks
+constexpr int SMEM = S_BETA + 2 * C * 4;
+static_assert(SMEM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+static_assert(B_SIZE % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TD % 16 == 0 &&
+              S_T22 % 16 == 0 && S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
+
+typedef Vec4<bf16> V4;
+
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// The 4x4 transpose of four rows of 4 bf16 (one uint2 each): out[e] holds
+// element e of rows 0..3.
+__device__ __forceinline__ void transpose4x4_bf16(const uint2 *in, uint2 *out)
+{
+    // selector 0x05040100 keeps the low 16 bits of (a, b), 0x07060302 the high ones
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const uint32_t a = e ? in[0].y : in[0].x, b = e ? in[1].y : in[1].x;
+        const uint32_t c = e ? in[2].y : in[2].x, d = e ? in[3].y : in[3].x;
+        out[2 * e].x = __builtin_amdgcn_perm(b, a, 0x05040100u);
+        out[2 * e].y = __builtin_amdgcn_perm(d, c, 0x05040100u);
+        out[2 * e + 1].x = __builtin_amdgcn_perm(b, a, 0x07060302u);
+        out[2 * e + 1].y = __builtin_amdgcn_perm(d, c, 0x07060302u);
+    }
+}
+
+template <bool STALL>
+__global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    float *sG = (float *)(smem + S_G);
+    bf16 *sX = (bf16 *)(smem + S_X), *sY = (bf16 *)(smem + S_Y), *sZ = (bf16 *)(smem + S_Z);
+    bf16 *sKb = (bf16 *)(smem + S_KB), *sA10 = (bf16 *)(smem + S_A10);
+    float *sAd = (float *)(smem + S_AD), *sTd = (float *)(smem + S_TD), *sT22 = (float *)(smem + S_T22);
+    float *sSc = (float *)(smem + S_SC), *sDec = (float *)(smem + S_DEC);
+    float *sBeta = (float *)(smem + S_BETA);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int l32 = lane & 31, g2 = lane >> 5, l16 = lane & 15, g4 = lane >> 4;
+    const bool producer = wave >= 4;
+
+    auto sync = [&]() {
+        __syncthreads();
+        if constexpr (STALL) {
+            if (wave == p.stall_wave)
+                for (int s = 0; s < p.stall_iters; ++s) __builtin_amdgcn_s_sleep(127);
+        }
+    };
+
+    // ------------------------------------------------ chain / segment
+    int wg = blockIdx.x;
+    int role = p.role;
+    if (role == ROLE_SEG_M) {
+        role = (wg & 1) ? ROLE_SEG_C : ROLE_SEG_M;
+        wg >>= 1;
+    }
+    const int seg = wg % p.nseg;
+    const int chain = wg / p.nseg;
+    const int n = chain / p.H, h = chain % p.H;
+    int64_t t0, bsel;
+    int len;
+    seq_range(p.cu, n, p.T, t0, len, bsel);
+    const int nchunks = (len + C - 1) / C;
+    const int cps = (nchunks + p.nseg - 1) / p.nseg;
+    const int c_begin = min(seg * cps, nchunks);
+    const int c_end = min(c_begin + cps, nchunks);
+    const int nck = c_end - c_begin;
+    const bool has_out = (role == ROLE_OUT || role == ROLE_SEG_OUT);
+    const bool has_v = (role != ROLE_SEG_M);
+
+    if (producer) {
+        // ============================================ producer waves
+        const int pt = tid - 256, pw = wave - 4;
+        const int cg = pt & 31, tg = pt >> 5;                      // elementwise: 4 channels x 4 tokens
+        const int blk = __builtin_amdgcn_readfirstlane(tg >> 2);   // 16-token sub-block, uniform per wave
+        const int ch = 4 * cg;
+        const int sc = pt - 128;                                   // scan threads (waves 6, 7): one key channel each
+        const bf16 *qb = (const bf16 *)p.q + bsel * p.q_sb + h * p.q_sh + t0 * p.q_st;
+        const bf16 *kb = (const bf16 *)p.k + bsel * p.k_sb + h * p.k_sh + t0 * p.k_st;
+        const bf16 *vb = (const bf16 *)p.v + bsel * p.v_sb + h * p.v_sh + t0 * p.v_st;
+        const float *gb = p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st;
+        const float *bb = p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st;
+
+        float rg[C];                    // scan threads: one channel's g over the chunk
+        uint2 rq[4], rk[4], rv[4];      // 4 tokens x 4 channels of q, k, v (bf16)
+        float rbeta = 0.f;
+        // Loads are unconditional from always in-bounds addresses (the rows of a
+        // short last chunk re-read its last token) so that no load sits in a
+        // branch whose merge would force a wait; such rows are zeroed at use.
+        auto prefetch_g = [&](int c) {
+            const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
+            if (sc >= 0) {
+                const float *gs = gb + (int64_t)tok0 * p.g_st + sc;
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    rg[i] = *gs;
+                    if (i < Lm1) gs += p.g_st;
+                }
+            }
+            if (pt < C) rbeta = bb[(int64_t)(tok0 + min(pt, Lm1)) * p.b_st];
+        };
+        auto prefetch_qkv = [&](int c) {
+            const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
+            const int r0 = min(4 * tg, Lm1);
+            const bf16 *qs = qb + (int64_t)(tok0 + r0) * p.q_st + ch;
+            const bf16 *ks = kb + (int64_t)(tok0 + r0) * p.k_st + ch;
+            const bf16 *vs = vb + (int64_t)(tok0 + r0) * p.v_st + ch;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                rq[r] = *(const uint2 *)qs;
+                rk[r] = *(const uint2 *)ks;
+                rv[r] = *(const uint2 *)vs;
+                const bool adv = 4 * tg + r < Lm1;
+                qs += adv ? p.q_st : 0;
+                ks += adv ? p.k_st : 0;
+                vs += adv ? p.v_st : 0;
+            }
+        };
+        // gate scan of chunk c (the t-th of this segment) into Gamma * log2(e), the
+        // per-channel scales, decay ring slot t % 3 and beta ring slot t % 2
+        auto scan = [&](int c, int t) {
+            const int buf = t & 1;
+            const int L = min(C, len - c * C);
+            if (sc >= 0) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    if (p.g_is_gamma) acc = (i < L) ? rg[i] : acc;      // tail rows hold Gamma_{L-1}
+                    else acc = acc + ((i < L) ? rg[i] : 0.f);           // fp32 adds in token order
+                    rg[i] = acc * LOG2E;
+                }
+#pragma unroll
+                for (int i = 0; i < C; ++i) sG[i * G_LD + sc] = rg[i];
+                sSc[0 * D + sc] = __builtin_amdgcn_exp2f(rg[15]);              // e^{G_15}
+                sSc[1 * D + sc] = __builtin_amdgcn_exp2f(rg[31] - rg[15]);     // e^{G_L - G_15}
+                sDec[(t % 3) * D + sc] = __builtin_amdgcn_exp2f(rg[31]);             // e^{G_L}
+            }
+            if (pt < C) sBeta[buf * C + pt] = (pt < L) ? rbeta : 0.f;
+        };
+        // gate-factored operands of this thread's 4 tokens x 4 channels (B1: sub-block 1)
+        auto operands = [&](auto b1_tag, int L, char *PB) {
+            constexpr bool B1 = decltype(b1_tag)::value;
+            bf16 *pQt = (bf16 *)(PB + B_QT), *pKt = (bf16 *)(PB + B_KT), *pKh = (bf16 *)(PB + B_KH);
+            bf16 *pVT = (bf16 *)(PB + B_VT);
+            float4 E1 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (B1) E1 = *(const float4 *)(sG + 15 * G_LD + ch);
+            const float4 e15 = *(const float4 *)(sSc + 0 * D + ch);
+            const float4 sl = *(const float4 *)(sSc + 1 * D + ch);
+            const float E1v[4] = {E1.x, E1.y, E1.z, E1.w}, e15v[4] = {e15.x, e15.y, e15.z, e15.w};
+            const float slv[4] = {sl.x, sl.y, sl.z, sl.w};
+            const bool tail = L < C;
+            float kh[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * tg + r;
+                const float4 Gv = *(const float4 *)(sG + i * G_LD + ch);
+                const float G4[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
+                float qf[4], kf[4];
+                V4::unpack(rq[r], qf);
+                V4::unpack(rk[r], kf);
+                if (tail && i >= L) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { qf[e] = 0.f; kf[e] = 0.f; }
+                }
+                float X[4], Y[4], Z[4], Kb[4], Qt[4], Kt[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f = __builtin_amdgcn_exp2f(G4[e] - E1v[e]);   // e^{G_i - E_b}, in [e^-80, 1]
+                    const float rr = fast_rcp(f);                             // e^{E_b - G_i}, in [1, e^80]
+                    X[e] = kf[e] * f;
+                    Y[e] = qf[e] * f;
+                    Z[e] = kf[e] * rr;
+                    if (!B1) {
+                        Kb[e] = Z[e] * e15v[e];              // k e^{G_15 - G_i} <= 1
+                        kh[r][e] = Kb[e] * slv[e];           // k e^{G_L - G_i}
+                        Kt[e] = -X[e];                       // -k e^{G_i}
+                        Qt[e] = Y[e];                        // q e^{G_i}
+                    } else {
+                        kh[r][e] = Z[e] * slv[e];
+                        Qt[e] = Y[e] * e15v[e];
+                        Kt[e] = -(X[e] * e15v[e]);
+                    }
+                }
+                V4::store(sX + i * X_LD + ch, V4::pack(X));
+                V4::store(sZ + i * X_LD + ch, V4::pack(Z));
+                V4::store(pKt + i * W_LD + ch, V4::pack(Kt));
+                if (has_out) {
+                    V4::store(sY + i * X_LD + ch, V4::pack(Y));
+                    V4::store(pQt + i * W_LD + ch, V4::pack(Qt));
+                }
+                if (!B1) V4::store(sKb + i * X_LD + ch, V4::pack(Kb));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a0[4] = {kh[0][e], kh[1][e], kh[2][e], kh[3][e]};
+                V4::store(pKh + (ch + e) * KH_LD + 4 * tg, V4::pack(a0));
+            }
+            if (has_v) {
+                uint2 vin[4], vt[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vin[r] = (tail && 4 * tg + r >= L) ? make_uint2(0u, 0u) : rv[r];
+                transpose4x4_bf16(vin, vt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) V4::store(pVT + (ch + e) * KH_LD + 4 * tg, vt[e]);
+            }
+        };
+
+        if (nck > 0) {
+            prefetch_g(c_begin);
+            prefetch_qkv(c_begin);
+            scan(c_begin, 0);
+            if (nck > 1) prefetch_g(c_begin + 1);
+        }
+        sync();
+        for (int t = 0; t <= nck; ++t) {
+            const bool pact = t < nck;                           // builds chunk c_begin + t into buffer t % 2
+            const int cur = t & 1;
+            char *PB = smem + cur * B_SIZE;
+            bf16 *pP = (bf16 *)(PB + B_P), *pT = (bf16 *)(PB + B_T);
+            const int pc = c_begin + t, pL = min(C, len - pc * C);
+            const bool more = t + 1 < nck;
+            const float *betac = sBeta + cur * C;
+            // ---------------- interval 1: gate-factored operands of chunk t
+            if (pact) {
+                if (blk == 0) operands(std::false_type{}, pL, PB);
+                else operands(std::true_type{}, pL, PB);
+                if (more) prefetch_qkv(pc + 1);
+            }
+            sync();
+            // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128)
+            if (pact) {
+                // wave 0 -> (0,0) A and P, wave 1 -> (1,0) A and P, wave 2 -> A (1,1), wave 3 -> P (1,1)
+                const int ib = (pw == 0) ? 0 : 1, jb = (pw == 1) ? 0 : ib;
+                const int nitem = (pw <= 1) ? 2 : 1;
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    if (it >= nitem) break;
+                    const int mat = (pw <= 1) ? it : (pw - 2);   // 0: A, 1: P
+                    if (mat == 1 && !has_out) continue;
+                    const bf16 *arow = ((ib == jb) ? sZ : sKb) + (16 * jb + l16) * X_LD;
+                    const bf16 *brow = (mat ? sY : sX) + (16 * ib + l16) * X_LD;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < D / 32; ++s) {
+                        Frag8<bf16> fa, fb;
+                        fa.load8(arow + 32 * s + 8 * g4);
+                        fb.load8(brow + 32 * s + 8 * g4);
+                        mma16(acc, fa, fb);
+                    }
+                    const int i = 16 * ib + l16, j0 = 16 * jb + 4 * g4;
+                    float vals[4];
+                    if (mat == 0) {
+                        const float bi = betac[i];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) vals[r] = (j0 + r < i) ? acc[r] * bi : 0.f;
+                        if (ib == jb)
+                            *(float4 *)(sAd + (ib * 16 + l16) * A_LD + 4 * g4) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                        else
+                            V4::store(sA10 + l16 * A_LD + 4 * g4, V4::pack(vals));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) vals[r] = (j0 + r <= i) ? acc[r] : 0.f;
+                        V4::store(pP + i * P_LD + j0, V4::pack(vals));
+                    }
+                }
+                if (pw == 3 && has_out) V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
+            }
+            sync();
+            // ---------------- interval 3: T diag(beta) of chunk t; gate scan of chunk t+1
+            if (pact && pw == 0) {
+                // diagonal 16x16 blocks of T = (I + A)^-1: lanes 0-15 block 0, lanes 16-31 block 1
+                // (lanes 32-63 repeat them), one column per lane.  Each block splits into 8x8
+                // quarters, T = [[T11, 0], [-T22 A21 T11, T22]]: lanes 0-7 solve T11's columns and
+                // lanes 8-15 T22's by forward substitution, then lanes 0-7 form -T22 (A21 T11).
+                const int b = g4 & 1, col = l16;
+                const float *Ab = sAd + b * 16 * A_LD;
+                const bool lo = col < 8;
+                const int off = lo ? 0 : 8, lc = col - off;
+                float xs[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float arow[8];
+#pragma unroll
+                    for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
+                        const float4 a4 = *(const float4 *)(Ab + (off + i) * A_LD + off + 4 * j4);
+                        arow[4 * j4] = a4.x; arow[4 * j4 + 1] = a4.y; arow[4 * j4 + 2] = a4.z; arow[4 * j4 + 3] = a4.w;
+                    }
+                    float s0 = (i == lc) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int j = 0; j < i; ++j) {
+                        if (j & 1) s1 = fmaf(-arow[j], xs[j], s1);
+                        else s0 = fmaf(-arow[j], xs[j], s0);
+                    }
+                    xs[i] = s0 + s1;
+                }
+                if (!lo && g4 < 2) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sT22[(b * 8 + i) * 8 + lc] = xs[i];
+                }
+                lds_fence();
+                float x[16];
+                if (lo) {
+                    float y[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {       // y = A21 T11[:, col]
+                        const float4 a0 = *(const float4 *)(Ab + (8 + i) * A_LD);
+                        const float4 a1 = *(const float4 *)(Ab + (8 + i) * A_LD + 4);
+                        y[i] = a0.x * xs[0] + a0.y * xs[1] + a0.z * xs[2] + a0.w * xs[3] +
+                               (a1.x * xs[4] + a1.y * xs[5] + a1.z * xs[6] + a1.w * xs[7]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {       // rows 8..15: -T22 y
+                        const float4 t0 = *(const float4 *)(sT22 + (b * 8 + i) * 8);
+                        const float4 t1 = *(const float4 *)(sT22 + (b * 8 + i) * 8 + 4);
+                        x[i] = xs[i];
+                        x[8 + i] = -(t0.x * y[0] + t0.y * y[1] + t0.z * y[2] + t0.w * y[3] +
+                                     (t1.x * y[4] + t1.y * y[5] + t1.z * y[6] + t1.w * y[7]));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) { x[i] = 0.f; x[8 + i] = xs[i]; }
+                }
+                const float bcol = betac[16 * b + col];
+                if (g4 == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) pT[i * P_LD + col] = (bf16)(x[i] * bcol);
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        *(float4 *)(sTd + col * A_LD + 4 * i4) = make_float4(x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]);
+                } else if (g4 == 1) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) pT[(16 + i) * P_LD + 16 + col] = (bf16)x[i];   // unscaled for now
+                } else {
+                    // T block (0,1) is zero
+                    const int idx = lane - 32;
+                    V4::store(pT + (idx >> 1) * P_LD + 16 + 8 * (idx & 1), V4::zero());
+                    V4::store(pT + (idx >> 1) * P_LD + 16 + 8 * (idx & 1) + 4, V4::zero());
+                }
+                lds_fence();
+                // T_10 = -T_11 (A_10 T_00); T_00 from its fp32 transpose
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+                Frag4<bf16> fa, fb;
+                fa.load4(sA10 + l16 * A_LD + 4 * g4);
+                {
+                    const float4 t4 = *(const float4 *)(sTd + l16 * A_LD + 4 * g4);
+                    const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+                    fb.set(tv);
+                }
+                mma16k16(Y, fa, fb);
+                Frag4<bf16> fa2, fy;
+                fa2.load4(pT + (16 + l16) * P_LD + 16 + 4 * g4);
+                const float y4[4] = {Y[0], Y[1], Y[2], Y[3]};
+                fy.set(y4);
+                f32x4 T10 = {0.f, 0.f, 0.f, 0.f};
+                mma16k16(T10, fa2, fy);
+                const float b0col = betac[l16];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pT[(16 + 4 * g4 + r) * P_LD + l16] = (bf16)(-T10[r] * b0col);
+                if (g4 == 1) {     // after the reads of T_11 above (LDS is in order within a wave)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) pT[(16 + i) * P_LD + 16 + col] = (bf16)(x[i] * bcol);
+                }
+            }
+            if (more) scan(pc + 1, t + 1);
+            if (t + 2 < nck) prefetch_g(pc + 2);
+            sync();
+        }
+    } else {
+        // ============================================ consumer waves
+        const int cw = wave;
+        bf16 *ob = has_out ? (bf16 *)p.o + bsel * p.o_sb + h * p.o_sh + t0 * p.o_st : nullptr;
+        f32x16 S[4];
+        const int vcol = 32 * cw + l32;
+        {
+            const float *src = nullptr;
+            int64_t rs = D;
+            if (role == ROLE_OUT && p.s0) {
+                src = p.s0 + n * p.s0_sn + h * p.s0_sh;
+                rs = p.s0_sr;
+            } else if (role == ROLE_SEG_OUT) {
+                src = p.ws_start + ((int64_t)chain * p.nseg + seg) * D * D;
+            }
+            const float one = (role == ROLE_SEG_M) ? 1.f : 0.f;
+            if (src) {              // one straight-line block of 64 loads
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[m][4 * q + r] = src[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol];
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[m][4 * q + r] = (32 * m + 8 * q + 4 * g2 + r == vcol) ? one : 0.f;
+            }
+        }
+        sync();
+        for (int t = 0; t <= nck; ++t) {
+            const bool cact = t >= 1;                       // runs chunk c_begin + t - 1 from buffer (t-1) % 2
+            const char *CB = smem + ((t + 1) & 1) * B_SIZE;
+            const bf16 *cQt = (const bf16 *)(CB + B_QT), *cKt = (const bf16 *)(CB + B_KT);
+            const bf16 *cKh = (const bf16 *)(CB + B_KH), *cVT = (const bf16 *)(CB + B_VT);
+            const bf16 *cP = (const bf16 *)(CB + B_P), *cT = (const bf16 *)(CB + B_T);
+            const float *cDec = sDec + ((t + 2) % 3) * D;   // ring slot (t - 1) % 3
+            const int cc = c_begin + t - 1, ctok0 = cc * C, cL = min(C, len - ctok0);
+            Frag8<bf16> SB[8], UB[2];
+            // ---------------- interval 1: R = V - Kt S, U = (T diag(beta)) R
+            if (cact) {
+                f32x16 R = {};
+                if (has_v) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v4[4];
+                        V4::unpack(*(const uint2 *)(cVT + (32 * cw + l32) * KH_LD + 8 * q + 4 * g2), v4);
+                        R[4 * q] = v4[0]; R[4 * q + 1] = v4[1]; R[4 * q + 2] = v4[2]; R[4 * q + 3] = v4[3];
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    float t8[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t8[e] = S[s >> 1][8 * (s & 1) + e];
+                    SB[s].set(t8);
+                }
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    Frag8<bf16> fa;
+                    const bf16 *row = cKt + l32 * W_LD + 16 * s + 4 * g2;
+                    fa.load44(row, row + 8);
+                    mma32(R, fa, SB[s]);
+                }
+                Frag8<bf16> RB[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    float t8[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t8[e] = R[8 * s + e];
+                    RB[s].set(t8);
+                }
+                f32x16 U = {};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    Frag8<bf16> fa;
+                    const bf16 *row = cT + l32 * P_LD + 16 * s + 4 * g2;
+                    fa.load44(row, row + 8);
+                    mma32(U, fa, RB[s]);
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    float t8[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t8[e] = U[8 * s + e];
+                    UB[s].set(t8);
+                }
+            }
+            sync();
+            // ---------------- interval 2: O = Qt S + P U, stored
+            if (cact && has_out) {
+                f32x16 O = {};
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    Frag8<bf16> fb;
+                    const bf16 *row = cQt + l32 * W_LD + 16 * s + 4 * g2;
+                    fb.load44(row, row + 8);
+                    mma32(O, SB[s], fb);
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    Frag8<bf16> fb;
+                    const bf16 *row = cP + l32 * P_LD + 16 * s + 4 * g2;
+                    fb.load44(row, row + 8);
+                    mma32(O, UB[s], fb);
+                }
+                if (l32 < cL) {
+                    bf16 *dst = ob + (int64_t)(ctok0 + l32) * p.o_st + 32 * cw + 4 * g2;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float o4[4] = {O[4 * q], O[4 * q + 1], O[4 * q + 2], O[4 * q + 3]};
+                        V4::store(dst + 8 * q, V4::pack(o4));
+                    }
+                }
+            }
+            sync();
+            // ---------------- interval 3: S <- Diag(e^{G_L}) S + Kh^T U
+            if (cact) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 d = *(const float4 *)(cDec + 32 * m + 8 * q + 4 * g2);
+                        S[m][4 * q + 0] *= d.x;
+                        S[m][4 * q + 1] *= d.y;
+                        S[m][4 * q + 2] *= d.z;
+                        S[m][4 * q + 3] *= d.w;
+                    }
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        Frag8<bf16> fa;
+                        const bf16 *row = cKh + (32 * m + l32) * KH_LD + 16 * s + 4 * g2;
+                        fa.load44(row, row + 8);
+                        mma32(S[m], fa, UB[s]);
+                    }
+                }
+            }
+            sync();
+        }
+        float *dst = nullptr;
+        int64_t rs = D;
+        if (role == ROLE_OUT || (role == ROLE_SEG_OUT && seg == p.nseg - 1)) {
+            if (p.sT) { dst = p.sT + n * p.sT_sn + h * p.sT_sh; rs = p.sT_sr; }
+        } else if (role == ROLE_SEG_M || role == ROLE_SEG_C) {
+            dst = p.ws_maps + (((int64_t)chain * p.nseg + seg) * 2 + (role == ROLE_SEG_C)) * D * D;
+        }
+        if (dst) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol] = S[m][4 * q + r];
+        }
+    }
+}
+
+}  // namespace pipe
+
+hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStream_t st)
+{
+    if (grid <= 0) return hipSuccess;
+    if (stall) hipLaunchKernelGGL(pipe::chunk_pipe_kernel<true>, dim3(grid), dim3(pipe::NT), 0, st, p);
+    else hipLaunchKernelGGL(pipe::chunk_pipe_kernel<false>, dim3(grid), dim3(pipe::NT), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -191,7 +191,8 @@ struct PrepParams {
     const int32_t *cu;
     int64_t g_sb, g_st, g_sh, y_sb, y_st, y_sh;
     int32_t N, H, T, D;
-    int32_t chunks_per_seq;    // dense layout: ceil(T / 64); packed: unused
+    int32_t chunk;             // tokens per chunk (32 or 64)
+    int32_t chunks_per_seq;    // dense layout: ceil(T / chunk); packed: unused
 };
 
 struct CombineParams {

@@ -6,6 +6,8 @@
 namespace kda {
 // CHUNK kernel, one workgroup per chain / segment (x2 for the segment-build roles).
 hipError_t launch_chunk(const ChunkParams &p, int D, bool fp32, int grid, bool stall, hipStream_t st);
+// Pipelined CHUNK kernel (d = 128, bf16, 32-token chunks), one 512-thread workgroup per chain / segment.
+hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStream_t st);
 // PREP kernel over `nvc` virtual chunks x H heads.
 hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st);
 // COMBINE kernel over chains x D/32 value slabs.

@@ -1,11 +1,11 @@
 // PREP kernel: the in-chunk inclusive cumulative sum of the log decays g.
 //
-// Chunks are 64 tokens and restart at every sequence start, so a chunk never
+// Chunks are `chunk` tokens (the chunk kernel's length) and restart at every sequence start, so a chunk never
 // straddles two sequences -- the "gap-safe virtual chunk mapping" of the
 // cudnn-frontend Hopper KDA prefill PR (#1056, walkthrough).  Virtual chunk v
 // maps to (sequence n, chunk j of n) through the running count of
-// ceil(len_n / 64); the packed layout's grid is the host-known bound
-// ceil(T_tot / 64) + N and the surplus workgroups exit at once.  One thread per
+// ceil(len_n / chunk); the packed layout's grid is the host-known bound
+// ceil(T_tot / chunk) + N and the surplus workgroups exit at once.  One thread per
 // key channel adds the chunk's g values in token order in fp32, the same
 // sequential order the chunk kernel's fused scan uses, so both produce the same
 // bits.
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(128) void prep_kernel(const PrepParams p)
         int carry = 0;
         for (int base = 0; base < p.N; base += nt) {
             const int s = base + tid;
-            const int cnt = (s < p.N) ? (p.cu[s + 1] - p.cu[s] + CHUNK - 1) / CHUNK : 0;
+            const int cnt = (s < p.N) ? (p.cu[s + 1] - p.cu[s] + p.chunk - 1) / p.chunk : 0;
             s_scan[tid] = cnt;
             __syncthreads();
             for (int off = 1; off < nt; off <<= 1) {         // inclusive Hillis-Steele scan
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(128) void prep_kernel(const PrepParams p)
     int64_t t0, bsel;
     int len;
     seq_range(p.cu, n, p.T, t0, len, bsel);
-    const int tok0 = j * CHUNK, L = min(CHUNK, len - tok0);
+    const int tok0 = j * p.chunk, L = min(p.chunk, len - tok0);
     const float *src = p.g + bsel * p.g_sb + h * p.g_sh + (t0 + tok0) * p.g_st + tid;
     float *dst = p.gamma + bsel * p.y_sb + h * p.y_sh + (t0 + tok0) * p.y_st + tid;
     float acc = 0.f;

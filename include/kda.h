@@ -88,6 +88,8 @@ typedef struct {
     int32_t prep;          /* 0 = planner; 1 = standalone PREP kernel; 2 = in-chunk (fused) gate scan */
     int32_t stall_wave;    /* test hook: -1/0 = none; w+1 stalls wave w at every LDS hand-off        */
     int32_t stall_cycles;  /* length of each injected stall, in s_sleep units of 64 cycles           */
+    int32_t variant;       /* 0 = planner; 1 = single-role 64-token chunk kernel; 2 = pipelined      */
+                           /* 32-token chunk kernel (head size 128, bf16 only)                       */
 } kda_options_t;
 
 /*
@@ -126,14 +128,16 @@ kda_status_t kda_prefill_ws(const kda_tensor_t *q, const kda_tensor_t *k, const 
 
 /*
  * kda_prep -- the standalone PREP kernel: the in-chunk inclusive cumulative sum
- * of g over 64-token chunks that restart at every sequence start (the
- * "gap-safe virtual chunk mapping" of the cudnn-frontend PR's walkthrough: a
- * chunk never straddles two sequences).  gamma has g's shape and dtype (fp32),
- * must not overlap g, and receives for token t of chunk [t0, t0 + L):
- *     gamma[t] = (((g[t0] + g[t0+1]) + ...) + g[t])   (fp32 adds in token order).
+ * of g over `chunk`-token chunks (32 or 64) that restart at every sequence
+ * start (the "gap-safe virtual chunk mapping" of the cudnn-frontend PR's
+ * walkthrough: a chunk never straddles two sequences).  gamma has g's shape
+ * and dtype (fp32), must not overlap g, and receives for token t of chunk
+ * [t0, t0 + L):
+ *     gamma[t] = (((g[t0] + g[t0+1]) + ...) + g[t])   (fp32 adds in token order),
+ * the same bits the chunk kernels' fused scan produces.
  */
-kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, kda_tensor_t *gamma,
-                      void *stream);
+kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int32_t chunk,
+                      kda_tensor_t *gamma, void *stream);
 
 /* Frees the workspace cached by kda_prefill on every device. */
 void kda_release_cached_workspace(void);

@@ -115,6 +115,9 @@ def test_edge_shapes_bf16(kda, lengths, H, D):
     x = gen(w)
     out, sT = run(kda, x)
     check_full(x, out, sT, TOL["bf16"])
+    if D == 128:     # the single-role 64-token kernel on the same inputs
+        out1, sT1 = run(kda, x, variant=1)
+        check_full(x, out1, sT1, TOL["bf16"])
 
 
 @pytest.mark.parametrize("lengths,H", [([130, 7], 2), ([64, 1, 200], 1)])
@@ -184,22 +187,26 @@ def test_repeat_runs_bitwise(kda):
         assert torch_equal(o0, o1) and torch_equal(s0, s1)
 
 
+STALLS = [(2, w) for w in range(8)] + [(1, w) for w in range(4)]
+
+
 @pytest.mark.parametrize("layout", ["padded_eqlen", "varlen"])
-@pytest.mark.parametrize("wave", [0, 1, 2, 3])
-def test_stalled_wave_gives_same_bits(kda, layout, wave):
+@pytest.mark.parametrize("variant,wave", STALLS)
+def test_stalled_wave_gives_same_bits(kda, layout, variant, wave):
     """A copy of the kernel with one wave stalled ~20 us after every barrier must
-    reproduce the unstalled bits (the warp-timing test of TensorRT-LLM PR #19826)."""
+    reproduce the unstalled bits (the warp-timing test of TensorRT-LLM PR #19826).
+    Variant 2 (pipelined) has 8 waves: 4 consumers, 4 producers; variant 1 has 4."""
     if layout == "padded_eqlen":
         w = workloads.custom([200] * 3, H=2, D=128, dense=True, seed=8)
     else:
         w = workloads.custom([130, 1, 77, 64], H=2, D=128, seed=8)
     x = gen(w)
-    say("stall", layout, "wave", wave)
-    o0, s0 = run(kda, x, nseg=1)
-    o1, s1 = run(kda, x, nseg=1, stall_wave=wave, stall_cycles=127 * 6)
+    say("stall", layout, "variant", variant, "wave", wave)
+    o0, s0 = run(kda, x, nseg=1, variant=variant)
+    o1, s1 = run(kda, x, nseg=1, variant=variant, stall_wave=wave, stall_cycles=127 * 6)
     assert torch_equal(o0, o1) and torch_equal(s0, s1)
-    o2, s2 = run(kda, x, nseg=3)
-    o3, s3 = run(kda, x, nseg=3, stall_wave=wave, stall_cycles=127 * 6)
+    o2, s2 = run(kda, x, nseg=3, variant=variant)
+    o3, s3 = run(kda, x, nseg=3, variant=variant, stall_wave=wave, stall_cycles=127 * 6)
     assert torch_equal(o2, o3) and torch_equal(s2, s3)
 
 
@@ -244,20 +251,22 @@ def test_dense_equals_packed(kda):
     assert torch_equal(workloads.to_packed(o0), o1) and torch_equal(s0, s1)
 
 
+@pytest.mark.parametrize("variant", [1, 2])
 @pytest.mark.parametrize("nseg", [1, 2, 4, 8])
-def test_forced_segments_match_oracle(kda, nseg):
+def test_forced_segments_match_oracle(kda, nseg, variant):
     w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=12)
     x = gen(w)
-    say("nseg", nseg)
-    out, sT = run(kda, x, nseg=nseg)
+    say("nseg", nseg, "variant", variant)
+    out, sT = run(kda, x, nseg=nseg, variant=variant)
     check_full(x, out, sT, TOL["bf16"])
 
 
-def test_standalone_prep_equals_fused_scan(kda):
+@pytest.mark.parametrize("variant", [1, 2])
+def test_standalone_prep_equals_fused_scan(kda, variant):
     w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=13)
     x = gen(w)
-    o1, s1 = run(kda, x, nseg=1, prep=1)
-    o2, s2 = run(kda, x, nseg=1, prep=2)
+    o1, s1 = run(kda, x, nseg=1, prep=1, variant=variant)
+    o2, s2 = run(kda, x, nseg=1, prep=2, variant=variant)
     assert torch_equal(o1, o2) and torch_equal(s1, s2)
 
 
@@ -273,17 +282,18 @@ def test_in_place_state(kda):
     assert torch_equal(o0, o1) and torch_equal(s0, st)
 
 
+@pytest.mark.parametrize("chunk", [32, 64])
 @pytest.mark.parametrize("dense", [True, False])
-def test_prep_kernel_bit_exact(kda, dense):
-    """PREP output equals a float32 sequential cumsum restarted every 64 tokens
-    of every sequence."""
+def test_prep_kernel_bit_exact(kda, dense, chunk):
+    """PREP output equals a float32 sequential cumsum restarted every `chunk`
+    tokens of every sequence."""
     import torch
     if dense:
         w = workloads.custom([130] * 2, H=3, D=128, dense=True, seed=15)
     else:
         w = workloads.custom([130, 0, 64, 1, 65], H=3, D=128, seed=15)
     x = gen(w)
-    gam = kda.prep(x["g"], x["cu_seqlens"])
+    gam = kda.prep(x["g"], x["cu_seqlens"], chunk=chunk)
     g = x["g"].cpu().numpy()
     got = gam.cpu().numpy()
     if dense:
@@ -294,9 +304,9 @@ def test_prep_kernel_bit_exact(kda, dense):
         cu = x["cu_seqlens"].cpu().numpy()
     want = np.zeros_like(g)
     for n in range(len(cu) - 1):
-        for c0 in range(cu[n], cu[n + 1], 64):
+        for c0 in range(cu[n], cu[n + 1], chunk):
             acc = np.zeros(g.shape[1:], dtype=np.float32)
-            for t in range(c0, min(c0 + 64, cu[n + 1])):
+            for t in range(c0, min(c0 + chunk, cu[n + 1])):
                 acc = (acc + g[t]).astype(np.float32)
                 want[t] = acc
     assert np.array_equal(want.view(np.int32), got.view(np.int32))
