@@ -43,9 +43,12 @@ def algorithmic(w):
 
 
 def source_sha():
+    """Hash of every kernel source: a traffic figure taken on other sources is stale."""
     h = hashlib.sha256()
-    for f in ("kda_chunk.hip", "kda_device.hpp"):
-        h.update(open(os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc", f), "rb").read())
+    d = os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
