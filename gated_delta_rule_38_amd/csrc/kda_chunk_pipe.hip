@@ -13,7 +13,9 @@
 //     never formed);
 //   * 4 producer waves meanwhile build the state-independent operators of the
 //     next chunk: the in-chunk gate scan, the gate-factored operands, A and P on
-//     16x16 MFMA tiles and T diag(beta) with T = (I + A)^-1.
+//     16x16 MFMA tiles, and the diagonal blocks of T diag(beta), T = (I + A)^-1.
+//     Its off-diagonal block is finished a step later by consumer wave 0, whose
+//     share of interval 1 is otherwise short.
 // The roles meet in a double buffer in LDS.  Step t: the producers build chunk
 // t into buffer t%2 while the consumers run chunk t-1 from buffer (t-1)%2.
 // Every wave executes the same three workgroup barriers per step; no buffer is
@@ -22,12 +24,14 @@
 // prefill between a chunk's readers and the next chunk's writers).  A VALU-heavy
 // producer wave and an MFMA-heavy consumer wave share each SIMD.
 //
-//   interval 1: producers -- gate-factored operands of chunk t; q, k, v of t+1 requested
-//               consumers -- R and U of chunk t-1
+//   interval 1: producers -- gate-factored operands of chunk t; raw g of t+1 staged;
+//               q, k, v of t+1 and g of t+2 requested
+//               consumers -- R of chunk t-1; wave 0 also the off-diagonal block of
+//               T diag(beta) of chunk t-1
 //   interval 2: producers -- A, P of chunk t
-//               consumers -- O of chunk t-1 (stored)
-//   interval 3: producer wave 0 -- T diag(beta) of chunk t
-//               producer waves 2, 3 -- gate scan of chunk t+1; g of t+2 requested
+//               consumers -- U and O of chunk t-1 (O stored)
+//   interval 3: producer wave 0 -- diagonal blocks of T diag(beta) of chunk t
+//               producer waves 2, 3 -- gate scan of chunk t+1
 //               consumers -- state update of chunk t-1
 //
 // 32-token chunks hold two 16-token gate sub-blocks: diagonal sub-blocks factor
@@ -50,7 +54,7 @@ constexpr int KH_LD = C + 4;    // Kh^T, V^T [128][32] bf16, 8-byte reads
 constexpr int P_LD = C + 4;     // P, T diag(beta) [32][32] bf16, 8-byte reads
 constexpr int G_LD = D + 4;     // Gamma * log2(e) [32][128] fp32
 constexpr int X_LD = D + 8;     // X, Y, Z, Kb [rows][128] bf16, 16-byte reads
-constexpr int A_LD = 16 + 4;    // 16x16 blocks: A10 (bf16), A diagonal (fp32), T diagonal^T (fp32)
+constexpr int A_LD = 16 + 4;    // 16x16 blocks: A10 (bf16), A diagonal (fp32), T_00 (fp32), T_11 (bf16)
 // one operand buffer (bytes)
 constexpr int B_QT = 0;
 constexpr int B_KT = B_QT + C * W_LD * 2;
@@ -61,23 +65,25 @@ constexpr int B_T = B_P + C * P_LD * 2;
 constexpr int B_SIZE = B_T + C * P_LD * 2;
 // producer scratch
 constexpr int S_G = 2 * B_SIZE;
-constexpr int S_X = S_G + C * G_LD * 4;
+constexpr int S_GRAW = S_G + C * G_LD * 4;   // raw g of the next chunk, staged for the scan
+constexpr int S_X = S_GRAW + C * G_LD * 4;
 constexpr int S_Y = S_X + C * X_LD * 2;
 constexpr int S_Z = S_Y + C * X_LD * 2;
 constexpr int S_KB = S_Z + C * X_LD * 2;
 constexpr int S_A10 = S_KB + 16 * X_LD * 2;
 constexpr int S_AD = S_A10 + 16 * A_LD * 2;
 constexpr int S_TD = S_AD + 2 * 16 * A_LD * 4;
-constexpr int S_T22 = S_TD + 16 * A_LD * 4;
-constexpr int S_SC = S_T22 + 2 * 8 * 8 * 4;
+constexpr int S_T11 = S_TD + 16 * A_LD * 4;
+constexpr int S_SC = S_T11 + 16 * A_LD * 2;
 constexpr int S_DEC = S_SC + 2 * D * 4;       // chunk decays e^{G_L}: a ring of 3 chunks
-constexpr int S_BETA = S_DEC + 3 * D * 4;     // beta: a ring of 2 chunks
-constexpr int SMEM = S_BETA + 2 * C * 4;
+constexpr int S_BETA = S_DEC + 3 * D * 4;     // beta: a ring of 3 chunks
+constexpr int SMEM = S_BETA + 3 * C * 4;
 static_assert(SMEM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-static_assert(B_SIZE % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TD % 16 == 0 &&
-              S_T22 % 16 == 0 && S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
+static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TD % 16 == 0 &&
+              S_T11 % 16 == 0 && S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
 
 typedef Vec4<bf16> V4;
+typedef Vec4<float> V4f;
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -97,14 +103,37 @@ __device__ __forceinline__ void transpose4x4_bf16(const uint2 *in, uint2 *out)
     }
 }
 
+// x += a[lane J of this lane's 16-lane row] * t: one v_fmac with a DPP row broadcast of a.
+// (The compiler does not fold a row-broadcast move into its FMA, and keeping the broadcast
+// values in registers of their own would cost 120 of them.)  The DPP source a is only ever
+// loaded from LDS, never written by a VALU instruction, so no DPP read-after-VALU-write wait
+// states are needed.
+template <int J>
+__device__ __forceinline__ void fmac_row_bcast(float &x, float a, float t)
+{
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(x) : "v"(a), "v"(t), "i"(J));
+}
+
+// Columns J, J-1, ..., 1 of the downward sweep of the 16x16 T solve: x is this lane's row
+// of T, a this lane's row of A; row J of A comes from lane J of the block.
+template <int J>
+__device__ __forceinline__ void tsweep(float (&x)[16], const float (&a)[16])
+{
+    const float ntj = -x[J];
+#pragma unroll
+    for (int c = 0; c < J; ++c) fmac_row_bcast<J>(x[c], a[c], ntj);
+    if constexpr (J > 1) tsweep<J - 1>(x, a);
+}
+
 template <bool STALL>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    float *sG = (float *)(smem + S_G);
+    float *sG = (float *)(smem + S_G), *sGraw = (float *)(smem + S_GRAW);
     bf16 *sX = (bf16 *)(smem + S_X), *sY = (bf16 *)(smem + S_Y), *sZ = (bf16 *)(smem + S_Z);
     bf16 *sKb = (bf16 *)(smem + S_KB), *sA10 = (bf16 *)(smem + S_A10);
-    float *sAd = (float *)(smem + S_AD), *sTd = (float *)(smem + S_TD), *sT22 = (float *)(smem + S_T22);
+    float *sAd = (float *)(smem + S_AD), *sTd = (float *)(smem + S_TD);
+    bf16 *sT11 = (bf16 *)(smem + S_T11);
     float *sSc = (float *)(smem + S_SC), *sDec = (float *)(smem + S_DEC);
     float *sBeta = (float *)(smem + S_BETA);
 
@@ -119,6 +148,75 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             if (wave == p.stall_wave)
                 for (int s = 0; s < p.stall_iters; ++s) __builtin_amdgcn_s_sleep(127);
         }
+    };
+
+    // T diag(beta) of one chunk from its A and beta, into pT, in two parts, each run by one
+    // wave: the diagonal 16x16 blocks (from sAd; also leaves T_00 in sTd and T_11 in sT11)
+    // and, a step later, the off-diagonal block (from sA10, sTd, sT11).
+    auto build_T_diag = [&](const float *betac, bf16 *pT) {
+        // Diagonal 16x16 blocks of T = (I + A)^-1, one row per lane: lanes 0-15 block 0,
+        // lanes 16-31 block 1, lanes 32-63 repeat them.  T = I - T A gives, for row i,
+        // T_ic = [i == c] - sum_{j > c} T_ij A_jc, so column j of the row is final once
+        // the columns after it are folded in: sweeping j downwards, each final T_ij is
+        // folded into the remaining columns with row j of A.  Each lane keeps its own row
+        // of A in registers; row j reaches the other lanes of its block by a DPP
+        // broadcast from lane j of the 16-lane row, so the sweep makes no LDS access.
+        const int b = (lane >> 4) & 1, i = l16;
+        float a[16], bt[16], x[16];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const float4 a4 = *(const float4 *)(sAd + (16 * b + i) * A_LD + 4 * c4);
+            const float4 b4 = *(const float4 *)(betac + 16 * b + 4 * c4);
+            a[4 * c4] = a4.x; a[4 * c4 + 1] = a4.y; a[4 * c4 + 2] = a4.z; a[4 * c4 + 3] = a4.w;
+            bt[4 * c4] = b4.x; bt[4 * c4 + 1] = b4.y; bt[4 * c4 + 2] = b4.z; bt[4 * c4 + 3] = b4.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = (c == i) ? 1.f : 0.f;
+        tsweep<15>(x, a);
+        if (lane < 32) {
+            bf16 *trow = pT + (16 * b + i) * P_LD + 16 * b;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const float tb[4] = {x[4 * c4] * bt[4 * c4], x[4 * c4 + 1] * bt[4 * c4 + 1],
+                                     x[4 * c4 + 2] * bt[4 * c4 + 2], x[4 * c4 + 3] * bt[4 * c4 + 3]};
+                V4::store(trow + 4 * c4, V4::pack(tb));
+            }
+            if (b == 0) {        // T_00 rows, fp32, for the off-diagonal product
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) *(float4 *)(sTd + i * A_LD + 4 * c4) = V4f::pack(x + 4 * c4);
+            } else {             // T_11 rows, bf16
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) V4::store(sT11 + i * A_LD + 4 * c4, V4::pack(x + 4 * c4));
+            }
+        } else if (b == 0) {     // block (0,1) of T is zero
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) V4::store(pT + i * P_LD + 16 + 4 * c4, V4::zero());
+        }
+    };
+    auto build_T_off = [&](const float *betac, bf16 *pT) {
+        // Off-diagonal block T_10 = -T_11 (A_10 T_00), formed transposed so that each lane
+        // ends with four consecutive entries of one row: Y = A_10 T_00 (lane = column of Y),
+        // then Y^T T_11^T = -T_10^T, whose accumulator puts row l16 of T_10 in lane l16.
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+        Frag4<bf16> fa, fb;
+        fa.load4(sA10 + l16 * A_LD + 4 * g4);
+        {
+            const float tv[4] = {sTd[(4 * g4) * A_LD + l16], sTd[(4 * g4 + 1) * A_LD + l16],
+                                 sTd[(4 * g4 + 2) * A_LD + l16], sTd[(4 * g4 + 3) * A_LD + l16]};
+            fb.set(tv);
+        }
+        mma16k16(Y, fa, fb);
+        Frag4<bf16> fy, ft;
+        {
+            const float y4[4] = {Y[0], Y[1], Y[2], Y[3]};
+            fy.set(y4);
+        }
+        ft.load4(sT11 + l16 * A_LD + 4 * g4);
+        f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+        mma16k16(Z, fy, ft);
+        const float4 b4 = *(const float4 *)(betac + 4 * g4);
+        const float z4[4] = {-Z[0] * b4.x, -Z[1] * b4.y, -Z[2] * b4.z, -Z[3] * b4.w};
+        V4::store(pT + (16 + l16) * P_LD + 4 * g4, V4::pack(z4));
     };
 
     // ------------------------------------------------ chain / segment
@@ -155,23 +253,25 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         const float *gb = p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st;
         const float *bb = p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st;
 
-        float rg[C];                    // scan threads: one channel's g over the chunk
         uint2 rq[4], rk[4], rv[4];      // 4 tokens x 4 channels of q, k, v (bf16)
-        float rbeta = 0.f;
-        // Loads are unconditional from always in-bounds addresses (the rows of a
-        // short last chunk re-read its last token) so that no load sits in a
-        // branch whose merge would force a wait; such rows are zeroed at use.
+        float rgv[16];                  // g of 4 tokens x 4 channels (rows gr, gr+8, gr+16, gr+24)
+        float rbeta;                    // beta of token gc
+        const int gr = pt >> 5, gc = pt & 31;
+        // Every producer thread issues the same loads, from always in-bounds addresses (the
+        // rows of a short last chunk re-read its last token; chunks past the segment's end
+        // re-read its last chunk), all in interval 1, and consumes them at the start of the
+        // next step's interval 1.  Whatever wait the compiler places before a use then only
+        // covers loads issued a whole step earlier: its bookkeeping of outstanding loads
+        // across the loop's branches is conservative, and a wait that also covered younger
+        // loads would expose their full memory latency.
         auto prefetch_g = [&](int c) {
             const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
-            if (sc >= 0) {
-                const float *gs = gb + (int64_t)tok0 * p.g_st + sc;
 #pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    rg[i] = *gs;
-                    if (i < Lm1) gs += p.g_st;
-                }
+            for (int k = 0; k < 4; ++k) {
+                const float4 v = *(const float4 *)(gb + (int64_t)(tok0 + min(gr + 8 * k, Lm1)) * p.g_st + 4 * gc);
+                rgv[4 * k] = v.x; rgv[4 * k + 1] = v.y; rgv[4 * k + 2] = v.z; rgv[4 * k + 3] = v.w;
             }
-            if (pt < C) rbeta = bb[(int64_t)(tok0 + min(pt, Lm1)) * p.b_st];
+            rbeta = bb[(int64_t)(tok0 + min(gc, Lm1)) * p.b_st];
         };
         auto prefetch_qkv = [&](int c) {
             const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
@@ -190,18 +290,40 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 vs += adv ? p.v_st : 0;
             }
         };
-        // gate scan of chunk c (the t-th of this segment) into Gamma * log2(e), the
-        // per-channel scales, decay ring slot t % 3 and beta ring slot t % 2
+        // raw g of chunk c (the t-th of this segment) into the staging buffer, beta into ring slot t % 3
+        auto stage_g = [&](int c, int t) {
+            const int L = min(C, len - c * C);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) *(float4 *)(sGraw + (gr + 8 * k) * G_LD + 4 * gc) = V4f::pack(rgv + 4 * k);
+            if (pt < C) sBeta[(t % 3) * C + pt] = (pt < L) ? rbeta : 0.f;
+        };
+        // gate scan of the staged chunk c (the t-th of this segment) into Gamma * log2(e),
+        // plus the per-channel scales and decay ring slot t % 3
         auto scan = [&](int c, int t) {
-            const int buf = t & 1;
             const int L = min(C, len - c * C);
             if (sc >= 0) {
-                float acc = 0.f;
+                float rg[C];
 #pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    if (p.g_is_gamma) acc = (i < L) ? rg[i] : acc;      // tail rows hold Gamma_{L-1}
-                    else acc = acc + ((i < L) ? rg[i] : 0.f);           // fp32 adds in token order
-                    rg[i] = acc * LOG2E;
+                for (int i = 0; i < C; ++i) rg[i] = sGraw[i * G_LD + sc];
+                // tail rows re-read token L-1 (clamped loads), so a precomputed Gamma needs
+                // no select there; the cumsum skips them so they hold Gamma_{L-1}
+                if (p.g_is_gamma) {
+#pragma unroll
+                    for (int i = 0; i < C; ++i) rg[i] *= LOG2E;
+                } else if (L == C) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < C; ++i) {
+                        acc += rg[i];                                   // fp32 adds in token order
+                        rg[i] = acc * LOG2E;
+                    }
+                } else {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < C; ++i) {
+                        acc += (i < L) ? rg[i] : 0.f;
+                        rg[i] = acc * LOG2E;
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < C; ++i) sG[i * G_LD + sc] = rg[i];
@@ -209,10 +331,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 sSc[1 * D + sc] = __builtin_amdgcn_exp2f(rg[31] - rg[15]);     // e^{G_L - G_15}
                 sDec[(t % 3) * D + sc] = __builtin_amdgcn_exp2f(rg[31]);             // e^{G_L}
             }
-            if (pt < C) sBeta[buf * C + pt] = (pt < L) ? rbeta : 0.f;
         };
         // gate-factored operands of this thread's 4 tokens x 4 channels (B1: sub-block 1)
-        auto operands = [&](auto b1_tag, int L, char *PB) {
+        auto operands = [&](auto b1_tag, char *PB) {
             constexpr bool B1 = decltype(b1_tag)::value;
             bf16 *pQt = (bf16 *)(PB + B_QT), *pKt = (bf16 *)(PB + B_KT), *pKh = (bf16 *)(PB + B_KH);
             bf16 *pVT = (bf16 *)(PB + B_VT);
@@ -222,7 +343,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const float4 sl = *(const float4 *)(sSc + 1 * D + ch);
             const float E1v[4] = {E1.x, E1.y, E1.z, E1.w}, e15v[4] = {e15.x, e15.y, e15.z, e15.w};
             const float slv[4] = {sl.x, sl.y, sl.z, sl.w};
-            const bool tail = L < C;
+            // Rows past a short chunk's end hold finite copies of token L-1: with beta = 0
+            // there, T diag(beta) has zero rows and columns, so they enter U, O and S only
+            // through exact zeros and need no masking.
             float kh[4][4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -232,10 +355,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 float qf[4], kf[4];
                 V4::unpack(rq[r], qf);
                 V4::unpack(rk[r], kf);
-                if (tail && i >= L) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { qf[e] = 0.f; kf[e] = 0.f; }
-                }
                 float X[4], Y[4], Z[4], Kb[4], Qt[4], Kt[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -270,36 +389,39 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 V4::store(pKh + (ch + e) * KH_LD + 4 * tg, V4::pack(a0));
             }
             if (has_v) {
-                uint2 vin[4], vt[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vin[r] = (tail && 4 * tg + r >= L) ? make_uint2(0u, 0u) : rv[r];
-                transpose4x4_bf16(vin, vt);
+                uint2 vt[4];
+                transpose4x4_bf16(rv, vt);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) V4::store(pVT + (ch + e) * KH_LD + 4 * tg, vt[e]);
             }
         };
 
+        const int c_last = c_end - 1;
         if (nck > 0) {
             prefetch_g(c_begin);
             prefetch_qkv(c_begin);
-            scan(c_begin, 0);
-            if (nck > 1) prefetch_g(c_begin + 1);
+            stage_g(c_begin, 0);
+            prefetch_g(min(c_begin + 1, c_last));
         }
         sync();
-        for (int t = 0; t <= nck; ++t) {
+        if (nck > 0) scan(c_begin, 0);
+        sync();
+        for (int t = 0; nck > 0 && t <= nck; ++t) {
             const bool pact = t < nck;                           // builds chunk c_begin + t into buffer t % 2
             const int cur = t & 1;
             char *PB = smem + cur * B_SIZE;
             bf16 *pP = (bf16 *)(PB + B_P), *pT = (bf16 *)(PB + B_T);
             const int pc = c_begin + t, pL = min(C, len - pc * C);
             const bool more = t + 1 < nck;
-            const float *betac = sBeta + cur * C;
-            // ---------------- interval 1: gate-factored operands of chunk t
+            const float *betac = sBeta + (t % 3) * C;
+            // ---------------- interval 1: gate-factored operands of chunk t; g of t+1 staged
+            stage_g(min(pc + 1, c_last), t + 1);
+            prefetch_g(min(pc + 2, c_last));
             if (pact) {
-                if (blk == 0) operands(std::false_type{}, pL, PB);
-                else operands(std::true_type{}, pL, PB);
-                if (more) prefetch_qkv(pc + 1);
+                if (blk == 0) operands(std::false_type{}, PB);
+                else operands(std::true_type{}, PB);
             }
+            prefetch_qkv(min(pc + 1, c_last));
             sync();
             // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128)
             if (pact) {
@@ -340,103 +462,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 if (pw == 3 && has_out) V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
             }
             sync();
-            // ---------------- interval 3: T diag(beta) of chunk t; gate scan of chunk t+1
-            if (pact && pw == 0) {
-                // diagonal 16x16 blocks of T = (I + A)^-1: lanes 0-15 block 0, lanes 16-31 block 1
-                // (lanes 32-63 repeat them), one column per lane.  Each block splits into 8x8
-                // quarters, T = [[T11, 0], [-T22 A21 T11, T22]]: lanes 0-7 solve T11's columns and
-                // lanes 8-15 T22's by forward substitution, then lanes 0-7 form -T22 (A21 T11).
-                const int b = g4 & 1, col = l16;
-                const float *Ab = sAd + b * 16 * A_LD;
-                const bool lo = col < 8;
-                const int off = lo ? 0 : 8, lc = col - off;
-                float xs[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float arow[8];
-#pragma unroll
-                    for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
-                        const float4 a4 = *(const float4 *)(Ab + (off + i) * A_LD + off + 4 * j4);
-                        arow[4 * j4] = a4.x; arow[4 * j4 + 1] = a4.y; arow[4 * j4 + 2] = a4.z; arow[4 * j4 + 3] = a4.w;
-                    }
-                    float s0 = (i == lc) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-                    for (int j = 0; j < i; ++j) {
-                        if (j & 1) s1 = fmaf(-arow[j], xs[j], s1);
-                        else s0 = fmaf(-arow[j], xs[j], s0);
-                    }
-                    xs[i] = s0 + s1;
-                }
-                if (!lo && g4 < 2) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) sT22[(b * 8 + i) * 8 + lc] = xs[i];
-                }
-                lds_fence();
-                float x[16];
-                if (lo) {
-                    float y[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {       // y = A21 T11[:, col]
-                        const float4 a0 = *(const float4 *)(Ab + (8 + i) * A_LD);
-                        const float4 a1 = *(const float4 *)(Ab + (8 + i) * A_LD + 4);
-                        y[i] = a0.x * xs[0] + a0.y * xs[1] + a0.z * xs[2] + a0.w * xs[3] +
-                               (a1.x * xs[4] + a1.y * xs[5] + a1.z * xs[6] + a1.w * xs[7]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {       // rows 8..15: -T22 y
-                        const float4 t0 = *(const float4 *)(sT22 + (b * 8 + i) * 8);
-                        const float4 t1 = *(const float4 *)(sT22 + (b * 8 + i) * 8 + 4);
-                        x[i] = xs[i];
-                        x[8 + i] = -(t0.x * y[0] + t0.y * y[1] + t0.z * y[2] + t0.w * y[3] +
-                                     (t1.x * y[4] + t1.y * y[5] + t1.z * y[6] + t1.w * y[7]));
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) { x[i] = 0.f; x[8 + i] = xs[i]; }
-                }
-                const float bcol = betac[16 * b + col];
-                if (g4 == 0) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) pT[i * P_LD + col] = (bf16)(x[i] * bcol);
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4)
-                        *(float4 *)(sTd + col * A_LD + 4 * i4) = make_float4(x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]);
-                } else if (g4 == 1) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) pT[(16 + i) * P_LD + 16 + col] = (bf16)x[i];   // unscaled for now
-                } else {
-                    // T block (0,1) is zero
-                    const int idx = lane - 32;
-                    V4::store(pT + (idx >> 1) * P_LD + 16 + 8 * (idx & 1), V4::zero());
-                    V4::store(pT + (idx >> 1) * P_LD + 16 + 8 * (idx & 1) + 4, V4::zero());
-                }
-                lds_fence();
-                // T_10 = -T_11 (A_10 T_00); T_00 from its fp32 transpose
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-                Frag4<bf16> fa, fb;
-                fa.load4(sA10 + l16 * A_LD + 4 * g4);
-                {
-                    const float4 t4 = *(const float4 *)(sTd + l16 * A_LD + 4 * g4);
-                    const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
-                    fb.set(tv);
-                }
-                mma16k16(Y, fa, fb);
-                Frag4<bf16> fa2, fy;
-                fa2.load4(pT + (16 + l16) * P_LD + 16 + 4 * g4);
-                const float y4[4] = {Y[0], Y[1], Y[2], Y[3]};
-                fy.set(y4);
-                f32x4 T10 = {0.f, 0.f, 0.f, 0.f};
-                mma16k16(T10, fa2, fy);
-                const float b0col = betac[l16];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pT[(16 + 4 * g4 + r) * P_LD + l16] = (bf16)(-T10[r] * b0col);
-                if (g4 == 1) {     // after the reads of T_11 above (LDS is in order within a wave)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) pT[(16 + i) * P_LD + 16 + col] = (bf16)(x[i] * bcol);
-                }
-            }
+            // ---------------- interval 3: diagonal blocks of T diag(beta) of chunk t; gate scan of chunk t+1
+            if (pact && pw == 0) build_T_diag(betac, pT);
             if (more) scan(pc + 1, t + 1);
-            if (t + 2 < nck) prefetch_g(pc + 2);
             sync();
         }
     } else {
@@ -472,16 +500,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             }
         }
         sync();
-        for (int t = 0; t <= nck; ++t) {
+        sync();
+        for (int t = 0; nck > 0 && t <= nck; ++t) {
             const bool cact = t >= 1;                       // runs chunk c_begin + t - 1 from buffer (t-1) % 2
-            const char *CB = smem + ((t + 1) & 1) * B_SIZE;
+            char *CB = smem + ((t + 1) & 1) * B_SIZE;
             const bf16 *cQt = (const bf16 *)(CB + B_QT), *cKt = (const bf16 *)(CB + B_KT);
             const bf16 *cKh = (const bf16 *)(CB + B_KH), *cVT = (const bf16 *)(CB + B_VT);
             const bf16 *cP = (const bf16 *)(CB + B_P), *cT = (const bf16 *)(CB + B_T);
             const float *cDec = sDec + ((t + 2) % 3) * D;   // ring slot (t - 1) % 3
             const int cc = c_begin + t - 1, ctok0 = cc * C, cL = min(C, len - ctok0);
             Frag8<bf16> SB[8], UB[2];
-            // ---------------- interval 1: R = V - Kt S, U = (T diag(beta)) R
+            // ---------------- interval 1: R = V - Kt S; wave 0 also finishes T diag(beta) of the chunk
+            Frag8<bf16> RB[2];
             if (cact) {
                 f32x16 R = {};
                 if (has_v) {
@@ -506,7 +536,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     fa.load44(row, row + 8);
                     mma32(R, fa, SB[s]);
                 }
-                Frag8<bf16> RB[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     float t8[8];
@@ -514,6 +543,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     for (int e = 0; e < 8; ++e) t8[e] = R[8 * s + e];
                     RB[s].set(t8);
                 }
+                if (cw == 0) build_T_off(sBeta + ((t + 2) % 3) * C, (bf16 *)(CB + B_T));
+            }
+            sync();
+            // ---------------- interval 2: U = (T diag(beta)) R; O = Qt S + P U, stored
+            if (cact) {
                 f32x16 U = {};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -530,8 +564,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     UB[s].set(t8);
                 }
             }
-            sync();
-            // ---------------- interval 2: O = Qt S + P U, stored
             if (cact && has_out) {
                 f32x16 O = {};
 #pragma unroll
