@@ -12,10 +12,11 @@
 //     Ut = T diag(beta) V and W = T diag(beta) Kt folded together, so W is
 //     never formed);
 //   * 4 producer waves meanwhile build the state-independent operators of the
-//     next chunk: the in-chunk gate scan, the gate-factored operands, A and P on
-//     16x16 MFMA tiles, and the diagonal blocks of T diag(beta), T = (I + A)^-1.
-//     Its off-diagonal block is finished a step later by consumer wave 0, whose
-//     share of interval 1 is otherwise short.
+//     next chunk: the in-chunk gate scan, A and P on 16x16 MFMA tiles, and the
+//     diagonal blocks of T diag(beta), T = (I + A)^-1.  The gate-factored operands
+//     are built by all 8 waves (consumers: gate sub-block 0, producers: sub-block 1),
+//     and the off-diagonal block of T diag(beta) is finished a step later by
+//     consumer wave 0: the consumers' own share of interval 1 is short.
 // The roles meet in a double buffer in LDS.  Step t: the producers build chunk
 // t into buffer t%2 while the consumers run chunk t-1 from buffer (t-1)%2.
 // Every wave executes the same three workgroup barriers per step; no buffer is
@@ -24,8 +25,8 @@
 // prefill between a chunk's readers and the next chunk's writers).  A VALU-heavy
 // producer wave and an MFMA-heavy consumer wave share each SIMD.
 //
-//   interval 1: producers -- gate-factored operands of chunk t; raw g of t+1 staged;
-//               q, k, v of t+1 and g of t+2 requested
+//   interval 1: all waves -- gate-factored operands of chunk t; q, k, v of t+1 requested
+//               producers -- raw g of t+1 staged, g of t+2 requested
 //               consumers -- R of chunk t-1; wave 0 also the off-diagonal block of
 //               T diag(beta) of chunk t-1
 //   interval 2: producers -- A, P of chunk t
@@ -84,6 +85,7 @@ static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 1
 
 typedef Vec4<bf16> V4;
 typedef Vec4<float> V4f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -121,7 +123,7 @@ __device__ __forceinline__ void tsweep(float (&x)[16], const float (&a)[16])
 {
     const float ntj = -x[J];
 #pragma unroll
-    for (int c = 0; c < J; ++c) fmac_row_bcast<J>(x[c], a[c], ntj);
+    for (int c = J - 1; c >= 0; --c) fmac_row_bcast<J>(x[c], a[c], ntj);   // column J-1 first: the next pivot
     if constexpr (J > 1) tsweep<J - 1>(x, a);
 }
 
@@ -240,24 +242,107 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     const bool has_out = (role == ROLE_OUT || role == ROLE_SEG_OUT);
     const bool has_v = (role != ROLE_SEG_M);
 
+    // ------------------------------------------------ gate-factored operands (all waves)
+    // Thread tid handles tokens 2*(tid>>5) and 2*(tid>>5)+1, channels 4*(tid&31)..+3 of a
+    // chunk: the consumer waves gate sub-block 0, the producer waves sub-block 1.
+    const int etp = tid >> 5, ech = 4 * (tid & 31);
+    const bf16 *qb = (const bf16 *)p.q + bsel * p.q_sb + h * p.q_sh + t0 * p.q_st;
+    const bf16 *kb = (const bf16 *)p.k + bsel * p.k_sb + h * p.k_sh + t0 * p.k_st;
+    const bf16 *vb = (const bf16 *)p.v + bsel * p.v_sb + h * p.v_sh + t0 * p.v_st;
+    uint2 rq[2], rk[2], rv[2];          // 2 tokens x 4 channels of q, k, v (bf16)
+    auto prefetch_qkv = [&](int c) {
+        const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int64_t row = tok0 + min(2 * etp + r, Lm1);
+            rq[r] = *(const uint2 *)(qb + row * p.q_st + ech);
+            rk[r] = *(const uint2 *)(kb + row * p.k_st + ech);
+            rv[r] = *(const uint2 *)(vb + row * p.v_st + ech);
+        }
+    };
+    // B1: sub-block 1.  Rows past a short chunk's end hold finite copies of token L-1: with
+    // beta = 0 there, T diag(beta) has zero rows and columns, so they enter U, O and S only
+    // through exact zeros and need no masking.
+    auto operands = [&](auto b1_tag, char *PB) {
+        constexpr bool B1 = decltype(b1_tag)::value;
+        bf16 *pQt = (bf16 *)(PB + B_QT), *pKt = (bf16 *)(PB + B_KT), *pKh = (bf16 *)(PB + B_KH);
+        bf16 *pVT = (bf16 *)(PB + B_VT);
+        float4 E1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (B1) E1 = *(const float4 *)(sG + 15 * G_LD + ech);
+        const float4 e15 = *(const float4 *)(sSc + 0 * D + ech);
+        const float4 sl = *(const float4 *)(sSc + 1 * D + ech);
+        const float E1v[4] = {E1.x, E1.y, E1.z, E1.w}, e15v[4] = {e15.x, e15.y, e15.z, e15.w};
+        const float slv[4] = {sl.x, sl.y, sl.z, sl.w};
+        float kh[2][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = 2 * etp + r;
+            const float4 Gv = *(const float4 *)(sG + i * G_LD + ech);
+            const float G4[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
+            float qf[4], kf[4];
+            V4::unpack(rq[r], qf);
+            V4::unpack(rk[r], kf);
+            float X[4], Y[4], Z[4], Kb[4], Qt[4], Kt[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = __builtin_amdgcn_exp2f(G4[e] - E1v[e]);   // e^{G_i - E_b}, in [e^-80, 1]
+                const float rr = fast_rcp(f);                             // e^{E_b - G_i}, in [1, e^80]
+                X[e] = kf[e] * f;
+                Y[e] = qf[e] * f;
+                Z[e] = kf[e] * rr;
+                if (!B1) {
+                    Kb[e] = Z[e] * e15v[e];              // k e^{G_15 - G_i} <= 1
+                    kh[r][e] = Kb[e] * slv[e];           // k e^{G_L - G_i}
+                    Kt[e] = -X[e];                       // -k e^{G_i}
+                    Qt[e] = Y[e];                        // q e^{G_i}
+                } else {
+                    kh[r][e] = Z[e] * slv[e];
+                    Qt[e] = Y[e] * e15v[e];
+                    Kt[e] = -(X[e] * e15v[e]);
+                }
+            }
+            V4::store(sX + i * X_LD + ech, V4::pack(X));
+            V4::store(sZ + i * X_LD + ech, V4::pack(Z));
+            V4::store(pKt + i * W_LD + ech, V4::pack(Kt));
+            if (has_out) {
+                V4::store(sY + i * X_LD + ech, V4::pack(Y));
+                V4::store(pQt + i * W_LD + ech, V4::pack(Qt));
+            }
+            if (!B1) V4::store(sKb + i * X_LD + ech, V4::pack(Kb));
+        }
+        // transposed tiles: channel rows of Kh^T and V^T get this thread's 2 tokens
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bf16x2 kp;
+            kp[0] = (bf16)kh[0][e];
+            kp[1] = (bf16)kh[1][e];
+            *(uint32_t *)(pKh + (ech + e) * KH_LD + 2 * etp) = __builtin_bit_cast(uint32_t, kp);
+        }
+        if (has_v) {
+            // selector 0x05040100 pairs the low bf16 of (rv[0], rv[1]), 0x07060302 the high ones
+            const uint32_t v0 = __builtin_amdgcn_perm(rv[1].x, rv[0].x, 0x05040100u);
+            const uint32_t v1 = __builtin_amdgcn_perm(rv[1].x, rv[0].x, 0x07060302u);
+            const uint32_t v2 = __builtin_amdgcn_perm(rv[1].y, rv[0].y, 0x05040100u);
+            const uint32_t v3 = __builtin_amdgcn_perm(rv[1].y, rv[0].y, 0x07060302u);
+            *(uint32_t *)(pVT + (ech + 0) * KH_LD + 2 * etp) = v0;
+            *(uint32_t *)(pVT + (ech + 1) * KH_LD + 2 * etp) = v1;
+            *(uint32_t *)(pVT + (ech + 2) * KH_LD + 2 * etp) = v2;
+            *(uint32_t *)(pVT + (ech + 3) * KH_LD + 2 * etp) = v3;
+        }
+    };
+    const int c_last = c_end - 1;
+
     if (producer) {
         // ============================================ producer waves
         const int pt = tid - 256, pw = wave - 4;
-        const int cg = pt & 31, tg = pt >> 5;                      // elementwise: 4 channels x 4 tokens
-        const int blk = __builtin_amdgcn_readfirstlane(tg >> 2);   // 16-token sub-block, uniform per wave
-        const int ch = 4 * cg;
         const int sc = pt - 128;                                   // scan threads (waves 6, 7): one key channel each
-        const bf16 *qb = (const bf16 *)p.q + bsel * p.q_sb + h * p.q_sh + t0 * p.q_st;
-        const bf16 *kb = (const bf16 *)p.k + bsel * p.k_sb + h * p.k_sh + t0 * p.k_st;
-        const bf16 *vb = (const bf16 *)p.v + bsel * p.v_sb + h * p.v_sh + t0 * p.v_st;
         const float *gb = p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st;
         const float *bb = p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st;
 
-        uint2 rq[4], rk[4], rv[4];      // 4 tokens x 4 channels of q, k, v (bf16)
         float rgv[16];                  // g of 4 tokens x 4 channels (rows gr, gr+8, gr+16, gr+24)
         float rbeta;                    // beta of token gc
         const int gr = pt >> 5, gc = pt & 31;
-        // Every producer thread issues the same loads, from always in-bounds addresses (the
+        // Every thread of a role issues the same loads, from always in-bounds addresses (the
         // rows of a short last chunk re-read its last token; chunks past the segment's end
         // re-read its last chunk), all in interval 1, and consumes them at the start of the
         // next step's interval 1.  Whatever wait the compiler places before a use then only
@@ -272,23 +357,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 rgv[4 * k] = v.x; rgv[4 * k + 1] = v.y; rgv[4 * k + 2] = v.z; rgv[4 * k + 3] = v.w;
             }
             rbeta = bb[(int64_t)(tok0 + min(gc, Lm1)) * p.b_st];
-        };
-        auto prefetch_qkv = [&](int c) {
-            const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
-            const int r0 = min(4 * tg, Lm1);
-            const bf16 *qs = qb + (int64_t)(tok0 + r0) * p.q_st + ch;
-            const bf16 *ks = kb + (int64_t)(tok0 + r0) * p.k_st + ch;
-            const bf16 *vs = vb + (int64_t)(tok0 + r0) * p.v_st + ch;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                rq[r] = *(const uint2 *)qs;
-                rk[r] = *(const uint2 *)ks;
-                rv[r] = *(const uint2 *)vs;
-                const bool adv = 4 * tg + r < Lm1;
-                qs += adv ? p.q_st : 0;
-                ks += adv ? p.k_st : 0;
-                vs += adv ? p.v_st : 0;
-            }
         };
         // raw g of chunk c (the t-th of this segment) into the staging buffer, beta into ring slot t % 3
         auto stage_g = [&](int c, int t) {
@@ -332,71 +400,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 sDec[(t % 3) * D + sc] = __builtin_amdgcn_exp2f(rg[31]);             // e^{G_L}
             }
         };
-        // gate-factored operands of this thread's 4 tokens x 4 channels (B1: sub-block 1)
-        auto operands = [&](auto b1_tag, char *PB) {
-            constexpr bool B1 = decltype(b1_tag)::value;
-            bf16 *pQt = (bf16 *)(PB + B_QT), *pKt = (bf16 *)(PB + B_KT), *pKh = (bf16 *)(PB + B_KH);
-            bf16 *pVT = (bf16 *)(PB + B_VT);
-            float4 E1 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (B1) E1 = *(const float4 *)(sG + 15 * G_LD + ch);
-            const float4 e15 = *(const float4 *)(sSc + 0 * D + ch);
-            const float4 sl = *(const float4 *)(sSc + 1 * D + ch);
-            const float E1v[4] = {E1.x, E1.y, E1.z, E1.w}, e15v[4] = {e15.x, e15.y, e15.z, e15.w};
-            const float slv[4] = {sl.x, sl.y, sl.z, sl.w};
-            // Rows past a short chunk's end hold finite copies of token L-1: with beta = 0
-            // there, T diag(beta) has zero rows and columns, so they enter U, O and S only
-            // through exact zeros and need no masking.
-            float kh[4][4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * tg + r;
-                const float4 Gv = *(const float4 *)(sG + i * G_LD + ch);
-                const float G4[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
-                float qf[4], kf[4];
-                V4::unpack(rq[r], qf);
-                V4::unpack(rk[r], kf);
-                float X[4], Y[4], Z[4], Kb[4], Qt[4], Kt[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float f = __builtin_amdgcn_exp2f(G4[e] - E1v[e]);   // e^{G_i - E_b}, in [e^-80, 1]
-                    const float rr = fast_rcp(f);                             // e^{E_b - G_i}, in [1, e^80]
-                    X[e] = kf[e] * f;
-                    Y[e] = qf[e] * f;
-                    Z[e] = kf[e] * rr;
-                    if (!B1) {
-                        Kb[e] = Z[e] * e15v[e];              // k e^{G_15 - G_i} <= 1
-                        kh[r][e] = Kb[e] * slv[e];           // k e^{G_L - G_i}
-                        Kt[e] = -X[e];                       // -k e^{G_i}
-                        Qt[e] = Y[e];                        // q e^{G_i}
-                    } else {
-                        kh[r][e] = Z[e] * slv[e];
-                        Qt[e] = Y[e] * e15v[e];
-                        Kt[e] = -(X[e] * e15v[e]);
-                    }
-                }
-                V4::store(sX + i * X_LD + ch, V4::pack(X));
-                V4::store(sZ + i * X_LD + ch, V4::pack(Z));
-                V4::store(pKt + i * W_LD + ch, V4::pack(Kt));
-                if (has_out) {
-                    V4::store(sY + i * X_LD + ch, V4::pack(Y));
-                    V4::store(pQt + i * W_LD + ch, V4::pack(Qt));
-                }
-                if (!B1) V4::store(sKb + i * X_LD + ch, V4::pack(Kb));
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a0[4] = {kh[0][e], kh[1][e], kh[2][e], kh[3][e]};
-                V4::store(pKh + (ch + e) * KH_LD + 4 * tg, V4::pack(a0));
-            }
-            if (has_v) {
-                uint2 vt[4];
-                transpose4x4_bf16(rv, vt);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) V4::store(pVT + (ch + e) * KH_LD + 4 * tg, vt[e]);
-            }
-        };
-
-        const int c_last = c_end - 1;
         if (nck > 0) {
             prefetch_g(c_begin);
             prefetch_qkv(c_begin);
@@ -411,16 +414,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const int cur = t & 1;
             char *PB = smem + cur * B_SIZE;
             bf16 *pP = (bf16 *)(PB + B_P), *pT = (bf16 *)(PB + B_T);
-            const int pc = c_begin + t, pL = min(C, len - pc * C);
+            const int pc = c_begin + t;
             const bool more = t + 1 < nck;
             const float *betac = sBeta + (t % 3) * C;
             // ---------------- interval 1: gate-factored operands of chunk t; g of t+1 staged
             stage_g(min(pc + 1, c_last), t + 1);
             prefetch_g(min(pc + 2, c_last));
-            if (pact) {
-                if (blk == 0) operands(std::false_type{}, PB);
-                else operands(std::true_type{}, PB);
-            }
+            if (pact) operands(std::true_type{}, PB);
             prefetch_qkv(min(pc + 1, c_last));
             sync();
             // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128)
@@ -499,6 +499,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                         for (int r = 0; r < 4; ++r) S[m][4 * q + r] = (32 * m + 8 * q + 4 * g2 + r == vcol) ? one : 0.f;
             }
         }
+        if (nck > 0) prefetch_qkv(c_begin);
         sync();
         sync();
         for (int t = 0; nck > 0 && t <= nck; ++t) {
@@ -510,7 +511,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const float *cDec = sDec + ((t + 2) % 3) * D;   // ring slot (t - 1) % 3
             const int cc = c_begin + t - 1, ctok0 = cc * C, cL = min(C, len - ctok0);
             Frag8<bf16> SB[8], UB[2];
-            // ---------------- interval 1: R = V - Kt S; wave 0 also finishes T diag(beta) of the chunk
+            // ---------------- interval 1: sub-block 0 operands of chunk t into buffer t % 2;
+            //                  R = V - Kt S; wave 0 also finishes T diag(beta) of the chunk
+            if (t < nck) operands(std::false_type{}, smem + (t & 1) * B_SIZE);
+            prefetch_qkv(min(c_begin + t + 1, c_last));
             Frag8<bf16> RB[2];
             if (cact) {
                 f32x16 R = {};
