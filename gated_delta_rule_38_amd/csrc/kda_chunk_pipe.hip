@@ -51,7 +51,7 @@ constexpr int D = 128;
 constexpr int NT = 512;         // 4 consumer + 4 producer waves
 // leading dimensions (elements); padding matches each tile's read width
 constexpr int W_LD = D + 4;     // Qt, -Kt [32][128] bf16, 8-byte reads
-constexpr int KH_LD = C + 4;    // Kh^T, V^T [128][32] bf16, 8-byte reads
+constexpr int KR_LD = D + 16;   // Kh, V [32][128] bf16, row-major, read transposed (4 rows x 32 B per 16 lanes)
 constexpr int P_LD = C + 4;     // P, T diag(beta) [32][32] bf16, 8-byte reads
 constexpr int G_LD = D + 4;     // Gamma * log2(e) [32][128] fp32
 constexpr int X_LD = D + 8;     // X, Y, Z, Kb [rows][128] bf16, 16-byte reads
@@ -60,8 +60,8 @@ constexpr int A_LD = 16 + 4;    // 16x16 blocks: A10 (bf16), A diagonal (fp32), 
 constexpr int B_QT = 0;
 constexpr int B_KT = B_QT + C * W_LD * 2;
 constexpr int B_KH = B_KT + C * W_LD * 2;
-constexpr int B_VT = B_KH + D * KH_LD * 2;
-constexpr int B_P = B_VT + D * KH_LD * 2;
+constexpr int B_V = B_KH + C * KR_LD * 2;
+constexpr int B_P = B_V + C * KR_LD * 2;
 constexpr int B_T = B_P + C * P_LD * 2;
 constexpr int B_SIZE = B_T + C * P_LD * 2;
 // producer scratch
@@ -89,20 +89,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// The 4x4 transpose of four rows of 4 bf16 (one uint2 each): out[e] holds
-// element e of rows 0..3.
-__device__ __forceinline__ void transpose4x4_bf16(const uint2 *in, uint2 *out)
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4a+b receives
+// 16-bit element b of the 8-byte words addressed by lanes a, a+4, a+8, a+12 of the group.
+__device__ __forceinline__ uint2 lds_tr16(const bf16 *p)
 {
-    // selector 0x05040100 keeps the low 16 bits of (a, b), 0x07060302 the high ones
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const uint32_t a = e ? in[0].y : in[0].x, b = e ? in[1].y : in[1].x;
-        const uint32_t c = e ? in[2].y : in[2].x, d = e ? in[3].y : in[3].x;
-        out[2 * e].x = __builtin_amdgcn_perm(b, a, 0x05040100u);
-        out[2 * e].y = __builtin_amdgcn_perm(d, c, 0x05040100u);
-        out[2 * e + 1].x = __builtin_amdgcn_perm(b, a, 0x07060302u);
-        out[2 * e + 1].y = __builtin_amdgcn_perm(d, c, 0x07060302u);
-    }
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+    return __builtin_bit_cast(uint2, v);
 }
 
 // x += a[lane J of this lane's 16-lane row] * t: one v_fmac with a DPP row broadcast of a.
@@ -266,7 +259,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     auto operands = [&](auto b1_tag, char *PB) {
         constexpr bool B1 = decltype(b1_tag)::value;
         bf16 *pQt = (bf16 *)(PB + B_QT), *pKt = (bf16 *)(PB + B_KT), *pKh = (bf16 *)(PB + B_KH);
-        bf16 *pVT = (bf16 *)(PB + B_VT);
+        bf16 *pV = (bf16 *)(PB + B_V);
         float4 E1 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (B1) E1 = *(const float4 *)(sG + 15 * G_LD + ech);
         const float4 e15 = *(const float4 *)(sSc + 0 * D + ech);
@@ -310,24 +303,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             }
             if (!B1) V4::store(sKb + i * X_LD + ech, V4::pack(Kb));
         }
-        // transposed tiles: channel rows of Kh^T and V^T get this thread's 2 tokens
+        // Kh and V rows, row-major like Qt and Kt (the consumers read them transposed)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bf16x2 kp;
-            kp[0] = (bf16)kh[0][e];
-            kp[1] = (bf16)kh[1][e];
-            *(uint32_t *)(pKh + (ech + e) * KH_LD + 2 * etp) = __builtin_bit_cast(uint32_t, kp);
-        }
-        if (has_v) {
-            // selector 0x05040100 pairs the low bf16 of (rv[0], rv[1]), 0x07060302 the high ones
-            const uint32_t v0 = __builtin_amdgcn_perm(rv[1].x, rv[0].x, 0x05040100u);
-            const uint32_t v1 = __builtin_amdgcn_perm(rv[1].x, rv[0].x, 0x07060302u);
-            const uint32_t v2 = __builtin_amdgcn_perm(rv[1].y, rv[0].y, 0x05040100u);
-            const uint32_t v3 = __builtin_amdgcn_perm(rv[1].y, rv[0].y, 0x07060302u);
-            *(uint32_t *)(pVT + (ech + 0) * KH_LD + 2 * etp) = v0;
-            *(uint32_t *)(pVT + (ech + 1) * KH_LD + 2 * etp) = v1;
-            *(uint32_t *)(pVT + (ech + 2) * KH_LD + 2 * etp) = v2;
-            *(uint32_t *)(pVT + (ech + 3) * KH_LD + 2 * etp) = v3;
+        for (int r = 0; r < 2; ++r) {
+            V4::store(pKh + (2 * etp + r) * KR_LD + ech, V4::pack(kh[r]));
+            if (has_v) V4::store(pV + (2 * etp + r) * KR_LD + ech, rv[r]);
         }
     };
     const int c_last = c_end - 1;
@@ -470,6 +450,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     } else {
         // ============================================ consumer waves
         const int cw = wave;
+        // transposed reads: lane k of each 16-lane group addresses row k/4 and channel
+        // 4*(k%4) of a 16-channel slice; it receives 4 rows of channel (its slice) + (lane%16)
+        const int tr_row = (lane & 15) >> 2, tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         bf16 *ob = has_out ? (bf16 *)p.o + bsel * p.o_sb + h * p.o_sh + t0 * p.o_st : nullptr;
         f32x16 S[4];
         const int vcol = 32 * cw + l32;
@@ -506,7 +489,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const bool cact = t >= 1;                       // runs chunk c_begin + t - 1 from buffer (t-1) % 2
             char *CB = smem + ((t + 1) & 1) * B_SIZE;
             const bf16 *cQt = (const bf16 *)(CB + B_QT), *cKt = (const bf16 *)(CB + B_KT);
-            const bf16 *cKh = (const bf16 *)(CB + B_KH), *cVT = (const bf16 *)(CB + B_VT);
+            const bf16 *cKh = (const bf16 *)(CB + B_KH), *cV = (const bf16 *)(CB + B_V);
             const bf16 *cP = (const bf16 *)(CB + B_P), *cT = (const bf16 *)(CB + B_T);
             const float *cDec = sDec + ((t + 2) % 3) * D;   // ring slot (t - 1) % 3
             const int cc = c_begin + t - 1, ctok0 = cc * C, cL = min(C, len - ctok0);
@@ -522,7 +505,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float v4[4];
-                        V4::unpack(*(const uint2 *)(cVT + (32 * cw + l32) * KH_LD + 8 * q + 4 * g2), v4);
+                        V4::unpack(lds_tr16(cV + (8 * q + 4 * g2 + tr_row) * KR_LD + 32 * cw + tr_col), v4);
                         R[4 * q] = v4[0]; R[4 * q + 1] = v4[1]; R[4 * q + 2] = v4[2]; R[4 * q + 3] = v4[3];
                     }
                 }
@@ -609,8 +592,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         Frag8<bf16> fa;
-                        const bf16 *row = cKh + (32 * m + l32) * KH_LD + 16 * s + 4 * g2;
-                        fa.load44(row, row + 8);
+                        const bf16 *p0 = cKh + (16 * s + 4 * g2 + tr_row) * KR_LD + 32 * m + tr_col;
+                        fa.load44_tr(p0, p0 + 8 * KR_LD);
                         mma32(S[m], fa, UB[s]);
                     }
                 }

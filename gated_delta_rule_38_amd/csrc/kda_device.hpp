@@ -92,6 +92,15 @@ template <> struct Frag8<bf16> {
         uint4 u = make_uint4(a.x, a.y, b.x, b.y);
         v = __builtin_bit_cast(bf16x8, u);
     }
+    // two transposing LDS reads (ds_read_b64_tr_b16): 4 rows of one column each
+    __device__ __forceinline__ void load44_tr(const bf16 *p, const bf16 *p2) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p2);
+        const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+        v = __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
+    }
 };
 template <> struct Frag8<float> {
     float v[8];
