@@ -73,15 +73,14 @@ constexpr int S_Z = S_Y + C * X_LD * 2;
 constexpr int S_KB = S_Z + C * X_LD * 2;
 constexpr int S_A10 = S_KB + 16 * X_LD * 2;
 constexpr int S_AD = S_A10 + 16 * A_LD * 2;
-constexpr int S_TD = S_AD + 2 * 16 * A_LD * 4;
-constexpr int S_T11 = S_TD + 16 * A_LD * 4;
-constexpr int S_SC = S_T11 + 16 * A_LD * 2;
+constexpr int S_TB = S_AD + 2 * 16 * A_LD * 4;   // T_00, T_11 (bf16) for the off-diagonal product
+constexpr int S_SC = S_TB + 2 * 16 * A_LD * 2;
 constexpr int S_DEC = S_SC + 2 * D * 4;       // chunk decays e^{G_L}: a ring of 3 chunks
 constexpr int S_BETA = S_DEC + 3 * D * 4;     // beta: a ring of 3 chunks
 constexpr int SMEM = S_BETA + 3 * C * 4;
 static_assert(SMEM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TD % 16 == 0 &&
-              S_T11 % 16 == 0 && S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
+static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TB % 16 == 0 &&
+              S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
 
 typedef Vec4<bf16> V4;
 typedef Vec4<float> V4f;
@@ -127,8 +126,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     float *sG = (float *)(smem + S_G), *sGraw = (float *)(smem + S_GRAW);
     bf16 *sX = (bf16 *)(smem + S_X), *sY = (bf16 *)(smem + S_Y), *sZ = (bf16 *)(smem + S_Z);
     bf16 *sKb = (bf16 *)(smem + S_KB), *sA10 = (bf16 *)(smem + S_A10);
-    float *sAd = (float *)(smem + S_AD), *sTd = (float *)(smem + S_TD);
-    bf16 *sT11 = (bf16 *)(smem + S_T11);
+    float *sAd = (float *)(smem + S_AD);
+    bf16 *sTb = (bf16 *)(smem + S_TB);
     float *sSc = (float *)(smem + S_SC), *sDec = (float *)(smem + S_DEC);
     float *sBeta = (float *)(smem + S_BETA);
 
@@ -146,8 +145,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     };
 
     // T diag(beta) of one chunk from its A and beta, into pT, in two parts, each run by one
-    // wave: the diagonal 16x16 blocks (from sAd; also leaves T_00 in sTd and T_11 in sT11)
-    // and, a step later, the off-diagonal block (from sA10, sTd, sT11).
+    // wave: the diagonal 16x16 blocks (from sAd; also leaves T_00 and T_11 in sTb) and, a
+    // step later, the off-diagonal block (from sA10 and sTb).
     auto build_T_diag = [&](const float *betac, bf16 *pT) {
         // Diagonal 16x16 blocks of T = (I + A)^-1, one row per lane: lanes 0-15 block 0,
         // lanes 16-31 block 1, lanes 32-63 repeat them.  T = I - T A gives, for row i,
@@ -168,24 +167,19 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
         for (int c = 0; c < 16; ++c) x[c] = (c == i) ? 1.f : 0.f;
         tsweep<15>(x, a);
-        if (lane < 32) {
-            bf16 *trow = pT + (16 * b + i) * P_LD + 16 * b;
+        // One branch-free store sequence: lanes 0-31 write row 16b+i of T diag(beta) (its
+        // diagonal block, and zeros over the other 16 columns -- block (0,1) is zero, block
+        // (1,0) is written a step later); lanes 32-63 write the unscaled row to sTb.
+        const bool hi = lane >= 32;
+        bf16 *dst0 = hi ? sTb + (16 * b + i) * A_LD : pT + (16 * b + i) * P_LD + 16 * b;
+        bf16 *dst1 = pT + (16 * b + i) * P_LD + 16 * (1 - b);
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const float tb[4] = {x[4 * c4] * bt[4 * c4], x[4 * c4 + 1] * bt[4 * c4 + 1],
-                                     x[4 * c4 + 2] * bt[4 * c4 + 2], x[4 * c4 + 3] * bt[4 * c4 + 3]};
-                V4::store(trow + 4 * c4, V4::pack(tb));
-            }
-            if (b == 0) {        // T_00 rows, fp32, for the off-diagonal product
+        for (int c4 = 0; c4 < 4; ++c4) {
+            float tb[4];
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) *(float4 *)(sTd + i * A_LD + 4 * c4) = V4f::pack(x + 4 * c4);
-            } else {             // T_11 rows, bf16
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) V4::store(sT11 + i * A_LD + 4 * c4, V4::pack(x + 4 * c4));
-            }
-        } else if (b == 0) {     // block (0,1) of T is zero
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) V4::store(pT + i * P_LD + 16 + 4 * c4, V4::zero());
+            for (int e = 0; e < 4; ++e) tb[e] = hi ? x[4 * c4 + e] : x[4 * c4 + e] * bt[4 * c4 + e];
+            V4::store(dst0 + 4 * c4, V4::pack(tb));
+            V4::store(dst1 + 4 * c4, V4::zero());
         }
     };
     auto build_T_off = [&](const float *betac, bf16 *pT) {
@@ -196,9 +190,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         Frag4<bf16> fa, fb;
         fa.load4(sA10 + l16 * A_LD + 4 * g4);
         {
-            const float tv[4] = {sTd[(4 * g4) * A_LD + l16], sTd[(4 * g4 + 1) * A_LD + l16],
-                                 sTd[(4 * g4 + 2) * A_LD + l16], sTd[(4 * g4 + 3) * A_LD + l16]};
-            fb.set(tv);
+            const bf16x4 tv = {sTb[(4 * g4) * A_LD + l16], sTb[(4 * g4 + 1) * A_LD + l16],
+                               sTb[(4 * g4 + 2) * A_LD + l16], sTb[(4 * g4 + 3) * A_LD + l16]};
+            fb.v = __builtin_bit_cast(s16x4, tv);
         }
         mma16k16(Y, fa, fb);
         Frag4<bf16> fy, ft;
@@ -206,7 +200,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const float y4[4] = {Y[0], Y[1], Y[2], Y[3]};
             fy.set(y4);
         }
-        ft.load4(sT11 + l16 * A_LD + 4 * g4);
+        ft.load4(sTb + (16 + l16) * A_LD + 4 * g4);
         f32x4 Z = {0.f, 0.f, 0.f, 0.f};
         mma16k16(Z, fy, ft);
         const float4 b4 = *(const float4 *)(betac + 4 * g4);
