@@ -189,11 +189,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         f32x4 Y = {0.f, 0.f, 0.f, 0.f};
         Frag4<bf16> fa, fb;
         fa.load4(sA10 + l16 * A_LD + 4 * g4);
-        {
-            const bf16x4 tv = {sTb[(4 * g4) * A_LD + l16], sTb[(4 * g4 + 1) * A_LD + l16],
-                               sTb[(4 * g4 + 2) * A_LD + l16], sTb[(4 * g4 + 3) * A_LD + l16]};
-            fb.v = __builtin_bit_cast(s16x4, tv);
-        }
+        // T_00 columns: rows 4*g4..4*g4+3 of column l16, by one transposing read
+        fb.v = __builtin_bit_cast(s16x4, lds_tr16(sTb + (4 * g4 + (l16 >> 2)) * A_LD + 4 * (l16 & 3)));
         mma16k16(Y, fa, fb);
         Frag4<bf16> fy, ft;
         {
