@@ -285,9 +285,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     Kt[e] = -(X[e] * e15v[e]);
                 }
             }
-            V4::store(sX + i * X_LD + ech, V4::pack(X));
+            const uint2 Xp = V4::pack(X);
+            V4::store(sX + i * X_LD + ech, Xp);
             V4::store(sZ + i * X_LD + ech, V4::pack(Z));
-            V4::store(pKt + i * W_LD + ech, V4::pack(Kt));
+            // sub-block 0: -Kt is X, negated exactly by flipping the bf16 sign bits
+            V4::store(pKt + i * W_LD + ech, B1 ? V4::pack(Kt) : make_uint2(Xp.x ^ 0x80008000u, Xp.y ^ 0x80008000u));
             if (has_out) {
                 V4::store(sY + i * X_LD + ech, V4::pack(Y));
                 V4::store(pQt + i * W_LD + ech, V4::pack(Qt));
