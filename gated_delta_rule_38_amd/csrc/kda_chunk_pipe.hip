@@ -19,7 +19,7 @@
 //     consumer wave 0: the consumers' own share of interval 1 is short.
 // The roles meet in a double buffer in LDS.  Step t: the producers build chunk
 // t into buffer t%2 while the consumers run chunk t-1 from buffer (t-1)%2.
-// Every wave executes the same three workgroup barriers per step; no buffer is
+// Every wave executes the same two workgroup barriers per step; no buffer is
 // written before the barrier that ends the last read of its previous contents
 // (the reader/writer ordering TensorRT-LLM PR #19826 had to add to its fused
 // prefill between a chunk's readers and the next chunk's writers).  A VALU-heavy
@@ -29,11 +29,10 @@
 //               producers -- raw g of t+1 staged, g of t+2 requested
 //               consumers -- R of chunk t-1; wave 0 also the off-diagonal block of
 //               T diag(beta) of chunk t-1
-//   interval 2: producers -- A, P of chunk t
-//               consumers -- U and O of chunk t-1 (O stored)
-//   interval 3: producer wave 0 -- diagonal blocks of T diag(beta) of chunk t
-//               producer waves 2, 3 -- gate scan of chunk t+1
-//               consumers -- state update of chunk t-1
+//   interval 2: producer waves 0, 2 -- A (0,0), A (1,1) and the diagonal blocks of
+//               T diag(beta) of chunk t; waves 1, 3 -- the other A and P tiles, then
+//               the gate scan of chunk t+1
+//               consumers -- U and O of chunk t-1 (O stored), then the state update
 //
 // 32-token chunks hold two 16-token gate sub-blocks: diagonal sub-blocks factor
 // the decay through the block start (factors within [e^-80, e^80] for g >= -5),
@@ -147,15 +146,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     // T diag(beta) of one chunk from its A and beta, into pT, in two parts, each run by one
     // wave: the diagonal 16x16 blocks (from sAd; also leaves T_00 and T_11 in sTb) and, a
     // step later, the off-diagonal block (from sA10 and sTb).
-    auto build_T_diag = [&](const float *betac, bf16 *pT) {
-        // Diagonal 16x16 blocks of T = (I + A)^-1, one row per lane: lanes 0-15 block 0,
-        // lanes 16-31 block 1, lanes 32-63 repeat them.  T = I - T A gives, for row i,
-        // T_ic = [i == c] - sum_{j > c} T_ij A_jc, so column j of the row is final once
-        // the columns after it are folded in: sweeping j downwards, each final T_ij is
-        // folded into the remaining columns with row j of A.  Each lane keeps its own row
-        // of A in registers; row j reaches the other lanes of its block by a DPP
-        // broadcast from lane j of the 16-lane row, so the sweep makes no LDS access.
-        const int b = (lane >> 4) & 1, i = l16;
+    auto build_T_diag = [&](const int b, const float *betac, bf16 *pT) {
+        // Diagonal 16x16 block b of T = (I + A)^-1, one row per lane (each 16-lane group
+        // holds the whole block).  T = I - T A gives, for row i, T_ic = [i == c] -
+        // sum_{j > c} T_ij A_jc, so column j of the row is final once the columns after it
+        // are folded in: sweeping j downwards, each final T_ij is folded into the remaining
+        // columns with row j of A.  Each lane keeps its own row of A in registers; row j
+        // reaches the other lanes of the group by a DPP broadcast from lane j of the 16-lane
+        // row, so the sweep makes no LDS access.
+        const int i = l16;
         float a[16], bt[16], x[16];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
@@ -169,7 +168,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         tsweep<15>(x, a);
         // One branch-free store sequence: lanes 0-31 write row 16b+i of T diag(beta) (its
         // diagonal block, and zeros over the other 16 columns -- block (0,1) is zero, block
-        // (1,0) is written a step later); lanes 32-63 write the unscaled row to sTb.
+        // (1,0) is written a step later); lanes 32-63 write the unscaled row to sTb.  Lanes
+        // 16-31 and 48-63 repeat the stores of lanes 0-15 and 32-47.
         const bool hi = lane >= 32;
         bf16 *dst0 = hi ? sTb + (16 * b + i) * A_LD : pT + (16 * b + i) * P_LD + 16 * b;
         bf16 *dst1 = pT + (16 * b + i) * P_LD + 16 * (1 - b);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     if (producer) {
         // ============================================ producer waves
         const int pt = tid - 256, pw = wave - 4;
-        const int sc = pt - 128;                                   // scan threads (waves 6, 7): one key channel each
+        const int sc = (pw == 1) ? lane : (pw == 3) ? 64 + lane : -1;   // scan threads (waves 5, 7): one key channel each
         const float *gb = p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st;
         const float *bb = p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st;
 
@@ -396,15 +396,19 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             if (pact) operands(std::true_type{}, PB);
             prefetch_qkv(min(pc + 1, c_last));
             sync();
-            // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128)
+            // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128), diagonal T blocks
+            //                  of chunk t; gate scan of chunk t+1
             if (pact) {
-                // wave 0 -> (0,0) A and P, wave 1 -> (1,0) A and P, wave 2 -> A (1,1), wave 3 -> P (1,1)
-                const int ib = (pw == 0) ? 0 : 1, jb = (pw == 1) ? 0 : ib;
-                const int nitem = (pw <= 1) ? 2 : 1;
+                // wave 0 -> A (0,0) then T_00, wave 2 -> A (1,1) then T_11,
+                // wave 1 -> A and P (1,0), wave 3 -> P (0,0) and P (1,1)
+                const bool diag = (pw & 1) == 0;
+                const int nitem = diag ? 1 : 2;
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
                     if (it >= nitem) break;
-                    const int mat = (pw <= 1) ? it : (pw - 2);   // 0: A, 1: P
+                    const int mat = diag ? 0 : ((pw == 1) ? it : 1);       // 0: A, 1: P
+                    const int ib = diag ? (pw >> 1) : ((pw == 1) ? 1 : it);
+                    const int jb = (pw == 1) ? 0 : ib;
                     if (mat == 1 && !has_out) continue;
                     const bf16 *arow = ((ib == jb) ? sZ : sKb) + (16 * jb + l16) * X_LD;
                     const bf16 *brow = (mat ? sY : sX) + (16 * ib + l16) * X_LD;
@@ -433,10 +437,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     }
                 }
                 if (pw == 3 && has_out) V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
+                if (diag) {
+                    lds_fence();          // this wave's A rows, written above by other lanes
+                    build_T_diag(pw >> 1, betac, pT);
+                }
             }
-            sync();
-            // ---------------- interval 3: diagonal blocks of T diag(beta) of chunk t; gate scan of chunk t+1
-            if (pact && pw == 0) build_T_diag(betac, pT);
             if (more) scan(pc + 1, t + 1);
             sync();
         }
@@ -569,8 +574,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     }
                 }
             }
-            sync();
-            // ---------------- interval 3: S <- Diag(e^{G_L}) S + Kh^T U
+            // ---------------- state update (same interval): S <- Diag(e^{G_L}) S + Kh^T U
             if (cact) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
