@@ -65,8 +65,9 @@ constexpr int B_T = B_P + C * P_LD * 2;
 constexpr int B_SIZE = B_T + C * P_LD * 2;
 // producer scratch
 constexpr int S_G = 2 * B_SIZE;
+constexpr int GT_LD = C + 4;    // raw g staged transposed [128 channels][32 tokens] fp32
 constexpr int S_GRAW = S_G + C * G_LD * 4;   // raw g of the next chunk, staged for the scan
-constexpr int S_X = S_GRAW + C * G_LD * 4;
+constexpr int S_X = S_GRAW + D * GT_LD * 4;
 constexpr int S_Y = S_X + C * X_LD * 2;
 constexpr int S_Z = S_Y + C * X_LD * 2;
 constexpr int S_KB = S_Z + C * X_LD * 2;
@@ -290,17 +291,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             V4::store(sZ + i * X_LD + ech, V4::pack(Z));
             // sub-block 0: -Kt is X, negated exactly by flipping the bf16 sign bits
             V4::store(pKt + i * W_LD + ech, B1 ? V4::pack(Kt) : make_uint2(Xp.x ^ 0x80008000u, Xp.y ^ 0x80008000u));
-            if (has_out) {
-                V4::store(sY + i * X_LD + ech, V4::pack(Y));
-                V4::store(pQt + i * W_LD + ech, V4::pack(Qt));
-            }
+            V4::store(sY + i * X_LD + ech, V4::pack(Y));      // (unused without outputs)
+            V4::store(pQt + i * W_LD + ech, V4::pack(Qt));
             if (!B1) V4::store(sKb + i * X_LD + ech, V4::pack(Kb));
         }
         // Kh and V rows, row-major like Qt and Kt (the consumers read them transposed)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             V4::store(pKh + (2 * etp + r) * KR_LD + ech, V4::pack(kh[r]));
-            if (has_v) V4::store(pV + (2 * etp + r) * KR_LD + ech, rv[r]);
+            V4::store(pV + (2 * etp + r) * KR_LD + ech, rv[r]);
         }
     };
     const int c_last = c_end - 1;
@@ -312,9 +311,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         const float *gb = p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st;
         const float *bb = p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st;
 
-        float rgv[16];                  // g of 4 tokens x 4 channels (rows gr, gr+8, gr+16, gr+24)
+        float rgv[16];                  // g of tokens 4*gq..4*gq+3 x channels 4*gc..4*gc+3
         float rbeta;                    // beta of token gc
-        const int gr = pt >> 5, gc = pt & 31;
+        const int gq = pt >> 5, gc = pt & 31;
         // Every thread of a role issues the same loads, from always in-bounds addresses (the
         // rows of a short last chunk re-read its last token; chunks past the segment's end
         // re-read its last chunk), all in interval 1, and consumes them at the start of the
@@ -326,16 +325,23 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float4 v = *(const float4 *)(gb + (int64_t)(tok0 + min(gr + 8 * k, Lm1)) * p.g_st + 4 * gc);
+                const float4 v = *(const float4 *)(gb + (int64_t)(tok0 + min(4 * gq + k, Lm1)) * p.g_st + 4 * gc);
                 rgv[4 * k] = v.x; rgv[4 * k + 1] = v.y; rgv[4 * k + 2] = v.z; rgv[4 * k + 3] = v.w;
             }
             rbeta = bb[(int64_t)(tok0 + min(gc, Lm1)) * p.b_st];
         };
-        // raw g of chunk c (the t-th of this segment) into the staging buffer, beta into ring slot t % 3
+        // Raw g of chunk c (the t-th of this segment) into the staging buffer, transposed: channel
+        // row ch holds its 32 tokens as 8 groups of 4, group k at slot k ^ ((ch >> 4) & 7), which
+        // keeps both these 16-byte stores and the scan's 16-byte row reads free of bank conflicts.
+        // Beta goes into ring slot t % 3.
         auto stage_g = [&](int c, int t) {
             const int L = min(C, len - c * C);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) *(float4 *)(sGraw + (gr + 8 * k) * G_LD + 4 * gc) = V4f::pack(rgv + 4 * k);
+            for (int e = 0; e < 4; ++e) {
+                const int ch = 4 * gc + e;
+                *(float4 *)(sGraw + ch * GT_LD + 4 * (gq ^ ((ch >> 4) & 7))) =
+                    make_float4(rgv[e], rgv[4 + e], rgv[8 + e], rgv[12 + e]);
+            }
             if (pt < C) sBeta[(t % 3) * C + pt] = (pt < L) ? rbeta : 0.f;
         };
         // gate scan of the staged chunk c (the t-th of this segment) into Gamma * log2(e),
@@ -345,7 +351,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             if (sc >= 0) {
                 float rg[C];
 #pragma unroll
-                for (int i = 0; i < C; ++i) rg[i] = sGraw[i * G_LD + sc];
+                for (int k = 0; k < C / 4; ++k) {
+                    const float4 v = *(const float4 *)(sGraw + sc * GT_LD + 4 * (k ^ ((sc >> 4) & 7)));
+                    rg[4 * k] = v.x; rg[4 * k + 1] = v.y; rg[4 * k + 2] = v.z; rg[4 * k + 3] = v.w;
+                }
                 // tail rows re-read token L-1 (clamped loads), so a precomputed Gamma needs
                 // no select there; the cumsum skips them so they hold Gamma_{L-1}
                 if (p.g_is_gamma) {
@@ -448,6 +457,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     } else {
         // ============================================ consumer waves
         const int cw = wave;
+        const float vscale = has_v ? 1.f : 0.f;     // the transition-map role runs with V = 0
         // transposed reads: lane k of each 16-lane group addresses row k/4 and channel
         // 4*(k%4) of a 16-channel slice; it receives 4 rows of channel (its slice) + (lane%16)
         const int tr_row = (lane & 15) >> 2, tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -494,18 +504,20 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             Frag8<bf16> SB[8], UB[2];
             // ---------------- interval 1: sub-block 0 operands of chunk t into buffer t % 2;
             //                  R = V - Kt S; wave 0 also finishes T diag(beta) of the chunk
-            if (t < nck) operands(std::false_type{}, smem + (t & 1) * B_SIZE);
+            // One straight-line block, so that the R products can overlap the operand arithmetic:
+            // the operands of the step past the last chunk, and R before the first one, are
+            // computed on stale data and never read.
+            operands(std::false_type{}, smem + (t & 1) * B_SIZE);
             prefetch_qkv(min(c_begin + t + 1, c_last));
             Frag8<bf16> RB[2];
-            if (cact) {
-                f32x16 R = {};
-                if (has_v) {
+            {
+                f32x16 R;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v4[4];
-                        V4::unpack(lds_tr16(cV + (8 * q + 4 * g2 + tr_row) * KR_LD + 32 * cw + tr_col), v4);
-                        R[4 * q] = v4[0]; R[4 * q + 1] = v4[1]; R[4 * q + 2] = v4[2]; R[4 * q + 3] = v4[3];
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    float v4[4];
+                    V4::unpack(lds_tr16(cV + (8 * q + 4 * g2 + tr_row) * KR_LD + 32 * cw + tr_col), v4);
+                    R[4 * q] = v4[0] * vscale; R[4 * q + 1] = v4[1] * vscale;
+                    R[4 * q + 2] = v4[2] * vscale; R[4 * q + 3] = v4[3] * vscale;
                 }
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
@@ -528,11 +540,22 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     for (int e = 0; e < 8; ++e) t8[e] = R[8 * s + e];
                     RB[s].set(t8);
                 }
-                if (cw == 0) build_T_off(sBeta + ((t + 2) % 3) * C, (bf16 *)(CB + B_T));
             }
+            if (cact && cw == 0) build_T_off(sBeta + ((t + 2) % 3) * C, (bf16 *)(CB + B_T));
             sync();
             // ---------------- interval 2: U = (T diag(beta)) R; O = Qt S + P U, stored
             if (cact) {
+                // the decay of the state update first: S is not read again before it (O uses SB)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 d = *(const float4 *)(cDec + 32 * m + 8 * q + 4 * g2);
+                        S[m][4 * q + 0] *= d.x;
+                        S[m][4 * q + 1] *= d.y;
+                        S[m][4 * q + 2] *= d.z;
+                        S[m][4 * q + 3] *= d.w;
+                    }
                 f32x16 U = {};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -578,14 +601,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             if (cact) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 d = *(const float4 *)(cDec + 32 * m + 8 * q + 4 * g2);
-                        S[m][4 * q + 0] *= d.x;
-                        S[m][4 * q + 1] *= d.y;
-                        S[m][4 * q + 2] *= d.z;
-                        S[m][4 * q + 3] *= d.w;
-                    }
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         Frag8<bf16> fa;
