@@ -571,8 +571,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     for (int e = 0; e < 8; ++e) t8[e] = U[8 * s + e];
                     UB[s].set(t8);
                 }
-            }
-            if (cact && has_out) {
+                // O = Qt S + P U (always formed: without outputs it is discarded), then the
+                // state update, in one block so the three MFMA chains and the conversions can
+                // interleave; the stores come last
                 f32x16 O = {};
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
@@ -588,17 +589,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     fb.load44(row, row + 8);
                     mma32(O, UB[s], fb);
                 }
-                if (l32 < cL) {
-                    bf16 *dst = ob + (int64_t)(ctok0 + l32) * p.o_st + 32 * cw + 4 * g2;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float o4[4] = {O[4 * q], O[4 * q + 1], O[4 * q + 2], O[4 * q + 3]};
-                        V4::store(dst + 8 * q, V4::pack(o4));
-                    }
-                }
-            }
-            // ---------------- state update (same interval): S <- Diag(e^{G_L}) S + Kh^T U
-            if (cact) {
+                // ---------------- state update: S <- Diag(e^{G_L}) S + Kh^T U
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -607,6 +598,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                         const bf16 *p0 = cKh + (16 * s + 4 * g2 + tr_row) * KR_LD + 32 * m + tr_col;
                         fa.load44_tr(p0, p0 + 8 * KR_LD);
                         mma32(S[m], fa, UB[s]);
+                    }
+                }
+                if (has_out && l32 < cL) {
+                    bf16 *dst = ob + (int64_t)(ctok0 + l32) * p.o_st + 32 * cw + 4 * g2;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float o4[4] = {O[4 * q], O[4 * q + 1], O[4 * q + 2], O[4 * q + 3]};
+                        V4::store(dst + 8 * q, V4::pack(o4));
                     }
                 }
             }
