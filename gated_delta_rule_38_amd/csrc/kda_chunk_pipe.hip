@@ -407,51 +407,51 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             sync();
             // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128), diagonal T blocks
             //                  of chunk t; gate scan of chunk t+1
-            if (pact) {
-                // wave 0 -> A (0,0) then T_00, wave 2 -> A (1,1) then T_11,
-                // wave 1 -> A and P (1,0), wave 3 -> P (0,0) and P (1,1)
-                const bool diag = (pw & 1) == 0;
-                const int nitem = diag ? 1 : 2;
+            // 16x16 tile of A^T (mat 0: rows i scaled by beta_i, strictly lower) or P^T (mat 1:
+            // lower including the diagonal) for row block ib, column block jb
+            auto tile = [&](int mat, int ib, int jb, float (&vals)[4]) {
+                const bf16 *arow = ((ib == jb) ? sZ : sKb) + (16 * jb + l16) * X_LD;
+                const bf16 *brow = (mat ? sY : sX) + (16 * ib + l16) * X_LD;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) {
+                    Frag8<bf16> fa, fb;
+                    fa.load8(arow + 32 * s + 8 * g4);
+                    fb.load8(brow + 32 * s + 8 * g4);
+                    mma16(acc, fa, fb);
+                }
+                const int i = 16 * ib + l16, j0 = 16 * jb + 4 * g4;
+                const float sc_i = mat ? 1.f : betac[i];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vals[r] = (j0 + r < i + mat) ? acc[r] * sc_i : 0.f;
+            };
+            if (pw == 0 || pw == 2) {
+                // wave 0 -> A (0,0) then T_00, wave 2 -> A (1,1) then T_11
+                if (pact) {
+                    const int b = pw >> 1;
+                    float vals[4];
+                    tile(0, b, b, vals);
+                    *(float4 *)(sAd + (b * 16 + l16) * A_LD + 4 * g4) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                    lds_fence();          // this wave's A rows, written above by other lanes
+                    build_T_diag(b, betac, pT);
+                }
+            } else {
+                // wave 1 -> A (1,0) and P (1,0), wave 3 -> P (0,0) and P (1,1); both write the zero
+                // P block (0,1); then the gate scan of chunk t+1.  One straight-line block (past the
+                // last chunk its results are never read), so the scan can overlap the MFMAs.
+                const bool w1 = pw == 1;
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
-                    if (it >= nitem) break;
-                    const int mat = diag ? 0 : ((pw == 1) ? it : 1);       // 0: A, 1: P
-                    const int ib = diag ? (pw >> 1) : ((pw == 1) ? 1 : it);
-                    const int jb = (pw == 1) ? 0 : ib;
-                    if (mat == 1 && !has_out) continue;
-                    const bf16 *arow = ((ib == jb) ? sZ : sKb) + (16 * jb + l16) * X_LD;
-                    const bf16 *brow = (mat ? sY : sX) + (16 * ib + l16) * X_LD;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < D / 32; ++s) {
-                        Frag8<bf16> fa, fb;
-                        fa.load8(arow + 32 * s + 8 * g4);
-                        fb.load8(brow + 32 * s + 8 * g4);
-                        mma16(acc, fa, fb);
-                    }
-                    const int i = 16 * ib + l16, j0 = 16 * jb + 4 * g4;
+                    const int mat = w1 ? it : 1;
+                    const int ib = w1 ? 1 : it, jb = w1 ? 0 : it;
                     float vals[4];
-                    if (mat == 0) {
-                        const float bi = betac[i];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) vals[r] = (j0 + r < i) ? acc[r] * bi : 0.f;
-                        if (ib == jb)
-                            *(float4 *)(sAd + (ib * 16 + l16) * A_LD + 4 * g4) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-                        else
-                            V4::store(sA10 + l16 * A_LD + 4 * g4, V4::pack(vals));
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) vals[r] = (j0 + r <= i) ? acc[r] : 0.f;
-                        V4::store(pP + i * P_LD + j0, V4::pack(vals));
-                    }
+                    tile(mat, ib, jb, vals);
+                    bf16 *dst = (mat == 0) ? sA10 + l16 * A_LD + 4 * g4 : pP + (16 * ib + l16) * P_LD + 16 * jb + 4 * g4;
+                    V4::store(dst, V4::pack(vals));
                 }
-                if (pw == 3 && has_out) V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
-                if (diag) {
-                    lds_fence();          // this wave's A rows, written above by other lanes
-                    build_T_diag(pw >> 1, betac, pT);
-                }
+                V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
+                scan(pc + 1, t + 1);
             }
-            if (more) scan(pc + 1, t + 1);
             sync();
         }
     } else {
