@@ -256,8 +256,13 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     const int64_t chains = P.N * P.H;
     const int variant = o ? o->variant : 0;
     if (variant < 0 || variant > 2) return fail(KDA_ERR_UNSUPPORTED, "kernel variant %d", variant);
-    const bool pipe_ok = P.D == 128 && !P.fp32;
-    if (variant == 2 && !pipe_ok) return fail(KDA_ERR_UNSUPPORTED, "the pipelined kernel needs head size 128 and bf16");
+    // the pipelined kernel addresses a 32-token chunk of every token-major tensor with 32-bit
+    // byte offsets from the chunk's first row
+    auto rows32 = [](const Tok &t, int64_t es) { return 32 * t.st * es + 1024 <= (int64_t)INT32_MAX; };
+    const bool pipe_ok = P.D == 128 && !P.fp32 && rows32(P.q, 2) && rows32(P.k, 2) && rows32(P.v, 2) &&
+                         rows32(P.out, 2) && rows32(P.g, 4) && rows32(P.beta, 4);
+    if (variant == 2 && !pipe_ok)
+        return fail(KDA_ERR_UNSUPPORTED, "the pipelined kernel needs head size 128, bf16 and token strides below 2^31 / 32 bytes");
     pl.pipe = pipe_ok && variant != 1;
     pl.chunk = pl.pipe ? 32 : 64;
     const int64_t max_chunks = P.dense ? (P.T + pl.chunk - 1) / pl.chunk : (P.Ttot + pl.chunk - 1) / pl.chunk;

@@ -231,18 +231,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     // Thread tid handles tokens 2*(tid>>5) and 2*(tid>>5)+1, channels 4*(tid&31)..+3 of a
     // chunk: the consumer waves gate sub-block 0, the producer waves sub-block 1.
     const int etp = tid >> 5, ech = 4 * (tid & 31);
-    const bf16 *qb = (const bf16 *)p.q + bsel * p.q_sb + h * p.q_sh + t0 * p.q_st;
-    const bf16 *kb = (const bf16 *)p.k + bsel * p.k_sb + h * p.k_sh + t0 * p.k_st;
-    const bf16 *vb = (const bf16 *)p.v + bsel * p.v_sb + h * p.v_sh + t0 * p.v_st;
+    const char *qb = (const char *)p.q + 2 * (bsel * p.q_sb + h * p.q_sh + t0 * p.q_st);
+    const char *kb = (const char *)p.k + 2 * (bsel * p.k_sb + h * p.k_sh + t0 * p.k_st);
+    const char *vb = (const char *)p.v + 2 * (bsel * p.v_sb + h * p.v_sh + t0 * p.v_st);
+    // Each load addresses a uniform chunk base plus a 32-bit per-lane byte offset (the host
+    // keeps a chunk's rows within 2^31 bytes).  Rows past a short chunk's end re-read its last
+    // row: with non-negative strides, min(row, L-1) * stride = min(row * stride, (L-1) * stride).
+    const uint32_t qst = 2 * (uint32_t)p.q_st, kst = 2 * (uint32_t)p.k_st, vst = 2 * (uint32_t)p.v_st;
+    const uint32_t qro = 2 * etp * qst + 2 * ech, kro = 2 * etp * kst + 2 * ech, vro = 2 * etp * vst + 2 * ech;
     uint2 rq[2], rk[2], rv[2];          // 2 tokens x 4 channels of q, k, v (bf16)
     auto prefetch_qkv = [&](int c) {
         const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
+        const char *qc = qb + (int64_t)tok0 * qst, *kc = kb + (int64_t)tok0 * kst, *vc = vb + (int64_t)tok0 * vst;
+        const uint32_t ql = Lm1 * qst + 2 * ech, kl = Lm1 * kst + 2 * ech, vl = Lm1 * vst + 2 * ech;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const int64_t row = tok0 + min(2 * etp + r, Lm1);
-            rq[r] = *(const uint2 *)(qb + row * p.q_st + ech);
-            rk[r] = *(const uint2 *)(kb + row * p.k_st + ech);
-            rv[r] = *(const uint2 *)(vb + row * p.v_st + ech);
+            rq[r] = *(const uint2 *)(qc + min(qro + r * qst, ql));
+            rk[r] = *(const uint2 *)(kc + min(kro + r * kst, kl));
+            rv[r] = *(const uint2 *)(vc + min(vro + r * vst, vl));
         }
     };
     // B1: sub-block 1.  Rows past a short chunk's end hold finite copies of token L-1: with
@@ -308,12 +314,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         // ============================================ producer waves
         const int pt = tid - 256, pw = wave - 4;
         const int sc = (pw == 1) ? lane : (pw == 3) ? 64 + lane : -1;   // scan threads (waves 5, 7): one key channel each
-        const float *gb = p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st;
-        const float *bb = p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st;
+        const char *gb = (const char *)(p.g + bsel * p.g_sb + h * p.g_sh + t0 * p.g_st);
+        const char *bb = (const char *)(p.beta + bsel * p.b_sb + h * p.b_sh + t0 * p.b_st);
 
         float rgv[16];                  // g of tokens 4*gq..4*gq+3 x channels 4*gc..4*gc+3
         float rbeta;                    // beta of token gc
         const int gq = pt >> 5, gc = pt & 31;
+        const uint32_t gst = 4 * (uint32_t)p.g_st, bst = 4 * (uint32_t)p.b_st;
+        const uint32_t gro = 4 * gq * gst + 16 * gc, bro = gc * bst;
         // Every thread of a role issues the same loads, from always in-bounds addresses (the
         // rows of a short last chunk re-read its last token; chunks past the segment's end
         // re-read its last chunk), all in interval 1, and consumes them at the start of the
@@ -323,12 +331,14 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         // loads would expose their full memory latency.
         auto prefetch_g = [&](int c) {
             const int tok0 = c * C, Lm1 = min(C, len - tok0) - 1;
+            const char *gcb = gb + (int64_t)tok0 * gst, *bcb = bb + (int64_t)tok0 * bst;
+            const uint32_t gl = Lm1 * gst + 16 * gc;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float4 v = *(const float4 *)(gb + (int64_t)(tok0 + min(4 * gq + k, Lm1)) * p.g_st + 4 * gc);
+                const float4 v = *(const float4 *)(gcb + min(gro + k * gst, gl));
                 rgv[4 * k] = v.x; rgv[4 * k + 1] = v.y; rgv[4 * k + 2] = v.z; rgv[4 * k + 3] = v.w;
             }
-            rbeta = bb[(int64_t)(tok0 + min(gc, Lm1)) * p.b_st];
+            rbeta = *(const float *)(bcb + min(bro, Lm1 * bst));
         };
         // Raw g of chunk c (the t-th of this segment) into the staging buffer, transposed: channel
         // row ch holds its 32 tokens as 8 groups of 4, group k at slot k ^ ((ch >> 4) & 7), which
@@ -461,7 +471,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         // transposed reads: lane k of each 16-lane group addresses row k/4 and channel
         // 4*(k%4) of a 16-channel slice; it receives 4 rows of channel (its slice) + (lane%16)
         const int tr_row = (lane & 15) >> 2, tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        bf16 *ob = has_out ? (bf16 *)p.o + bsel * p.o_sb + h * p.o_sh + t0 * p.o_st : nullptr;
+        char *ob = has_out ? (char *)p.o + 2 * (bsel * p.o_sb + h * p.o_sh + t0 * p.o_st) : nullptr;
+        const uint32_t ost = 2 * (uint32_t)p.o_st, oro = l32 * ost + 2 * (32 * cw + 4 * g2);
         f32x16 S[4];
         const int vcol = 32 * cw + l32;
         {
@@ -490,6 +501,17 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                         for (int r = 0; r < 4; ++r) S[m][4 * q + r] = (32 * m + 8 * q + 4 * g2 + r == vcol) ? one : 0.f;
             }
         }
+        // V enters R = V - Kt S on the matrix cores: IdV[j] is the A operand of an identity
+        // over tokens 16j..16j+15 (element e of lane (i, g) is 1 where token 16j + 8(e/4) + 4g +
+        // e%4 is row i), scaled by vscale
+        Frag8<bf16> IdV[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float t8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t8[e] = (l32 == 16 * j + 8 * (e >> 2) + 4 * g2 + (e & 3)) ? vscale : 0.f;
+            IdV[j].set(t8);
+        }
         if (nck > 0) prefetch_qkv(c_begin);
         sync();
         sync();
@@ -511,13 +533,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             prefetch_qkv(min(c_begin + t + 1, c_last));
             Frag8<bf16> RB[2];
             {
-                f32x16 R;
+                f32x16 R = {};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float v4[4];
-                    V4::unpack(lds_tr16(cV + (8 * q + 4 * g2 + tr_row) * KR_LD + 32 * cw + tr_col), v4);
-                    R[4 * q] = v4[0] * vscale; R[4 * q + 1] = v4[1] * vscale;
-                    R[4 * q + 2] = v4[2] * vscale; R[4 * q + 3] = v4[3] * vscale;
+                for (int j = 0; j < 2; ++j) {
+                    Frag8<bf16> fv;
+                    const bf16 *p0 = cV + (16 * j + 4 * g2 + tr_row) * KR_LD + 32 * cw + tr_col;
+                    fv.load44_tr(p0, p0 + 8 * KR_LD);
+                    mma32(R, IdV[j], fv);
                 }
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
@@ -601,7 +623,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     }
                 }
                 if (has_out && l32 < cL) {
-                    bf16 *dst = ob + (int64_t)(ctok0 + l32) * p.o_st + 32 * cw + 4 * g2;
+                    bf16 *dst = (bf16 *)(ob + (int64_t)ctok0 * ost + oro);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float o4[4] = {O[4 * q], O[4 * q + 1], O[4 * q + 2], O[4 * q + 3]};

@@ -46,6 +46,16 @@ template <> struct Elem<float> {
     static __device__ __forceinline__ float from_f(float x) { return x; }
 };
 
+// Two fp32 values rounded to bf16 (nearest-even) as one packed word, low half first: a
+// two-wide conversion, which maps onto one packed-convert instruction.
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // 4 consecutive elements, loaded/stored as one 8-byte (bf16) or 16-byte (fp32) access.
 template <typename ET> struct Vec4;
 template <> struct Vec4<bf16> {
@@ -59,9 +69,7 @@ template <> struct Vec4<bf16> {
         f[3] = __builtin_bit_cast(float, v.y & 0xffff0000u);
     }
     static __device__ __forceinline__ raw pack(const float *f) {
-        bf16x4 b;
-        b[0] = (bf16)f[0]; b[1] = (bf16)f[1]; b[2] = (bf16)f[2]; b[3] = (bf16)f[3];
-        return __builtin_bit_cast(uint2, b);
+        return make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
     }
     static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
 };
@@ -81,8 +89,7 @@ template <typename ET> struct Frag8;
 template <> struct Frag8<bf16> {
     bf16x8 v;
     __device__ __forceinline__ void set(const float *f) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (bf16)f[e];
+        v = __builtin_bit_cast(bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
     }
     // 8 contiguous elements
     __device__ __forceinline__ void load8(const bf16 *p) { v = *(const bf16x8 *)p; }
@@ -141,9 +148,7 @@ template <typename ET> struct Frag4;
 template <> struct Frag4<bf16> {
     s16x4 v;
     __device__ __forceinline__ void set(const float *f) {
-        bf16x4 b;
-        b[0] = (bf16)f[0]; b[1] = (bf16)f[1]; b[2] = (bf16)f[2]; b[3] = (bf16)f[3];
-        v = __builtin_bit_cast(s16x4, b);
+        v = __builtin_bit_cast(s16x4, make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3])));
     }
     __device__ __forceinline__ void load4(const bf16 *p) { v = __builtin_bit_cast(s16x4, *(const uint2 *)p); }
 };

@@ -182,6 +182,30 @@ def test_workspace_size_of_segmented_plan(lib):
     assert st == 0 and n.value == 0     # single segment with the in-chunk scan: no workspace
 
 
+def test_pipelined_kernel_needs_32bit_chunk_offsets(lib):
+    """The pipelined kernel addresses each 32-token chunk with 32-bit byte offsets: a token
+    stride of 2^25 bf16 elements (32 rows = 2 GiB) is refused when that kernel is forced,
+    and planned onto the 64-token kernel otherwise."""
+    big = 1 << 25
+    gap = 1 << 38
+    s = dict(q=desc([100, 2, 128], KDA_BF16, FAKE, strides=[big, 128, 1]),
+             k=desc([100, 2, 128], base=FAKE + gap), v=desc([100, 2, 128], base=FAKE + 2 * gap),
+             g=desc([100, 2, 128], KDA_F32, FAKE + 3 * gap), beta=desc([100, 2], KDA_F32, FAKE + 4 * gap),
+             s0=None, cu=desc([4], KDA_I32, FAKE + 6 * gap), out=desc([100, 2, 128], base=FAKE + 7 * gap), sT=None)
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    n = ctypes.c_size_t(0)
+    args = [r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")]
+    opts = kda.options(nseg=1, variant=2)
+    assert lib.kda_prefill_workspace_size(*args, ctypes.byref(opts), ctypes.byref(n)) == 6
+    assert b"token strides" in lib.kda_last_error()
+    opts = kda.options(nseg=1, variant=0)
+    assert lib.kda_prefill_workspace_size(*args, ctypes.byref(opts), ctypes.byref(n)) == 0, lib.kda_last_error()
+    s["q"] = desc([100, 2, 128], KDA_BF16, FAKE, strides=[big // 2, 128, 1])      # 1 GiB per 32 rows: fits
+    args = [r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")]
+    opts = kda.options(nseg=1, variant=2)
+    assert lib.kda_prefill_workspace_size(*args, ctypes.byref(opts), ctypes.byref(n)) == 0, lib.kda_last_error()
+
+
 def test_python_binding_refuses_without_gpu():
     import torch
     if torch.cuda.is_available():
