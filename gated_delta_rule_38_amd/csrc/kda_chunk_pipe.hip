@@ -119,6 +119,43 @@ __device__ __forceinline__ void tsweep(float (&x)[16], const float (&a)[16])
     if constexpr (J > 1) tsweep<J - 1>(x, a);
 }
 
+// The decay of one 32x32 state tile: accumulator element 4q + r (row 32M + 8q + 4g + r, g the
+// lane's half) times element r of dd on lane 4M + q of the lane's 16-lane row, by DPP row
+// broadcast -- every lane loads dd = decays 8 l16 + 4g + 0..3, so a 16-lane row holds the 64
+// decays its half of the tile needs.  dd comes straight from LDS (no VALU write before the DPP
+// read).  The closing s_nop gives the two wait states a matrix-core read of the tile needs after
+// a VALU write, which the compiler does not insert after inline assembly.
+template <int M>
+__device__ __forceinline__ void decay_tile(f32x16 &s, const float4 dd)
+{
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = s[k];
+    asm(
+        "v_mul_f32_dpp %0, %16, %0 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %1, %17, %1 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %2, %18, %2 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %3, %19, %3 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %4, %16, %4 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %5, %17, %5 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %6, %18, %6 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %7, %19, %7 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %8, %16, %8 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %9, %17, %9 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %10, %18, %10 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %11, %19, %11 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %12, %16, %12 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %13, %17, %13 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %14, %18, %14 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %15, %19, %15 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n"
+        "s_nop 1"
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+          "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
+        : "v"(dd.x), "v"(dd.y), "v"(dd.z), "v"(dd.w), "i"(4 * M), "i"(4 * M + 1), "i"(4 * M + 2), "i"(4 * M + 3));
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s[k] = x[k];
+}
+
 template <bool STALL>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
@@ -568,16 +605,13 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             // ---------------- interval 2: U = (T diag(beta)) R; O = Qt S + P U, stored
             if (cact) {
                 // the decay of the state update first: S is not read again before it (O uses SB)
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 d = *(const float4 *)(cDec + 32 * m + 8 * q + 4 * g2);
-                        S[m][4 * q + 0] *= d.x;
-                        S[m][4 * q + 1] *= d.y;
-                        S[m][4 * q + 2] *= d.z;
-                        S[m][4 * q + 3] *= d.w;
-                    }
+                {
+                    const float4 dd = *(const float4 *)(cDec + 8 * l16 + 4 * g2);
+                    decay_tile<0>(S[0], dd);
+                    decay_tile<1>(S[1], dd);
+                    decay_tile<2>(S[2], dd);
+                    decay_tile<3>(S[3], dd);
+                }
                 f32x16 U = {};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
