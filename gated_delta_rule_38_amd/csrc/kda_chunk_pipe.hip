@@ -184,7 +184,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     // T diag(beta) of one chunk from its A and beta, into pT, in two parts, each run by one
     // wave: the diagonal 16x16 blocks (from sAd; also leaves T_00 and T_11 in sTb) and, a
     // step later, the off-diagonal block (from sA10 and sTb).
-    auto build_T_diag = [&](const int b, const float *betac, bf16 *pT) {
+    auto build_T_diag = [&](const int b, const float (&bt)[16], bf16 *pT) {
         // Diagonal 16x16 block b of T = (I + A)^-1, one row per lane (each 16-lane group
         // holds the whole block).  T = I - T A gives, for row i, T_ic = [i == c] -
         // sum_{j > c} T_ij A_jc, so column j of the row is final once the columns after it
@@ -193,13 +193,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         // reaches the other lanes of the group by a DPP broadcast from lane j of the 16-lane
         // row, so the sweep makes no LDS access.
         const int i = l16;
-        float a[16], bt[16], x[16];
+        float a[16], x[16];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const float4 a4 = *(const float4 *)(sAd + (16 * b + i) * A_LD + 4 * c4);
-            const float4 b4 = *(const float4 *)(betac + 16 * b + 4 * c4);
             a[4 * c4] = a4.x; a[4 * c4 + 1] = a4.y; a[4 * c4 + 2] = a4.z; a[4 * c4 + 3] = a4.w;
-            bt[4 * c4] = b4.x; bt[4 * c4 + 1] = b4.y; bt[4 * c4 + 2] = b4.z; bt[4 * c4 + 3] = b4.w;
         }
 #pragma unroll
         for (int c = 0; c < 16; ++c) x[c] = (c == i) ? 1.f : 0.f;
@@ -393,13 +391,17 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         };
         // gate scan of the staged chunk c (the t-th of this segment) into Gamma * log2(e),
         // plus the per-channel scales and decay ring slot t % 3
-        auto scan = [&](int c, int t) {
+        auto scan_load = [&](float4 (&gcol)[C / 4]) {
+#pragma unroll
+            for (int k = 0; k < C / 4; ++k) gcol[k] = *(const float4 *)(sGraw + sc * GT_LD + 4 * (k ^ ((sc >> 4) & 7)));
+        };
+        auto scan = [&](int c, int t, const float4 (&gcol)[C / 4]) {
             const int L = min(C, len - c * C);
             if (sc >= 0) {
                 float rg[C];
 #pragma unroll
                 for (int k = 0; k < C / 4; ++k) {
-                    const float4 v = *(const float4 *)(sGraw + sc * GT_LD + 4 * (k ^ ((sc >> 4) & 7)));
+                    const float4 v = gcol[k];
                     rg[4 * k] = v.x; rg[4 * k + 1] = v.y; rg[4 * k + 2] = v.z; rg[4 * k + 3] = v.w;
                 }
                 // tail rows re-read token L-1 (clamped loads), so a precomputed Gamma needs
@@ -436,7 +438,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             prefetch_g(min(c_begin + 1, c_last));
         }
         sync();
-        if (nck > 0) scan(c_begin, 0);
+        if (nck > 0 && sc >= 0) {
+            float4 gcol[C / 4];
+            scan_load(gcol);
+            scan(c_begin, 0, gcol);
+        }
         sync();
         for (int t = 0; nck > 0 && t <= nck; ++t) {
             const bool pact = t < nck;                           // builds chunk c_begin + t into buffer t % 2
@@ -455,20 +461,24 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             // ---------------- interval 2: A^T and P^T sub-tiles (16x16, k = 128), diagonal T blocks
             //                  of chunk t; gate scan of chunk t+1
             // 16x16 tile of A^T (mat 0: rows i scaled by beta_i, strictly lower) or P^T (mat 1:
-            // lower including the diagonal) for row block ib, column block jb
-            auto tile = [&](int mat, int ib, int jb, float (&vals)[4]) {
+            // lower including the diagonal) for row block ib, column block jb.  A wave first issues
+            // every LDS read of its interval-2 work, then computes: its reads then wait in the
+            // LDS queue once, not once per dependent step.
+            struct TileOps { Frag8<bf16> fa[D / 32], fb[D / 32]; };
+            auto tile_load = [&](int mat, int ib, int jb, TileOps &o) {
                 const bf16 *arow = ((ib == jb) ? sZ : sKb) + (16 * jb + l16) * X_LD;
                 const bf16 *brow = (mat ? sY : sX) + (16 * ib + l16) * X_LD;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < D / 32; ++s) {
-                    Frag8<bf16> fa, fb;
-                    fa.load8(arow + 32 * s + 8 * g4);
-                    fb.load8(brow + 32 * s + 8 * g4);
-                    mma16(acc, fa, fb);
+                    o.fa[s].load8(arow + 32 * s + 8 * g4);
+                    o.fb[s].load8(brow + 32 * s + 8 * g4);
                 }
+            };
+            auto tile = [&](int mat, int ib, int jb, const TileOps &o, float sc_i, float (&vals)[4]) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) mma16(acc, o.fa[s], o.fb[s]);
                 const int i = 16 * ib + l16, j0 = 16 * jb + 4 * g4;
-                const float sc_i = mat ? 1.f : betac[i];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) vals[r] = (j0 + r < i + mat) ? acc[r] * sc_i : 0.f;
             };
@@ -476,28 +486,45 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 // wave 0 -> A (0,0) then T_00, wave 2 -> A (1,1) then T_11
                 if (pact) {
                     const int b = pw >> 1;
+                    TileOps o;
+                    tile_load(0, b, b, o);
+                    float bt[16];
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4) {
+                        const float4 b4 = *(const float4 *)(betac + 16 * b + 4 * c4);
+                        bt[4 * c4] = b4.x; bt[4 * c4 + 1] = b4.y; bt[4 * c4 + 2] = b4.z; bt[4 * c4 + 3] = b4.w;
+                    }
+                    const float sc_i = betac[16 * b + l16];
+                    __builtin_amdgcn_sched_barrier(0);
                     float vals[4];
-                    tile(0, b, b, vals);
+                    tile(0, b, b, o, sc_i, vals);
                     *(float4 *)(sAd + (b * 16 + l16) * A_LD + 4 * g4) = make_float4(vals[0], vals[1], vals[2], vals[3]);
                     lds_fence();          // this wave's A rows, written above by other lanes
-                    build_T_diag(b, betac, pT);
+                    build_T_diag(b, bt, pT);
                 }
             } else {
                 // wave 1 -> A (1,0) and P (1,0), wave 3 -> P (0,0) and P (1,1); both write the zero
                 // P block (0,1); then the gate scan of chunk t+1.  One straight-line block (past the
                 // last chunk its results are never read), so the scan can overlap the MFMAs.
                 const bool w1 = pw == 1;
+                TileOps o[2];
+#pragma unroll
+                for (int it = 0; it < 2; ++it) tile_load(w1 ? it : 1, w1 ? 1 : it, w1 ? 0 : it, o[it]);
+                float4 gcol[C / 4];
+                scan_load(gcol);
+                const float sc_a = betac[16 + l16];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
                     const int mat = w1 ? it : 1;
                     const int ib = w1 ? 1 : it, jb = w1 ? 0 : it;
                     float vals[4];
-                    tile(mat, ib, jb, vals);
+                    tile(mat, ib, jb, o[it], mat ? 1.f : sc_a, vals);
                     bf16 *dst = (mat == 0) ? sA10 + l16 * A_LD + 4 * g4 : pP + (16 * ib + l16) * P_LD + 16 * jb + 4 * g4;
                     V4::store(dst, V4::pack(vals));
                 }
                 V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
-                scan(pc + 1, t + 1);
+                scan(pc + 1, t + 1, gcol);
             }
             sync();
         }
