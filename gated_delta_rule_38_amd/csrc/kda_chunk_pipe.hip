@@ -50,10 +50,11 @@ constexpr int D = 128;
 constexpr int NT = 512;         // 4 consumer + 4 producer waves
 // leading dimensions (elements); padding matches each tile's read width
 constexpr int W_LD = D + 4;     // Qt, -Kt [32][128] bf16, 8-byte reads
-constexpr int KR_LD = D + 16;   // Kh, V [32][128] bf16, row-major, read transposed (4 rows x 32 B per 16 lanes)
+constexpr int KR_LD = D + 32;   // Kh, V [32][128] bf16, row-major, read transposed (4 rows x 32 B per 16 lanes;
+                                // this stride makes those reads free of LDS bank conflicts)
 constexpr int P_LD = C + 4;     // P, T diag(beta) [32][32] bf16, 8-byte reads
 constexpr int G_LD = D + 4;     // Gamma * log2(e) [32][128] fp32
-constexpr int X_LD = D + 8;     // X, Y, Z, Kb [rows][128] bf16, 16-byte reads
+constexpr int X_LD = D + 16;    // X, Y, Z, Kb [rows][128] bf16, 16-byte reads (bank-conflict free at this stride)
 constexpr int A_LD = 16 + 4;    // 16x16 blocks: A10 (bf16), A diagonal (fp32), T_00 (fp32), T_11 (bf16)
 // one operand buffer (bytes)
 constexpr int B_QT = 0;
