@@ -303,8 +303,24 @@ struct ProfRec {
     hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-std::vector<ProfRec> g_prof;
+std::vector<ProfRec> g_prof;                         // launches recorded since the last read
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_pool;   // idle event pairs
 bool g_prof_on = false;
+
+// Event pairs come from a pool that profiling's enable call fills, so that a timed launch
+// costs two event records and no event creation.
+hipError_t prof_pair(hipEvent_t &a, hipEvent_t &b)
+{
+    if (!g_prof_pool.empty()) {
+        a = g_prof_pool.back().first;
+        b = g_prof_pool.back().second;
+        g_prof_pool.pop_back();
+        return hipSuccess;
+    }
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    return e;
+}
 
 template <typename F>
 hipError_t timed(const char *name, hipStream_t st, F &&launch)
@@ -312,8 +328,10 @@ hipError_t timed(const char *name, hipStream_t st, F &&launch)
     if (!g_prof_on) return launch();
     ProfRec r{name, nullptr, nullptr};
     hipError_t e;
-    if ((e = hipEventCreate(&r.a)) != hipSuccess) return e;
-    if ((e = hipEventCreate(&r.b)) != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if ((e = prof_pair(r.a, r.b)) != hipSuccess) return e;
+    }
     if ((e = hipEventRecord(r.a, st)) != hipSuccess) return e;
     e = launch();
     if (e != hipSuccess) return e;
@@ -539,7 +557,21 @@ void kda_release_cached_workspace(void)
     (void)hipSetDevice(cur);
 }
 
-void kda_profile_enable(int on) { g_prof_on = on != 0; }
+void kda_profile_enable(int on)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = on != 0;
+    // enough idle pairs for a few hundred launches between reads
+    while (g_prof_on && g_prof_pool.size() + g_prof.size() < 512) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) break;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            break;
+        }
+        g_prof_pool.emplace_back(a, b);
+    }
+}
 
 kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *launches)
 {
@@ -556,8 +588,7 @@ kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *lau
             tot += ms;
             ++cnt;
         }
-        (void)hipEventDestroy(r.a);
-        (void)hipEventDestroy(r.b);
+        g_prof_pool.emplace_back(r.a, r.b);
     }
     g_prof.clear();
     if (total_ms) *total_ms = tot;

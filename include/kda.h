@@ -145,7 +145,9 @@ void kda_release_cached_workspace(void);
 /* Kernel timing for measurement: when enabled, every kernel the library
  * enqueues is bracketed by hipEvents on its stream.  kda_profile_read()
  * synchronises those events, returns the summed milliseconds and launch count
- * of kernels whose name contains `kernel` (e.g. "chunk"), and clears them. */
+ * of kernels whose name contains `kernel` (e.g. "chunk"), and clears them.
+ * Enabling creates a pool of events on the current device (reused across
+ * reads), so timed launches create none; call it with that device current. */
 void kda_profile_enable(int on);
 kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 
