@@ -4,8 +4,10 @@
 // Plan (host-known values only, never a device read): chains = N * H.  When
 // chains fill the GPU's compute units one chunk-kernel workgroup runs each
 // chain start to end (one launch, no workspace).  When they do not, each chain
-// is cut into nseg segments and the path is PREP -> segment build (M, C) ->
-// COMBINE -> segment outputs, following the PREP / SEG / COMB pipeline of the
+// is cut into nseg segments and the path is segment build (M, C) -> COMBINE ->
+// segment outputs (each chunk-kernel pass runs the in-chunk gate scan of PREP
+// on its own chunks; the standalone PREP kernel is an option), following the
+// PREP / SEG / COMB pipeline of the
 // cudnn-frontend Hopper KDA prefill PR (#1056), whose launch selection picks
 // the segment count from the SM count and N*H; here the CU count of the device
 // plays that role.  The workspace is sized exactly for the plan and is empty
@@ -280,7 +282,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     }
     const int prep = o ? o->prep : 0;
     if (prep < 0 || prep > 2) return fail(KDA_ERR_UNSUPPORTED, "prep mode %d", prep);
-    pl.standalone_prep = prep == 1 || (prep == 0 && pl.nseg > 1);
+    pl.standalone_prep = prep == 1;   // otherwise every chunk-kernel pass scans its own chunks
     size_t off = 0;
     if (pl.standalone_prep) {
         pl.off_gamma = off;

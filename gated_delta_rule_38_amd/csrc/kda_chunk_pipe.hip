@@ -157,7 +157,9 @@ __device__ __forceinline__ void decay_tile(f32x16 &s, const float4 dd)
     for (int k = 0; k < 16; ++k) s[k] = x[k];
 }
 
-template <bool STALL>
+// OUT: the launch's roles store outputs (ROLE_OUT, ROLE_SEG_OUT); the segment-map roles do
+// not, and skip everything that only feeds O: q, Qt, the P tiles and the O products.
+template <bool STALL, bool OUT>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     const int c_begin = min(seg * cps, nchunks);
     const int c_end = min(c_begin + cps, nchunks);
     const int nck = c_end - c_begin;
-    const bool has_out = (role == ROLE_OUT || role == ROLE_SEG_OUT);
+    constexpr bool has_out = OUT;
     const bool has_v = (role != ROLE_SEG_M);
 
     // ------------------------------------------------ gate-factored operands (all waves)
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         const uint32_t ql = Lm1 * qst + 2 * ech, kl = Lm1 * kst + 2 * ech, vl = Lm1 * vst + 2 * ech;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            rq[r] = *(const uint2 *)(qc + min(qro + r * qst, ql));
+            if constexpr (OUT) rq[r] = *(const uint2 *)(qc + min(qro + r * qst, ql));
             rk[r] = *(const uint2 *)(kc + min(kro + r * kst, kl));
             rv[r] = *(const uint2 *)(vc + min(vro + r * vst, vl));
         }
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             const int i = 2 * etp + r;
             const float4 Gv = *(const float4 *)(sG + i * G_LD + ech);
             const float G4[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
-            float qf[4], kf[4];
-            V4::unpack(rq[r], qf);
+            float qf[4] = {0.f, 0.f, 0.f, 0.f}, kf[4];
+            if constexpr (OUT) V4::unpack(rq[r], qf);
             V4::unpack(rk[r], kf);
             float X[4], Y[4], Z[4], Kb[4], Qt[4], Kt[4];
 #pragma unroll
@@ -333,8 +335,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             V4::store(sZ + i * X_LD + ech, V4::pack(Z));
             // sub-block 0: -Kt is X, negated exactly by flipping the bf16 sign bits
             V4::store(pKt + i * W_LD + ech, B1 ? V4::pack(Kt) : make_uint2(Xp.x ^ 0x80008000u, Xp.y ^ 0x80008000u));
-            V4::store(sY + i * X_LD + ech, V4::pack(Y));      // (unused without outputs)
-            V4::store(pQt + i * W_LD + ech, V4::pack(Qt));
+            if constexpr (OUT) {
+                V4::store(sY + i * X_LD + ech, V4::pack(Y));
+                V4::store(pQt + i * W_LD + ech, V4::pack(Qt));
+            }
             if (!B1) V4::store(sKb + i * X_LD + ech, V4::pack(Kb));
         }
         // Kh and V rows, row-major like Qt and Kt (the consumers read them transposed)
@@ -507,25 +511,43 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 // wave 1 -> A (1,0) and P (1,0), wave 3 -> P (0,0) and P (1,1); both write the zero
                 // P block (0,1); then the gate scan of chunk t+1.  One straight-line block (past the
                 // last chunk its results are never read), so the scan can overlap the MFMAs.
-                const bool w1 = pw == 1;
-                TileOps o[2];
+                if constexpr (OUT) {
+                    const bool w1 = pw == 1;
+                    TileOps o[2];
 #pragma unroll
-                for (int it = 0; it < 2; ++it) tile_load(w1 ? it : 1, w1 ? 1 : it, w1 ? 0 : it, o[it]);
-                float4 gcol[C / 4];
-                scan_load(gcol);
-                const float sc_a = betac[16 + l16];
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int it = 0; it < 2; ++it) tile_load(w1 ? it : 1, w1 ? 1 : it, w1 ? 0 : it, o[it]);
+                    float4 gcol[C / 4];
+                    scan_load(gcol);
+                    const float sc_a = betac[16 + l16];
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int it = 0; it < 2; ++it) {
-                    const int mat = w1 ? it : 1;
-                    const int ib = w1 ? 1 : it, jb = w1 ? 0 : it;
-                    float vals[4];
-                    tile(mat, ib, jb, o[it], mat ? 1.f : sc_a, vals);
-                    bf16 *dst = (mat == 0) ? sA10 + l16 * A_LD + 4 * g4 : pP + (16 * ib + l16) * P_LD + 16 * jb + 4 * g4;
-                    V4::store(dst, V4::pack(vals));
+                    for (int it = 0; it < 2; ++it) {
+                        const int mat = w1 ? it : 1;
+                        const int ib = w1 ? 1 : it, jb = w1 ? 0 : it;
+                        float vals[4];
+                        tile(mat, ib, jb, o[it], mat ? 1.f : sc_a, vals);
+                        bf16 *dst = (mat == 0) ? sA10 + l16 * A_LD + 4 * g4 : pP + (16 * ib + l16) * P_LD + 16 * jb + 4 * g4;
+                        V4::store(dst, V4::pack(vals));
+                    }
+                    V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
+                    scan(pc + 1, t + 1, gcol);
+                } else {
+                    // no outputs: wave 1 -> A (1,0) only, wave 3 -> the scan only
+                    float4 gcol[C / 4];
+                    if (pw == 1) {
+                        TileOps o;
+                        tile_load(0, 1, 0, o);
+                        scan_load(gcol);
+                        const float sc_a = betac[16 + l16];
+                        __builtin_amdgcn_sched_barrier(0);
+                        float vals[4];
+                        tile(0, 1, 0, o, sc_a, vals);
+                        V4::store(sA10 + l16 * A_LD + 4 * g4, V4::pack(vals));
+                    } else {
+                        scan_load(gcol);
+                    }
+                    scan(pc + 1, t + 1, gcol);
                 }
-                V4::store(pP + l16 * P_LD + 16 + 4 * g4, V4::zero());   // P block (0,1)
-                scan(pc + 1, t + 1, gcol);
             }
             sync();
         }
@@ -659,19 +681,21 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 // state update, in one block so the three MFMA chains and the conversions can
                 // interleave; the stores come last
                 f32x16 O = {};
+                if constexpr (OUT) {
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    Frag8<bf16> fb;
-                    const bf16 *row = cQt + l32 * W_LD + 16 * s + 4 * g2;
-                    fb.load44(row, row + 8);
-                    mma32(O, SB[s], fb);
-                }
+                    for (int s = 0; s < 8; ++s) {
+                        Frag8<bf16> fb;
+                        const bf16 *row = cQt + l32 * W_LD + 16 * s + 4 * g2;
+                        fb.load44(row, row + 8);
+                        mma32(O, SB[s], fb);
+                    }
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    Frag8<bf16> fb;
-                    const bf16 *row = cP + l32 * P_LD + 16 * s + 4 * g2;
-                    fb.load44(row, row + 8);
-                    mma32(O, UB[s], fb);
+                    for (int s = 0; s < 2; ++s) {
+                        Frag8<bf16> fb;
+                        const bf16 *row = cP + l32 * P_LD + 16 * s + 4 * g2;
+                        fb.load44(row, row + 8);
+                        mma32(O, UB[s], fb);
+                    }
                 }
                 // ---------------- state update: S <- Diag(e^{G_L}) S + Kh^T U
 #pragma unroll
@@ -684,7 +708,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                         mma32(S[m], fa, UB[s]);
                     }
                 }
-                if (has_out && l32 < cL) {
+                if (OUT && l32 < cL) {
                     bf16 *dst = (bf16 *)(ob + (int64_t)ctok0 * ost + oro);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -718,8 +742,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStream_t st)
 {
     if (grid <= 0) return hipSuccess;
-    if (stall) hipLaunchKernelGGL(pipe::chunk_pipe_kernel<true>, dim3(grid), dim3(pipe::NT), 0, st, p);
-    else hipLaunchKernelGGL(pipe::chunk_pipe_kernel<false>, dim3(grid), dim3(pipe::NT), 0, st, p);
+    const bool out = p.role == ROLE_OUT || p.role == ROLE_SEG_OUT;
+    if (stall && out) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<true, true>), dim3(grid), dim3(pipe::NT), 0, st, p);
+    else if (stall) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<true, false>), dim3(grid), dim3(pipe::NT), 0, st, p);
+    else if (out) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<false, true>), dim3(grid), dim3(pipe::NT), 0, st, p);
+    else hipLaunchKernelGGL((pipe::chunk_pipe_kernel<false, false>), dim3(grid), dim3(pipe::NT), 0, st, p);
     return hipGetLastError();
 }
 

@@ -6,57 +6,72 @@
 //     S_end = M_s S_start + C_s,
 // where M_s is the segment's end state from (V = 0, S_start = I) and C_s from
 // S_start = 0 (both built by the chunk kernel's segment roles).  Columns of S
-// evolve independently, so one workgroup owns one 32-column value slab of one
+// evolve independently, so one workgroup owns one 16-column value slab of one
 // chain and walks the segments in order: start[0] = initial state,
-// start[s+1] = M_s start[s] + C_s, in fp32 on the fp32 matrix cores
-// (M_s and C_s stay fp32: they compose many chunk maps).
+// start[s+1] = M_s start[s] + C_s, in fp32 on the fp32 matrix cores (M_s and
+// C_s stay fp32: they compose many chunk maps).  Narrow slabs put D/16
+// workgroups on every chain, so a handful of chains still spreads over many
+// CUs; M_s and C_s do not depend on the scan, so each wave loads the next
+// segment's operands while it multiplies the current one.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
 template <int D>
-__global__ __launch_bounds__(64 * (D / 32)) void combine_kernel(const CombineParams p)
+__global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombineParams p)
 {
-    constexpr int NW = D / 32, NT = 64 * NW, ST_LD = D + 4;
-    __shared__ __attribute__((aligned(16))) float sS[32 * ST_LD];   // slab, transposed: [v][key channel]
-    const int chain = blockIdx.x, slab = blockIdx.y;
+    constexpr int NW = D / 16, NT = 64 * NW, SL = 16, ST_LD = D + 4, KB = D / 16;
+    // the slab's current state, transposed ([value column][key channel]), double-buffered so
+    // that one barrier per segment orders every write after the reads it replaces
+    __shared__ __attribute__((aligned(16))) float sS[2][SL * ST_LD];
+    const int chain = blockIdx.x, slab = blockIdx.y, v0 = SL * slab;
     const int n = chain / p.H, h = chain % p.H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
-    const int v0 = 32 * slab;
-    for (int e = tid; e < D * 32; e += NT) {
-        const int ch = e >> 5, v = e & 31;
-        sS[v * ST_LD + ch] = p.s0 ? p.s0[n * p.s0_sn + h * p.s0_sh + ch * p.s0_sr + v0 + v] : 0.f;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    float *start = p.start + (int64_t)chain * p.nseg * D * D;
+    const float *maps = p.maps + (int64_t)chain * p.nseg * 2 * D * D;
+
+    for (int e = tid; e < D * SL; e += NT) {
+        const int ch = e / SL, v = e % SL;
+        const float x = p.s0 ? p.s0[n * p.s0_sn + h * p.s0_sh + ch * p.s0_sr + v0 + v] : 0.f;
+        sS[0][v * ST_LD + ch] = x;
+        start[ch * D + v0 + v] = x;
     }
+    // Wave w produces rows 16w..16w+15 of the slab with 16x16x4 fp32 MFMAs.  The sum over key
+    // channels k is taken in the order k = 16j + 4(lane/16) + e for MFMA 4j + e, so each lane
+    // feeds four consecutive MFMAs from one 16-byte read of its M row and one of the slab.
+    const int mrow = 16 * wave + l16;
+    float4 m[KB];
+    float c[4];
+    auto load_maps = [&](int s) {
+        const float *M = maps + (int64_t)s * 2 * D * D, *C = M + D * D;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) m[j] = *(const float4 *)(M + mrow * D + 16 * j + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[r] = C[(16 * wave + 4 * g4 + r) * D + v0 + l16];
+    };
+    if (p.nseg > 1) load_maps(0);
     __syncthreads();
-    for (int s = 0; s < p.nseg; ++s) {
-        float *st = p.start + ((int64_t)chain * p.nseg + s) * D * D;
-        for (int e = tid; e < D * 32; e += NT) {
-            const int ch = e >> 5, v = e & 31;
-            st[ch * D + v0 + v] = sS[v * ST_LD + ch];
+    for (int s = 0; s + 1 < p.nseg; ++s) {
+        const float *cur = sS[s & 1];
+        f32x4 acc = {c[0], c[1], c[2], c[3]};
+        float4 a[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) a[j] = m[j];
+        if (s + 2 < p.nseg) load_maps(s + 1);
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const float4 b = *(const float4 *)(cur + l16 * ST_LD + 16 * j + 4 * g4);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].x, b.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].y, b.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].z, b.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].w, b.w, acc, 0, 0, 0);
         }
-        if (s == p.nseg - 1) break;
-        const float *M = p.maps + (((int64_t)chain * p.nseg + s) * 2) * D * D;
-        const float *C = M + D * D;
-        f32x16 acc;
+        // lane (column l16, group g4) holds rows 16w + 4 g4 + r of start[s+1]
+        *(float4 *)(sS[(s + 1) & 1] + l16 * ST_LD + 16 * wave + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        float *st = start + (int64_t)(s + 1) * D * D;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[4 * q + r] = C[(32 * wave + 8 * q + 4 * g2 + r) * D + v0 + l32];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            Frag8<float> fa, fb;
-            const float *mrow = M + (32 * wave + l32) * D + 16 * ks + 4 * g2;
-            fa.load44(mrow, mrow + 8);
-            const float *srow = sS + l32 * ST_LD + 16 * ks + 4 * g2;
-            fb.load44(srow, srow + 8);
-            mma32(acc, fa, fb);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *(float4 *)(sS + l32 * ST_LD + 32 * wave + 8 * q + 4 * g2) =
-                make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        for (int r = 0; r < 4; ++r) st[(16 * wave + 4 * g4 + r) * D + v0 + l16] = acc[r];
         __syncthreads();
     }
 }
@@ -64,8 +79,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void combine_kernel(const CombinePar
 hipError_t launch_combine(const CombineParams &p, int D, int chains, hipStream_t st)
 {
     if (chains <= 0) return hipSuccess;
-    if (D == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(chains, 4), dim3(256), 0, st, p);
-    else if (D == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(chains, 2), dim3(128), 0, st, p);
+    if (D == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(chains, 128 / 16), dim3(64 * 128 / 16), 0, st, p);
+    else if (D == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(chains, 64 / 16), dim3(64 * 64 / 16), 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

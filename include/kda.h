@@ -85,7 +85,7 @@ typedef struct {
 /* Planner and test knobs.  A zero-filled struct (or NULL) means "automatic". */
 typedef struct {
     int32_t nseg;          /* segments per (sequence, head) chain; 0 = planner's choice, 1..64 forces */
-    int32_t prep;          /* 0 = planner; 1 = standalone PREP kernel; 2 = in-chunk (fused) gate scan */
+    int32_t prep;          /* 0 or 2 = in-chunk (fused) gate scan; 1 = standalone PREP kernel first     */
     int32_t stall_wave;    /* test hook: -1/0 = none; w+1 stalls wave w at every LDS hand-off        */
     int32_t stall_cycles;  /* length of each injected stall, in s_sleep units of 64 cycles           */
     int32_t variant;       /* 0 = planner; 1 = single-role 64-token chunk kernel; 2 = pipelined      */

@@ -160,8 +160,9 @@ def test_in_place_state_allowed(lib):
 
 
 def test_workspace_size_of_segmented_plan(lib):
-    """Forced nseg = 8 on B=2, H=16, T=4096, d=128: Gamma (fp32, one per
-    token-head-channel) + (M, C) per segment + start state per segment."""
+    """Forced nseg = 8 on B=2, H=16, T=4096, d=128: (M, C) per segment + start
+    state per segment, plus Gamma (fp32, one per token-head-channel) when the
+    standalone PREP kernel is asked for."""
     B, T, H, D = 2, 4096, 16, 128
     gap = 1 << 34
     s = dict(q=desc([B, T, H, D]), k=desc([B, T, H, D], base=FAKE + gap), v=desc([B, T, H, D], base=FAKE + 2 * gap),
@@ -174,8 +175,12 @@ def test_workspace_size_of_segmented_plan(lib):
                                         ctypes.byref(opts), ctypes.byref(n))
     assert st == 0, lib.kda_last_error()
     chains, dd = B * H, D * D * 4
-    want = B * T * H * D * 4 + chains * 8 * 2 * dd + chains * 8 * dd
+    want = chains * 8 * 2 * dd + chains * 8 * dd
     assert n.value == want
+    opts = kda.options(nseg=8, prep=1)
+    st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                        ctypes.byref(opts), ctypes.byref(n))
+    assert st == 0 and n.value == B * T * H * D * 4 + want
     opts = kda.options(nseg=1, prep=2)
     st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
                                         ctypes.byref(opts), ctypes.byref(n))

@@ -261,13 +261,40 @@ def test_forced_segments_match_oracle(kda, nseg, variant):
     check_full(x, out, sT, TOL["bf16"])
 
 
+@pytest.mark.parametrize("nseg", [1, 4])
 @pytest.mark.parametrize("variant", [1, 2])
-def test_standalone_prep_equals_fused_scan(kda, variant):
+def test_standalone_prep_equals_fused_scan(kda, variant, nseg):
     w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=13)
     x = gen(w)
-    o1, s1 = run(kda, x, nseg=1, prep=1, variant=variant)
-    o2, s2 = run(kda, x, nseg=1, prep=2, variant=variant)
+    say("nseg", nseg, "variant", variant)
+    o1, s1 = run(kda, x, nseg=nseg, prep=1, variant=variant)
+    o2, s2 = run(kda, x, nseg=nseg, prep=2, variant=variant)
     assert torch_equal(o1, o2) and torch_equal(s1, s2)
+
+
+@pytest.mark.parametrize("gate", [None, "mild", "zero"])
+@pytest.mark.parametrize("nseg", [3, 8])
+def test_forced_segments_fp32_d64(kda, nseg, gate):
+    """The fp32 debug mode (d = 64) through the segment maps and the d = 64 COMBINE."""
+    w = workloads.custom([700, 64, 1, 300], H=2, D=64, dtype="f32", dense=False, seed=15)
+    x = gen(w, gate=gate)
+    say("nseg", nseg, "fp32 d=64 gate", gate)
+    out, sT = run(kda, x, nseg=nseg)
+    check_full(x, out, sT, TOL["f32"])
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("gate", ["mild", "zero"])
+@pytest.mark.parametrize("nseg", [2, 5, 16])
+def test_forced_segments_slow_decay(kda, nseg, gate, variant):
+    """Segment maps M that are far from zero: with the drawn gates a state decays to
+    nothing within a segment (M underflows to 0), so slow and absent decay are what
+    exercise the M S_start term of COMBINE."""
+    w = workloads.custom([1500, 64, 1, 700], H=2, D=128, seed=16)
+    x = gen(w, gate=gate)
+    say("nseg", nseg, "gate", gate, "variant", variant)
+    out, sT = run(kda, x, nseg=nseg, variant=variant)
+    check_full(x, out, sT, TOL["bf16"])
 
 
 def test_in_place_state(kda):

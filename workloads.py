@@ -87,7 +87,8 @@ def make_inputs(w: Workload, device="cpu", gate: Optional[str] = None) -> dict:
     cu_seqlens (int32, or None in dense layout) and lengths.
 
     ``gate`` overrides the gate distribution for edge cases: "floor" sets every g
-    to -5, "zero" sets every g to 0.
+    to -5, "zero" sets every g to 0, "mild" scales the drawn g by 0.01 (slow decay,
+    so a state carries across many chunks).
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -115,6 +116,8 @@ def make_inputs(w: Workload, device="cpu", gate: Optional[str] = None) -> dict:
         g.fill_(GATE_LOWER_BOUND)
     elif gate == "zero":
         g.zero_()
+    elif gate == "mild":
+        g.mul_(0.01)
     s0 = None if w.zero_state else 0.1 * randn(N, H, D, D)
 
     out = {"lengths": list(w.lengths), "initial_state": s0}
