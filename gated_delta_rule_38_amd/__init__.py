@@ -34,7 +34,8 @@ class KdaTensor(ctypes.Structure):
 
 class KdaOptions(ctypes.Structure):
     _fields_ = [("nseg", ctypes.c_int32), ("prep", ctypes.c_int32),
-                ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32), ("variant", ctypes.c_int32)]
+                ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("gate_act", ctypes.c_int32), ("gate_lower_bound", ctypes.c_float), ("beta_act", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -124,9 +125,11 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be on the GPU")
 
 
-def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0, variant: int = 0) -> KdaOptions:
+def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0, variant: int = 0,
+            gate_logits: bool = False, gate_lower_bound: float = -5.0, beta_logits: bool = False) -> KdaOptions:
     o = KdaOptions()
     o.nseg, o.prep, o.variant = nseg, prep, variant
+    o.gate_act, o.gate_lower_bound, o.beta_act = int(bool(gate_logits)), gate_lower_bound, int(bool(beta_logits))
     o.stall_wave = stall_wave + 1 if stall_wave >= 0 else 0
     o.stall_cycles = stall_cycles
     return o
@@ -144,24 +147,29 @@ def _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, want_final
 
 
 def workspace_size(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
-                   nseg: int = 0, prep: int = 0, variant: int = 0) -> int:
+                   nseg: int = 0, prep: int = 0, variant: int = 0, gate_logits: bool = False,
+                   gate_lower_bound: float = -5.0, beta_logits: bool = False) -> int:
     lib = load_library()
     out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, False)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     n = ctypes.c_size_t(0)
-    _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(options(nseg, prep, variant=variant)),
-                                          ctypes.byref(n)))
+    opts = options(nseg, prep, variant=variant, gate_logits=gate_logits, gate_lower_bound=gate_lower_bound,
+                   beta_logits=beta_logits)
+    _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(n)))
     return n.value
 
 
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
             output_final_state: bool = True, nseg: int = 0, prep: int = 0, stall_wave: int = -1,
-            stall_cycles: int = 0, variant: int = 0, workspace=None, stream=None) -> Tuple:
+            stall_cycles: int = 0, variant: int = 0, gate_logits: bool = False, gate_lower_bound: float = -5.0,
+            beta_logits: bool = False, workspace=None, stream=None) -> Tuple:
     """KDA chunked prefill.  Returns (out, final_state).
 
     Dense layout: q, k, g [B, T, H, K], v [B, T, H, V], beta [B, T, H].
     Packed layout: q, k, g [T, H, K], v [T, H, V], beta [T, H] and int32
     ``cu_seqlens`` [N + 1] on the GPU.  States are fp32 [N, H, K, V].
+    ``gate_logits``: g holds logits x, the log decay is gate_lower_bound * sigmoid(x);
+    ``beta_logits``: beta holds logits, beta = sigmoid(beta) (both fused into the gate scan).
     With the default knobs this calls ``kda_prefill`` (library-cached
     workspace); any knob or a ``workspace`` tensor routes through
     ``kda_prefill_ws`` with a torch-allocated workspace.
@@ -172,11 +180,12 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, output_final_state)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    plain = nseg == 0 and prep == 0 and stall_wave < 0 and variant == 0 and workspace is None
+    plain = (nseg == 0 and prep == 0 and stall_wave < 0 and variant == 0 and workspace is None
+             and not gate_logits and not beta_logits)
     if plain:
         _check(lib.kda_prefill(*[_ptr(d) for d in ds], ctypes.c_void_p(st)))
         return out, final_state
-    opts = options(nseg, prep, stall_wave, stall_cycles, variant)
+    opts = options(nseg, prep, stall_wave, stall_cycles, variant, gate_logits, gate_lower_bound, beta_logits)
     need = ctypes.c_size_t(0)
     _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value:

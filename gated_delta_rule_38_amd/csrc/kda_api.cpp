@@ -282,6 +282,10 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     }
     const int prep = o ? o->prep : 0;
     if (prep < 0 || prep > 2) return fail(KDA_ERR_UNSUPPORTED, "prep mode %d", prep);
+    if (o && (o->gate_act < 0 || o->gate_act > 1 || o->beta_act < 0 || o->beta_act > 1))
+        return fail(KDA_ERR_UNSUPPORTED, "gate_act %d / beta_act %d (0 or 1)", o->gate_act, o->beta_act);
+    if (o && o->gate_act && !(o->gate_lower_bound >= -5.f && o->gate_lower_bound <= 0.f))
+        return fail(KDA_ERR_UNSUPPORTED, "gate_lower_bound %g outside [-5, 0]", (double)o->gate_lower_bound);
     pl.standalone_prep = prep == 1;   // otherwise every chunk-kernel pass scans its own chunks
     size_t off = 0;
     if (pl.standalone_prep) {
@@ -373,6 +377,9 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     cp.g_is_gamma = 0;
     cp.stall_wave = (o && o->stall_wave > 0) ? o->stall_wave - 1 : -1;
     cp.stall_iters = (o && o->stall_cycles > 0) ? std::max(1, o->stall_cycles / 127) : 0;
+    cp.gate_act = (o && o->gate_act) ? 1 : 0;
+    cp.gate_lb = o ? o->gate_lower_bound : 0.f;
+    cp.beta_act = (o && o->beta_act) ? 1 : 0;
     const bool stall = cp.stall_wave >= 0 && cp.stall_iters > 0;
     const int D = (int)P.D;
     hipError_t e;
@@ -390,6 +397,8 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
         pp.N = (int32_t)P.N; pp.H = (int32_t)P.H; pp.T = (int32_t)P.T; pp.D = D;
         pp.chunk = pl.chunk;
         pp.chunks_per_seq = P.dense ? (int32_t)((P.T + pl.chunk - 1) / pl.chunk) : 0;
+        pp.gate_act = cp.gate_act;
+        pp.gate_lb = cp.gate_lb;
         const int64_t nvc = P.dense ? P.B * pp.chunks_per_seq : (P.Ttot + pl.chunk - 1) / pl.chunk + P.N;
         if ((e = timed("kda_prep", st, [&] { return kda::launch_prep(pp, (int)nvc, st); })) != hipSuccess)
             return hip_fail(e, "PREP launch");

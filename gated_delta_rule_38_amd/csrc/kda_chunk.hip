@@ -234,14 +234,25 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
         const int tok0 = c * CHUNK;
         const int L = min(CHUNK, len - tok0);
 
-        // ---------------- stage 1: raw g (or Gamma) and beta into LDS
+        // ---------------- stage 1: raw g (or Gamma) and beta into LDS; logits in: the decays
+        //                  lb * sigmoid(x) (tail rows stay zero, so the scan skips them)
+        if (p.gate_act && !p.g_is_gamma) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float4 &x = rg[hh][r];
+                    x = make_float4(gate_act(x.x, p.gate_lb), gate_act(x.y, p.gate_lb), gate_act(x.z, p.gate_lb),
+                                    gate_act(x.w, p.gate_lb));
+                }
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 *(float4 *)(sG + (4 * tg + r) * G_LD + hh * HALF + 4 * cg) =
                     (4 * tg + r < L) ? rg[hh][r] : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tid < CHUNK) sBeta[tid] = (tid < L) ? rbeta : 0.f;
+        if (tid < CHUNK) sBeta[tid] = (tid < L) ? (p.beta_act ? sigmoid_act(rbeta) : rbeta) : 0.f;
         if (c + 1 < c_end) load_g(c + 1);
         sync();
 

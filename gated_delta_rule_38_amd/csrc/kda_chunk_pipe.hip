@@ -392,7 +392,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 *(float4 *)(sGraw + ch * GT_LD + 4 * (gq ^ ((ch >> 4) & 7))) =
                     make_float4(rgv[e], rgv[4 + e], rgv[8 + e], rgv[12 + e]);
             }
-            if (pt < C) sBeta[(t % 3) * C + pt] = (pt < L) ? rbeta : 0.f;
+            if (pt < C) sBeta[(t % 3) * C + pt] = (pt < L) ? (p.beta_act ? sigmoid_act(rbeta) : rbeta) : 0.f;
         };
         // gate scan of the staged chunk c (the t-th of this segment) into Gamma * log2(e),
         // plus the per-channel scales and decay ring slot t % 3
@@ -408,6 +408,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 for (int k = 0; k < C / 4; ++k) {
                     const float4 v = gcol[k];
                     rg[4 * k] = v.x; rg[4 * k + 1] = v.y; rg[4 * k + 2] = v.z; rg[4 * k + 3] = v.w;
+                }
+                // logits in: the decays lb * sigmoid(x), before the sum
+                if (p.gate_act && !p.g_is_gamma) {
+#pragma unroll
+                    for (int i = 0; i < C; ++i) rg[i] = gate_act(rg[i], p.gate_lb);
                 }
                 // tail rows re-read token L-1 (clamped loads), so a precomputed Gamma needs
                 // no select there; the cumsum skips them so they hold Gamma_{L-1}

@@ -35,6 +35,19 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// lb * sigmoid(x) and sigmoid(x) = 1 / (1 + e^-x): the fused gate and beta activations.  The
+// multiply is kept out of FMA contraction so that a sum of these values has the same bits in
+// every kernel that forms it (the standalone PREP and the chunk kernels' in-chunk scans).
+__device__ __forceinline__ float sigmoid_act(float x)
+{
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * LOG2E));
+}
+__device__ __forceinline__ float gate_act(float x, float lb)
+{
+#pragma clang fp contract(off)
+    return lb * sigmoid_act(x);
+}
+
 // ---------------------------------------------------------------- element IO
 template <typename ET> struct Elem;
 template <> struct Elem<bf16> {
@@ -197,6 +210,9 @@ struct ChunkParams {
     int32_t g_is_gamma;
     int32_t stall_wave;        // wave index to stall, or -1
     int32_t stall_iters;       // s_sleep(127) repetitions per stall
+    int32_t gate_act;          // g holds logits: log decay = gate_lb * sigmoid(g)
+    float gate_lb;
+    int32_t beta_act;          // beta holds logits: beta = sigmoid(beta)
 };
 
 struct PrepParams {
@@ -207,6 +223,8 @@ struct PrepParams {
     int32_t N, H, T, D;
     int32_t chunk;             // tokens per chunk (32 or 64)
     int32_t chunks_per_seq;    // dense layout: ceil(T / chunk); packed: unused
+    int32_t gate_act;          // g holds logits: log decay = gate_lb * sigmoid(g)
+    float gate_lb;
 };
 
 struct CombineParams {

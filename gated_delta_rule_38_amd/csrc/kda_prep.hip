@@ -8,7 +8,8 @@
 // ceil(T_tot / chunk) + N and the surplus workgroups exit at once.  One thread per
 // key channel adds the chunk's g values in token order in fp32, the same
 // sequential order the chunk kernel's fused scan uses, so both produce the same
-// bits.
+// bits.  With gate_act each g is first taken as a logit x and replaced by
+// gate_lb * sigmoid(x) (the same device function the fused scans use).
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -58,7 +59,8 @@ __global__ __launch_bounds__(128) void prep_kernel(const PrepParams p)
     float *dst = p.gamma + bsel * p.y_sb + h * p.y_sh + (t0 + tok0) * p.y_st + tid;
     float acc = 0.f;
     for (int i = 0; i < L; ++i) {
-        acc = acc + src[(int64_t)i * p.g_st];
+        const float x = src[(int64_t)i * p.g_st];
+        acc = acc + (p.gate_act ? gate_act(x, p.gate_lb) : x);
         dst[(int64_t)i * p.y_st] = acc;
     }
 }

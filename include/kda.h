@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -90,6 +90,16 @@ typedef struct {
     int32_t stall_cycles;  /* length of each injected stall, in s_sleep units of 64 cycles           */
     int32_t variant;       /* 0 = planner; 1 = single-role 64-token chunk kernel; 2 = pipelined      */
                            /* 32-token chunk kernel (head size 128, bf16 only)                       */
+    /* Activations fused into the gate scan (the production gate lower bound of the
+     * cudnn-frontend PR's correctness section, and the "beta_sigmoid" path of the
+     * TensorRT-LLM KDA prefill fix PR #19826):
+     *   gate_act = 1: g holds logits x and the log decay is gate_lower_bound * sigmoid(x),
+     *                 gate_lower_bound in [-5, 0] (the range the kernels are guaranteed on);
+     *   beta_act = 1: beta holds logits b and the delta strength is sigmoid(b).
+     * 0 (the default) takes g and beta as the values of the recurrence. */
+    int32_t gate_act;
+    float gate_lower_bound;
+    int32_t beta_act;
 } kda_options_t;
 
 /*

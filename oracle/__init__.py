@@ -10,7 +10,10 @@ Contents
   * ``run_c``           -- the same recurrence in C (``kda_oracle.c``), OpenMP
                            over (sequence, head) chains, for the large workloads;
   * ``chunked.chunked`` -- a brute-force float64 chunked (WY/UT) form used only
-                           to pin the oracle and the chunk algebra (pin P7).
+                           to pin the oracle and the chunk algebra (pin P7);
+  * ``activations``     -- float64 gate and beta activations for inputs given
+                           as logits (g = lower_bound * sigmoid(x), beta =
+                           sigmoid(b)), applied before the recurrence.
 
 The method (the reading of the pages, which name Kimi Delta Attention and its
 "WY-form chunk" but never print the recurrence): per sequence n and head h,
@@ -130,6 +133,25 @@ def run_c(q, k, v, g, beta, initial_state=None, cu_seqlens=None, threads: int = 
     if return_threads:
         return o, sT, used.value
     return o, sT
+
+
+def activations(g_logits=None, beta_logits=None, lower_bound: float = -5.0):
+    """Float64 activations for gate and beta inputs given as logits.
+
+    The pages name a production gate lower bound of -5 (cudnn-frontend PR #1056,
+    correctness section: the fp64 oracle is run "at the production gate") and a
+    "beta_sigmoid" prefill test (TensorRT-LLM PR #19826, description) but print
+    no formula; the reading taken here is the plainest one consistent with a
+    lower bound: the per-token, per-channel log decay is lower_bound * sigmoid(x),
+    so it lies in [lower_bound, 0], and beta = sigmoid(b) lies in (0, 1).
+    Returns (g, beta) as float64 arrays (None where the input is None).
+    """
+    def sigmoid(x):
+        x = _f64(x)
+        return 1.0 / (1.0 + np.exp(-x))
+    g = None if g_logits is None else float(lower_bound) * sigmoid(g_logits)
+    beta = None if beta_logits is None else sigmoid(beta_logits)
+    return g, beta
 
 
 def rel_l2(x, ref) -> float:

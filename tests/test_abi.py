@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(5) == b"KDA_ERR_ALIAS"
     assert lib.kda_status_string(8) == b"KDA_ERR_HIP"
@@ -218,3 +218,27 @@ def test_python_binding_refuses_without_gpu():
     x = torch.zeros(4, 1, 64)
     with pytest.raises(RuntimeError):
         kda.prefill(x, x, x, x, torch.zeros(4, 1), cu_seqlens=torch.tensor([0, 4], dtype=torch.int32))
+
+
+def test_activation_options_validated(lib):
+    """gate_act / beta_act must be 0 or 1 and the gate lower bound must lie in
+    [-5, 0] (the range the kernels' gate factorisation is guaranteed on); the
+    check runs on the host before anything is enqueued."""
+    s = packed_set()
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    n = ctypes.c_size_t(0)
+
+    def size(**kw):
+        opts = kda.options(**kw)
+        return lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                              ctypes.byref(opts), ctypes.byref(n))
+    assert size(gate_logits=True, gate_lower_bound=-5.0, beta_logits=True) == 0
+    assert size(gate_logits=True, gate_lower_bound=0.0) == 0
+    for bad in (-5.5, 0.25, float("nan"), float("-inf")):
+        assert size(gate_logits=True, gate_lower_bound=bad) == 6, bad
+        assert b"gate_lower_bound" in lib.kda_last_error()
+    assert size(gate_logits=False, gate_lower_bound=-9.0) == 0     # the bound is unused without logits
+    opts = kda.options()
+    opts.gate_act = 2
+    assert lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                          ctypes.byref(opts), ctypes.byref(n)) == 6

@@ -371,3 +371,71 @@ def test_graph_replay_with_changed_q(kda):
         o_ref, s_ref = run(kda, dict(x, q=newq.clone()), nseg=2)
         torch.cuda.synchronize()
         assert torch_equal(out, o_ref) and torch_equal(fin, s_ref), f"replay {rep}"
+
+
+# ------------------------------------------------ activations fused into the gate scan
+def _oracle_with_activations(x, lower_bound=-5.0):
+    g64, b64 = oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), lower_bound)
+    return oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), g64, b64,
+                        None if x["initial_state"] is None else x["initial_state"].cpu(),
+                        None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu())
+
+
+@pytest.mark.parametrize("nseg", [1, 4])
+@pytest.mark.parametrize("variant", [1, 2])
+def test_logit_inputs_match_oracle(kda, variant, nseg):
+    """g and beta given as logits (g = -5 sigmoid(x), beta = sigmoid(b)), the
+    activations fused into the gate scan, against the float64 oracle applied to
+    the float64 activations of the same logits."""
+    w = workloads.custom([700, 0, 64, 1, 300], H=2, D=128, seed=21)
+    x = gen(w)
+    say("nseg", nseg, "variant", variant, "logits")
+    out, sT = kda.prefill(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], x["initial_state"],
+                          x["cu_seqlens"], nseg=nseg, variant=variant, gate_logits=True, beta_logits=True)
+    o_ref, s_ref = _oracle_with_activations(x)
+    eo = oracle.rel_l2(out.float().cpu().numpy().reshape(o_ref.shape), o_ref)
+    es = oracle.rel_l2(sT.cpu().numpy(), s_ref)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], f"rel-L2 out {eo:.3e} state {es:.3e}"
+
+
+def test_logit_inputs_fp32_d64(kda):
+    w = workloads.custom([130, 7, 0, 64], H=2, D=64, dtype="f32", dense=False, seed=22)
+    x = gen(w)
+    out, sT = kda.prefill(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], x["initial_state"],
+                          x["cu_seqlens"], gate_logits=True, beta_logits=True)
+    o_ref, s_ref = _oracle_with_activations(x)
+    eo = oracle.rel_l2(out.cpu().numpy().reshape(o_ref.shape), o_ref)
+    es = oracle.rel_l2(sT.cpu().numpy(), s_ref)
+    assert eo <= TOL["f32"] and es <= TOL["f32"], f"rel-L2 out {eo:.3e} state {es:.3e}"
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_fused_activations_match_unfused(kda, variant):
+    """Fused activations against the same kernel fed values activated by torch on
+    the device beforehand (the fused-vs-unfused check of the TensorRT-LLM KDA
+    prefill fix PR #19826).  Only the rounding of the two sigmoids differs."""
+    import torch
+    w = workloads.custom([300, 64, 45], H=2, D=128, seed=23)
+    x = gen(w)
+    o1, s1 = kda.prefill(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], x["initial_state"],
+                         x["cu_seqlens"], variant=variant, gate_logits=True, beta_logits=True)
+    g = -5.0 * torch.sigmoid(x["g_logits"])
+    b = torch.sigmoid(x["beta_logits"])
+    o2, s2 = kda.prefill(x["q"], x["k"], x["v"], g, b, x["initial_state"], x["cu_seqlens"], variant=variant)
+    do = ((o1.float() - o2.float()).norm() / o2.float().norm()).item()
+    ds = ((s1 - s2).norm() / s2.norm()).item()
+    assert do <= 1e-3 and ds <= 1e-3, f"fused vs unfused: out {do:.2e} state {ds:.2e}"
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_standalone_prep_with_gate_logits_equals_fused(kda, variant):
+    """The standalone PREP kernel applies the same gate activation as the fused
+    scans: the two plans give the same bits."""
+    w = workloads.custom([400, 33], H=2, D=128, seed=24)
+    x = gen(w)
+    kw = dict(variant=variant, gate_logits=True, gate_lower_bound=-3.0, beta_logits=True)
+    o1, s1 = kda.prefill(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], x["initial_state"],
+                         x["cu_seqlens"], prep=1, **kw)
+    o2, s2 = kda.prefill(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], x["initial_state"],
+                         x["cu_seqlens"], prep=2, **kw)
+    assert torch_equal(o1, o2) and torch_equal(s1, s2)

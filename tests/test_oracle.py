@@ -300,3 +300,67 @@ def test_tiny_workload_runs(oracle_lib):
     assert abs(float(np.linalg.norm(o)) - ref["o_norm"]) <= 1e-9 * ref["o_norm"]
     assert abs(float(np.linalg.norm(sT)) - ref["state_norm"]) <= 1e-9 * ref["state_norm"]
     np.testing.assert_allclose(o[::37, :, ::13].ravel(), ref["o_samples"], rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------- activations (NEXT-1)
+def _activation_closed_forms(act):
+    x = np.array([0.0, np.log(3.0), -np.log(3.0), 800.0, -800.0])
+    g, b = act(x, x, lower_bound=-5.0)
+    np.testing.assert_allclose(g, [-2.5, -3.75, -1.25, -5.0, 0.0], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(b, [0.5, 0.75, 0.25, 1.0, 0.0], rtol=1e-15, atol=0)
+
+
+def test_activations_closed_forms():
+    """g = lb * sigmoid(x), beta = sigmoid(b) at points with exact values:
+    sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4; the limits
+    lb (x -> +inf) and 0 (x -> -inf); and sigmoid(x) + sigmoid(-x) = 1."""
+    _activation_closed_forms(oracle.activations)
+    rng = np.random.default_rng(3)
+    y = rng.normal(size=1000) * 4
+    _, b1 = oracle.activations(None, y)
+    _, b2 = oracle.activations(None, -y)
+    np.testing.assert_allclose(b1 + b2, 1.0, rtol=0, atol=1e-15)
+    gz, _ = oracle.activations(y, None, lower_bound=0.0)
+    assert np.all(gz == 0.0)
+
+
+def test_activations_match_library_logistic():
+    """The activation is the logistic function of scipy.special.expit (a library
+    routine), scaled by the lower bound."""
+    from scipy.special import expit
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(64, 3, 16)) * 3
+    g, b = oracle.activations(x, x[..., 0], lower_bound=-3.5)
+    np.testing.assert_allclose(g, -3.5 * expit(x), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(b, expit(x[..., 0]), rtol=1e-14, atol=1e-300)
+
+
+def test_activations_with_zero_beta_reduce_to_pure_decay(oracle_lib):
+    """beta logits at -inf give beta = 0: the recurrence is pure decay (pin P1),
+    S_T = Diag(e^{sum g}) S0 with g = lb * sigmoid(x)."""
+    rng = np.random.default_rng(5)
+    T, H, D = 7, 1, 3
+    q, k, v = (rng.normal(size=(T, H, D)) for _ in range(3))
+    x = rng.normal(size=(T, H, D))
+    g, beta = oracle.activations(x, np.full((T, H), -1e4), lower_bound=-2.0)
+    s0 = rng.normal(size=(1, H, D, D))
+    _, sT = oracle.recurrence(q, k, v, g, beta, s0, np.array([0, T]))
+    want = np.exp(g.sum(axis=0))[0][:, None] * s0[0, 0]
+    np.testing.assert_allclose(sT[0, 0], want, rtol=1e-13)
+
+
+@pytest.mark.parametrize("kind", ["sign", "no_bound", "exp_not_logistic"])
+def test_activation_pins_catch_planted_mistake(kind):
+    """A plausible slip in the activation (a sign, the bound dropped, e^x in
+    place of the logistic) fails the closed-form pin."""
+    def bad(gx, bx, lower_bound=-5.0):
+        def f(x):
+            x = np.asarray(x, dtype=np.float64)
+            if kind == "sign":
+                return 1.0 / (1.0 + np.exp(x))
+            if kind == "exp_not_logistic":
+                return np.exp(np.minimum(x, 0.0))
+            return 1.0 / (1.0 + np.exp(-x))
+        return (f(gx) * (1.0 if kind == "no_bound" else lower_bound)), f(bx)
+    with pytest.raises(AssertionError):
+        _activation_closed_forms(bad)

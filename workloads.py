@@ -89,6 +89,11 @@ def make_inputs(w: Workload, device="cpu", gate: Optional[str] = None) -> dict:
     ``gate`` overrides the gate distribution for edge cases: "floor" sets every g
     to -5, "zero" sets every g to 0, "mild" scales the drawn g by 0.01 (slow decay,
     so a state carries across many chunks).
+
+    ``g_logits`` and ``beta_logits`` hold the normal draws the gates and betas are
+    the activations of (g = -5 sigmoid(g_logits), beta = sigmoid(beta_logits)); a
+    gate pinned at -5 has the logit 30 and a zero gate -1e4, whose fp32 activations
+    are exactly -5 and 0.  Under "mild" there is no such logit and g_logits is None.
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -106,18 +111,26 @@ def make_inputs(w: Workload, device="cpu", gate: Optional[str] = None) -> dict:
     q = unit_rows(randn(T_tot, H, D)).to(dt)
     k = unit_rows(randn(T_tot, H, D)).to(dt)
     v = randn(T_tot, H, D).to(dt)
-    g = GATE_LOWER_BOUND * torch.sigmoid(randn(T_tot, H, D))
-    beta = torch.sigmoid(randn(T_tot, H))
+    g_logits = randn(T_tot, H, D)
+    g = GATE_LOWER_BOUND * torch.sigmoid(g_logits)
+    beta_logits = randn(T_tot, H)
+    beta = torch.sigmoid(beta_logits)
+    # logits whose fp32 activation lands on the bound or on zero exactly
+    LOGIT_AT_BOUND, LOGIT_AT_ZERO = 30.0, -1.0e4
     if w.floor_channels:
         for h in range(H):
             ch = torch.randperm(D, generator=gen, device=dev)[: w.floor_channels]
             g[:, h, ch] = GATE_LOWER_BOUND
+            g_logits[:, h, ch] = LOGIT_AT_BOUND
     if gate == "floor":
         g.fill_(GATE_LOWER_BOUND)
+        g_logits.fill_(LOGIT_AT_BOUND)
     elif gate == "zero":
         g.zero_()
+        g_logits.fill_(LOGIT_AT_ZERO)
     elif gate == "mild":
         g.mul_(0.01)
+        g_logits = None
     s0 = None if w.zero_state else 0.1 * randn(N, H, D, D)
 
     out = {"lengths": list(w.lengths), "initial_state": s0}
@@ -125,11 +138,13 @@ def make_inputs(w: Workload, device="cpu", gate: Optional[str] = None) -> dict:
         L = w.lengths[0]
         assert all(x == L for x in w.lengths), "dense layout needs equal lengths"
         out.update(q=q.view(N, L, H, D), k=k.view(N, L, H, D), v=v.view(N, L, H, D),
-                   g=g.view(N, L, H, D), beta=beta.view(N, L, H), cu_seqlens=None)
+                   g=g.view(N, L, H, D), beta=beta.view(N, L, H), cu_seqlens=None,
+                   g_logits=None if g_logits is None else g_logits.view(N, L, H, D),
+                   beta_logits=beta_logits.view(N, L, H))
     else:
         cu = torch.zeros(N + 1, dtype=torch.int32)
         cu[1:] = torch.cumsum(torch.tensor(w.lengths, dtype=torch.int64), 0).to(torch.int32)
-        out.update(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu.to(dev))
+        out.update(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu.to(dev), g_logits=g_logits, beta_logits=beta_logits)
     return out
 
 
