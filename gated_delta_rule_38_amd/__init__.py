@@ -8,7 +8,8 @@ library's HIP kernels; there is no fallback.  Importing works without a GPU
 raises if the library or a GPU is missing.
 
 Names follow the C ABI: ``prefill`` (kda_prefill / kda_prefill_ws),
-``workspace_size``, ``prep`` (kda_prep), ``profile_enable``/``profile_read``.
+``workspace_size``, ``prep`` (kda_prep), ``decode`` (kda_decode),
+``profile_enable``/``profile_read``.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 KDA_BF16, KDA_F32, KDA_I32 = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_LAYOUT",
           5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP"}
-EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prep",
+EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prep", "kda_decode",
            "kda_release_cached_workspace", "kda_profile_enable", "kda_profile_read",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 
@@ -64,6 +65,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_prefill_ws.restype = ctypes.c_int
     lib.kda_prefill_workspace_size.argtypes = [T, T, T, T, T, T, T, T, T, O, ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_prefill_workspace_size.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int32, O, V]
+    lib.kda_decode.restype = ctypes.c_int
     lib.kda_prep.argtypes = [T, T, ctypes.c_int32, T, V]
     lib.kda_prep.restype = ctypes.c_int
     lib.kda_release_cached_workspace.argtypes = []
@@ -198,6 +201,34 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     _check(lib.kda_prefill_ws(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.c_void_p(wptr),
                               ctypes.c_size_t(wbytes), ctypes.c_void_p(st)))
     return out, final_state
+
+
+def decode(q, k, v, g, beta, state_pool, state_indices, num_tokens=None, out=None, update_state: bool = True,
+           write_out: bool = True, gate_logits: bool = False, gate_lower_bound: float = -5.0,
+           beta_logits: bool = False, stream=None):
+    """Recurrent decode / draft verify against a state pool (kda_decode).
+
+    q, k, g [R, T, H, K]; v [R, T, H, V]; beta [R, T, H]; 1 <= T <= 8.
+    state_pool [P, H, K, V] fp32 or bf16; state_indices int32 [R] (negative:
+    skip the request); num_tokens int32 [R] or None (all T tokens).
+    update_state=False is the verify pass (the pool is only read);
+    write_out=False with update_state=True is the replay-only commit.
+    Returns out (allocated when not given and write_out), or None.
+    """
+    import torch
+    lib = load_library()
+    _require_gpu(q, k, v, g, beta, state_pool, state_indices, num_tokens, out)
+    if out is None and write_out:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    opts = options(gate_logits=gate_logits, gate_lower_bound=gate_lower_bound, beta_logits=beta_logits)
+    do = describe(out) if out is not None else None
+    dn = describe(num_tokens) if num_tokens is not None else None
+    _check(lib.kda_decode(ctypes.byref(describe(q)), ctypes.byref(describe(k)), ctypes.byref(describe(v)),
+                          ctypes.byref(describe(g)), ctypes.byref(describe(beta)), ctypes.byref(describe(state_pool)),
+                          ctypes.byref(describe(state_indices)), _ptr(dn), _ptr(do), ctypes.c_int32(int(update_state)),
+                          ctypes.byref(opts), ctypes.c_void_p(st)))
+    return out
 
 
 def prep(g, cu_seqlens=None, gamma=None, chunk: int = 64, stream=None):

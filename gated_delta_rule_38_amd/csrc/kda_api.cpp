@@ -509,6 +509,90 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
     return run(P, pl, nullptr, ws, pl.bytes, (hipStream_t)stream);
 }
 
+kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v, const kda_tensor_t *g,
+                        const kda_tensor_t *beta, kda_tensor_t *state_pool, const kda_tensor_t *state_indices,
+                        const kda_tensor_t *num_tokens, kda_tensor_t *out, int32_t update_state,
+                        const kda_options_t *opts, void *stream)
+{
+    kda_status_t st;
+    if ((st = check_basic(q, "q", false)) || (st = check_basic(k, "k", false)) || (st = check_basic(v, "v", false)) ||
+        (st = check_basic(g, "g", false)) || (st = check_basic(beta, "beta", false)) ||
+        (st = check_basic(state_pool, "state_pool", false)) || (st = check_basic(state_indices, "state_indices", false)) ||
+        (st = check_basic(num_tokens, "num_tokens", true)) || (st = check_basic(out, "out", true)))
+        return st;
+    if (q->dtype != KDA_BF16 && q->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "q must be bf16 or fp32");
+    if (k->dtype != q->dtype || v->dtype != q->dtype || (out && out->dtype != q->dtype))
+        return fail(KDA_ERR_DTYPE, "q, k, v and out must share one dtype");
+    if (g->dtype != KDA_F32 || beta->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "g and beta must be fp32");
+    if (state_pool->dtype != KDA_F32 && state_pool->dtype != KDA_BF16)
+        return fail(KDA_ERR_DTYPE, "state_pool must be fp32 or bf16");
+    if (state_indices->dtype != KDA_I32 || (num_tokens && num_tokens->dtype != KDA_I32))
+        return fail(KDA_ERR_DTYPE, "state_indices and num_tokens must be int32");
+    if (q->ndim != 4) return fail(KDA_ERR_SHAPE, "q must be [R, T, H, K]");
+    const int64_t R = q->shape[0], T = q->shape[1], H = q->shape[2], D = q->shape[3];
+    if (D != 64 && D != 128) return fail(KDA_ERR_UNSUPPORTED, "head size %lld not in {64, 128}", (long long)D);
+    if (T < 1 || T > kda::DECODE_MAX_TOKENS)
+        return fail(KDA_ERR_UNSUPPORTED, "%lld tokens per request: decode takes 1..%d", (long long)T, kda::DECODE_MAX_TOKENS);
+    if (H < 1) return fail(KDA_ERR_SHAPE, "H must be >= 1");
+    auto same4 = [&](const kda_tensor_t *t, const char *name) -> kda_status_t {
+        if (t->ndim != 4 || t->shape[0] != R || t->shape[1] != T || t->shape[2] != H || t->shape[3] != D)
+            return fail(KDA_ERR_SHAPE, "%s must be [%lld, %lld, %lld, %lld]", name, (long long)R, (long long)T,
+                        (long long)H, (long long)D);
+        return KDA_OK;
+    };
+    if ((st = same4(k, "k")) || (st = same4(v, "v")) || (st = same4(g, "g")) || (out && (st = same4(out, "out"))))
+        return st;
+    if (beta->ndim != 3 || beta->shape[0] != R || beta->shape[1] != T || beta->shape[2] != H)
+        return fail(KDA_ERR_SHAPE, "beta must be [R, T, H]");
+    if (state_pool->ndim != 4 || state_pool->shape[1] != H || state_pool->shape[2] != D || state_pool->shape[3] != D)
+        return fail(KDA_ERR_SHAPE, "state_pool must be [P, %lld, %lld, %lld]", (long long)H, (long long)D, (long long)D);
+    const int64_t P = state_pool->shape[0];
+    if (state_indices->ndim != 1 || state_indices->shape[0] != R) return fail(KDA_ERR_SHAPE, "state_indices must be [R]");
+    if (num_tokens && (num_tokens->ndim != 1 || num_tokens->shape[0] != R))
+        return fail(KDA_ERR_SHAPE, "num_tokens must be [R]");
+    if (R * H * (D / 32) >= (int64_t)1 << 31 || P >= (int64_t)1 << 31)
+        return fail(KDA_ERR_SHAPE, "too many requests or pool slots");
+    const Span sp = span_of(state_pool), so = span_of(out);
+    const kda_tensor_t *ins[] = {q, k, v, g, beta, state_indices, num_tokens};
+    const char *names[] = {"q", "k", "v", "g", "beta", "state_indices", "num_tokens"};
+    for (int i = 0; i < 7; ++i) {
+        if (!ins[i]) continue;
+        if (overlaps(sp, span_of(ins[i]))) return fail(KDA_ERR_ALIAS, "state_pool overlaps %s", names[i]);
+        if (overlaps(so, span_of(ins[i]))) return fail(KDA_ERR_ALIAS, "out overlaps %s", names[i]);
+    }
+    if (overlaps(so, sp)) return fail(KDA_ERR_ALIAS, "out overlaps state_pool");
+    if (opts && (opts->gate_act < 0 || opts->gate_act > 1 || opts->beta_act < 0 || opts->beta_act > 1))
+        return fail(KDA_ERR_UNSUPPORTED, "gate_act %d / beta_act %d (0 or 1)", opts->gate_act, opts->beta_act);
+    if (opts && opts->gate_act && !(opts->gate_lower_bound >= -5.f && opts->gate_lower_bound <= 0.f))
+        return fail(KDA_ERR_UNSUPPORTED, "gate_lower_bound %g outside [-5, 0]", (double)opts->gate_lower_bound);
+    if (R == 0 || (!out && !update_state)) return KDA_OK;
+
+    kda::DecodeParams dp{};
+    dp.q = q->data; dp.k = k->data; dp.v = v->data;
+    dp.g = (const float *)g->data; dp.beta = (const float *)beta->data;
+    dp.pool = state_pool->data;
+    dp.idx = (const int32_t *)state_indices->data;
+    dp.ntok = num_tokens ? (const int32_t *)num_tokens->data : nullptr;
+    dp.o = out ? out->data : nullptr;
+    dp.q_sr = q->stride[0]; dp.q_st = q->stride[1]; dp.q_sh = q->stride[2];
+    dp.k_sr = k->stride[0]; dp.k_st = k->stride[1]; dp.k_sh = k->stride[2];
+    dp.v_sr = v->stride[0]; dp.v_st = v->stride[1]; dp.v_sh = v->stride[2];
+    dp.g_sr = g->stride[0]; dp.g_st = g->stride[1]; dp.g_sh = g->stride[2];
+    dp.b_sr = beta->stride[0]; dp.b_st = beta->stride[1]; dp.b_sh = beta->stride[2];
+    if (out) { dp.o_sr = out->stride[0]; dp.o_st = out->stride[1]; dp.o_sh = out->stride[2]; }
+    dp.p_sn = state_pool->stride[0]; dp.p_sh = state_pool->stride[1]; dp.p_sr = state_pool->stride[2];
+    dp.R = (int32_t)R; dp.T = (int32_t)T; dp.H = (int32_t)H; dp.P = (int32_t)P;
+    dp.update = update_state ? 1 : 0;
+    dp.gate_act = (opts && opts->gate_act) ? 1 : 0;
+    dp.gate_lb = opts ? opts->gate_lower_bound : 0.f;
+    dp.beta_act = (opts && opts->beta_act) ? 1 : 0;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = timed("kda_decode", s, [&] {
+        return kda::launch_decode(dp, (int)D, q->dtype == KDA_F32, state_pool->dtype == KDA_BF16, s);
+    });
+    return e == hipSuccess ? KDA_OK : hip_fail(e, "DECODE launch");
+}
+
 kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int32_t chunk, kda_tensor_t *gamma,
                       void *stream)
 {

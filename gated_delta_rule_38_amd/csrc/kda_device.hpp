@@ -227,6 +227,25 @@ struct PrepParams {
     float gate_lb;
 };
 
+constexpr int DECODE_MAX_TOKENS = 8;
+
+struct DecodeParams {
+    const void *q, *k, *v;     // [R][T][H][D], bf16 or fp32
+    const float *g, *beta;     // [R][T][H][D], [R][T][H]
+    void *pool;                // [P][H][D][D], fp32 or bf16
+    const int32_t *idx;        // [R] pool slot per request (outside [0, P): skipped)
+    const int32_t *ntok;       // [R] tokens per request (clamped to [0, T]), or NULL for T
+    void *o;                   // [R][T][H][D] or NULL
+    int64_t q_sr, q_st, q_sh, k_sr, k_st, k_sh, v_sr, v_st, v_sh, g_sr, g_st, g_sh;
+    int64_t b_sr, b_st, b_sh, o_sr, o_st, o_sh;
+    int64_t p_sn, p_sh, p_sr;  // pool: slot, head, row
+    int32_t R, T, H, P;
+    int32_t update;
+    int32_t gate_act;
+    float gate_lb;
+    int32_t beta_act;
+};
+
 struct CombineParams {
     const float *maps;         // [chain][seg][2][D][D]
     float *start;              // [chain][seg][D][D]

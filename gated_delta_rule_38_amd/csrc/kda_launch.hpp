@@ -10,6 +10,8 @@ hipError_t launch_chunk(const ChunkParams &p, int D, bool fp32, int grid, bool s
 hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStream_t st);
 // PREP kernel over `nvc` virtual chunks x H heads.
 hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st);
-// COMBINE kernel over chains x D/32 value slabs.
+// COMBINE kernel over chains x D/16 value slabs.
 hipError_t launch_combine(const CombineParams &p, int D, int chains, hipStream_t st);
+// DECODE kernel over requests x heads x D/32 value slabs.
+hipError_t launch_decode(const DecodeParams &p, int D, bool io_f32, bool state_bf16, hipStream_t st);
 }  // namespace kda

@@ -149,6 +149,39 @@ kda_status_t kda_prefill_ws(const kda_tensor_t *q, const kda_tensor_t *k, const 
 kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int32_t chunk,
                       kda_tensor_t *gamma, void *stream);
 
+/*
+ * kda_decode -- the recurrence token by token against a pool of states: decode
+ * and multi-token (MTP) draft verification, and the replay-only commit of
+ * accepted drafts (the KDA decode / verify path, state pools and replay of
+ * TensorRT-LLM PR #19960).  For every request r and head h, with the slot
+ * S = state_pool[state_indices[r], h] and n_r = num_tokens ? num_tokens[r] : T
+ * (clamped to [0, T]), the same recurrence as kda_prefill runs over tokens
+ * t = 0 .. n_r - 1 of the request:
+ *     out[r, t, h] = S_t^T q_t              (when out != NULL; rows t >= n_r untouched)
+ *     state_pool[state_indices[r], h] = S   (after the last token, when update_state != 0;
+ *                                            otherwise the pool is only read: the verify pass)
+ * q, k, g: [R, T, H, K]; v, out: [R, T, H, V]; beta: [R, T, H]; 1 <= T <= 8;
+ * K == V in {64, 128}.  q, k, v, out: all bf16 or all fp32; g, beta: fp32.
+ * state_pool: [P, H, K, V], fp32 or bf16 (a bf16 pool is widened to fp32 for
+ * the arithmetic and rounded to nearest even when written back).
+ * state_indices: int32 [R], device memory: a value outside [0, P) skips the
+ * request (no output rows, no state write).  num_tokens: int32 [R], device
+ * memory, or NULL.  Both are read on the device only.
+ * opts: NULL, or a kda_options_t whose gate_act / gate_lower_bound / beta_act
+ * take g and beta as logits exactly as in kda_prefill_ws (its other fields are
+ * ignored here).
+ * Strides in elements with unit last stride, as for kda_prefill.  out may not
+ * overlap any input or the pool; the pool may not overlap any input.  Two
+ * requests that name the same slot with update_state set race (the result is
+ * one of the two); with update_state == 0 any indices may repeat.
+ * Enqueues one kernel on `stream`; allocates nothing; never synchronises.
+ */
+kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                        const kda_tensor_t *g, const kda_tensor_t *beta, kda_tensor_t *state_pool,
+                        const kda_tensor_t *state_indices, const kda_tensor_t *num_tokens,
+                        kda_tensor_t *out, int32_t update_state, const kda_options_t *opts,
+                        void *stream);
+
 /* Frees the workspace cached by kda_prefill on every device. */
 void kda_release_cached_workspace(void);
 

@@ -242,3 +242,50 @@ def test_activation_options_validated(lib):
     opts.gate_act = 2
     assert lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
                                           ctypes.byref(opts), ctypes.byref(n)) == 6
+
+
+def decode_set(R=4, T=3, H=2, D=128, P=6, dt=KDA_BF16, pool_dt=KDA_F32):
+    gap = 1 << 32
+    return dict(q=desc([R, T, H, D], dt, FAKE), k=desc([R, T, H, D], dt, FAKE + gap),
+                v=desc([R, T, H, D], dt, FAKE + 2 * gap), g=desc([R, T, H, D], KDA_F32, FAKE + 3 * gap),
+                beta=desc([R, T, H], KDA_F32, FAKE + 4 * gap), pool=desc([P, H, D, D], pool_dt, FAKE + 5 * gap),
+                idx=desc([R], KDA_I32, FAKE + 6 * gap), ntok=desc([R], KDA_I32, FAKE + 7 * gap),
+                out=desc([R, T, H, D], dt, FAKE + 8 * gap))
+
+
+def call_decode(lib, s, update=1):
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    return lib.kda_decode(r(s["q"]), r(s["k"]), r(s["v"]), r(s["g"]), r(s["beta"]), r(s["pool"]), r(s["idx"]),
+                          r(s["ntok"]), r(s["out"]), update, None, None)
+
+
+def test_decode_validation(lib):
+    """kda_decode's host checks; none of these calls reaches a launch."""
+    s = decode_set(T=9)
+    for x in ("q", "k", "v", "g", "out"):
+        s[x] = desc([4, 9, 2, 128], s[x].dtype, s[x].data)
+    s["beta"] = desc([4, 9, 2], KDA_F32, s["beta"].data)
+    assert call_decode(lib, s) == 6 and b"1..8" in lib.kda_last_error()
+    s = decode_set(pool_dt=KDA_I32)
+    assert call_decode(lib, s) == 3
+    s = decode_set()
+    s["idx"] = desc([4], KDA_F32, s["idx"].data)
+    assert call_decode(lib, s) == 3
+    s = decode_set()
+    s["pool"] = desc([6, 2, 128, 64], KDA_F32, s["pool"].data)
+    assert call_decode(lib, s) == 2
+    s = decode_set()
+    s["ntok"] = desc([3], KDA_I32, s["ntok"].data)
+    assert call_decode(lib, s) == 2
+    s = decode_set()
+    s["out"] = desc([4, 3, 2, 128], KDA_BF16, s["pool"].data)
+    assert call_decode(lib, s) == 5
+    s = decode_set()
+    s["pool"] = desc([6, 2, 128, 128], KDA_F32, s["q"].data)
+    assert call_decode(lib, s) == 5
+    s = decode_set(D=96)
+    assert call_decode(lib, s) == 6
+    s = decode_set()
+    s["state_dummy"] = None
+    s["idx"] = None
+    assert call_decode(lib, s) == 1

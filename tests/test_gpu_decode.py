@@ -1,0 +1,190 @@
+"""GPU parity of the recurrent decode / draft-verify kernel (kda_decode, called
+through the C ABI) against the float64 oracle.
+
+The oracle is the same token recurrence the prefill tests use: request r starts
+from the pool slot it names (widened to float64 from the stored fp32 or bf16
+values) and runs over its first n_r tokens.  Tolerances (whole-tensor relative
+L2): 1e-4 with fp32 inputs and an fp32 pool; 5e-3 when q/k/v/out or the pool
+are bf16 (a bf16 pool slot is rounded once when written back).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_38_amd as k
+    k.load_library()
+    return k
+
+
+def make_case(R, T, H, D, dtype, pool_dtype, seed, P=None):
+    """Decode inputs in the workload recipe: R requests of T tokens ([R, T, H, D],
+    a dense workload of R equal-length sequences), a pool of P random states
+    (N(0, 0.1^2)), a permutation of slots with one request skipped (index -1) and
+    per-request token counts in [0, T]."""
+    import torch
+    w = workloads.custom([T] * R, H=H, D=D, dtype=dtype, dense=True, seed=seed)
+    x = workloads.make_inputs(w, device="cuda")
+    P = P or R + 3
+    gen = torch.Generator().manual_seed(seed + 1000)
+    pool = (0.1 * torch.randn(P, H, D, D, generator=gen)).to({"f32": torch.float32, "bf16": torch.bfloat16}[pool_dtype])
+    idx = torch.randperm(P, generator=gen)[:R].to(torch.int32)
+    idx[R // 2] = -1
+    ntok = torch.randint(0, T + 1, (R,), generator=gen, dtype=torch.int32)
+    ntok[0] = T
+    return x, pool.cuda(), idx.cuda(), ntok.cuda()
+
+
+def oracle_decode(x, pool, idx, ntok, g=None, beta=None):
+    """Per request: the float64 recurrence from pool[idx[r]] over its first n_r
+    tokens.  Returns ({r: out rows [n_r, H, D]}, {r: final state [H, D, D]})."""
+    import torch
+    idx_h, n_h = idx.cpu().numpy(), ntok.cpu().numpy()
+    g = x["g"].cpu() if g is None else torch.as_tensor(g)
+    beta = x["beta"].cpu() if beta is None else torch.as_tensor(beta)
+    reqs = [r for r in range(len(idx_h)) if idx_h[r] >= 0]
+    cat = lambda t: torch.cat([t[r, : int(n_h[r])].double() for r in reqs])
+    q, k, v = (cat(x[n].cpu()) for n in ("q", "k", "v"))
+    gg, bb = cat(g), cat(beta)
+    s0 = torch.stack([pool[int(idx_h[r])].cpu().double() for r in reqs])
+    cu = np.concatenate([[0], np.cumsum([int(n_h[r]) for r in reqs])]).astype(np.int64)
+    o, s = oracle.run_c(q, k, v, gg, bb, s0, cu)
+    outs = {r: o[cu[i]:cu[i + 1]] for i, r in enumerate(reqs)}
+    states = {r: s[i] for i, r in enumerate(reqs)}
+    return outs, states
+
+
+def check(x, out, pool_before, pool_after, idx, ntok, tol, update=True, **kw):
+    import torch
+    outs, states = oracle_decode(x, pool_before, idx, ntok, **kw)
+    o_gpu = out.float().cpu().numpy()
+    got = np.concatenate([o_gpu[r, : outs[r].shape[0]] for r in outs])
+    want = np.concatenate([outs[r] for r in outs])
+    eo = oracle.rel_l2(got, want) if want.size else 0.0
+    idx_h, n_h = idx.cpu().numpy(), ntok.cpu().numpy()
+    # rows past each request's count, and skipped requests, keep the sentinel
+    for r in range(len(idx_h)):
+        n = int(n_h[r]) if idx_h[r] >= 0 else 0
+        assert torch.all(out[r, n:].float() == -512.0), f"request {r}: rows past {n} written"
+    used = {int(idx_h[r]) for r in outs}
+    for sl in range(pool_before.shape[0]):
+        if sl not in used or not update:
+            assert torch.equal(pool_after[sl].cpu(), pool_before[sl].cpu()), f"slot {sl} changed"
+    es = 0.0
+    if update and states:
+        s_gpu = np.stack([pool_after[int(idx_h[r])].float().cpu().numpy() for r in states])
+        s_ref = np.stack([states[r] for r in states])
+        es = oracle.rel_l2(s_gpu, s_ref)
+    assert eo <= tol and es <= tol, f"rel-L2 out {eo:.3e} state {es:.3e}"
+    return eo, es
+
+
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_decode_matches_oracle(kda, T, D, dtype, pool_dtype):
+    import torch
+    say("decode T", T, "D", D, dtype, "pool", pool_dtype)
+    x, pool, idx, ntok = make_case(R=7, T=T, H=3, D=D, dtype=dtype, pool_dtype=pool_dtype, seed=40 + T + D)
+    before = pool.clone()
+    out = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, idx, ntok, out=out)
+    torch.cuda.synchronize()
+    tol = 1e-4 if dtype == "f32" and pool_dtype == "f32" else 5e-3
+    check(x, out, before, pool, idx, ntok, tol)
+
+
+def test_decode_all_tokens_and_repeat_bitwise(kda):
+    """num_tokens = NULL runs every token; two runs from the same pool give the same bits."""
+    import torch
+    x, pool, idx, _ = make_case(R=5, T=3, H=2, D=128, dtype="bf16", pool_dtype="f32", seed=51)
+    ntok = torch.full((5,), 3, dtype=torch.int32, device="cuda")
+    p1, p2 = pool.clone(), pool.clone()
+    o1 = torch.full_like(x["v"], -512.0)
+    o2 = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], p1, idx, None, out=o1)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], p2, idx, None, out=o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(p1, p2)
+    check(x, o1, pool, p1, idx, ntok, 5e-3)
+
+
+def test_verify_then_replay_commit(kda):
+    """The draft-verify flow: a verify pass over T drafts reads the pool only; a
+    replay-only commit of the accepted count per request then writes the state
+    the oracle reaches after those tokens, and the verify outputs of the accepted
+    tokens are the oracle's."""
+    import torch
+    x, pool, idx, acc = make_case(R=6, T=4, H=2, D=128, dtype="bf16", pool_dtype="bf16", seed=52)
+    before = pool.clone()
+    out = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, idx, None, out=out, update_state=False)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, before), "the verify pass wrote the pool"
+    full = torch.full((6,), 4, dtype=torch.int32, device="cuda")
+    check(x, out, before, pool, idx, full, 5e-3, update=False)
+    r = kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, idx, acc, update_state=True, write_out=False)
+    torch.cuda.synchronize()
+    assert r is None
+    _, states = oracle_decode(x, before, idx, acc)
+    idx_h = idx.cpu().numpy()
+    s_gpu = np.stack([pool[int(idx_h[r])].float().cpu().numpy() for r in states])
+    s_ref = np.stack([states[r] for r in states])
+    assert oracle.rel_l2(s_gpu, s_ref) <= 5e-3
+    # verify outputs equal a committing decode's outputs bit for bit (one kernel, same order)
+    p3 = before.clone()
+    o3 = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], p3, idx, None, out=o3, update_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(torch.int16), out.view(torch.int16))
+
+
+def test_decode_continues_prefill(kda):
+    """Prefill L tokens (chunked kernel) into a pool slot, then decode the next T
+    tokens (recurrent kernel): the decode outputs match a prefill of all L + T
+    tokens within the tolerance (two different kernels, same recurrence)."""
+    import torch
+    H, D, L, T = 2, 128, 200, 4
+    w = workloads.custom([L + T], H=H, D=D, dtype="bf16", dense=True, seed=53)
+    x = workloads.make_inputs(w, device="cuda")
+    o_all, s_all = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"])
+    cut = lambda t, a, b: t[:, a:b].contiguous()
+    _, s_mid = kda.prefill(cut(x["q"], 0, L), cut(x["k"], 0, L), cut(x["v"], 0, L), cut(x["g"], 0, L),
+                           cut(x["beta"], 0, L), x["initial_state"])
+    pool = torch.zeros(3, H, D, D, device="cuda")
+    pool[2] = s_mid[0]
+    idx = torch.tensor([2], dtype=torch.int32, device="cuda")
+    out = kda.decode(cut(x["q"], L, L + T), cut(x["k"], L, L + T), cut(x["v"], L, L + T), cut(x["g"], L, L + T),
+                     cut(x["beta"], L, L + T), pool, idx)
+    torch.cuda.synchronize()
+    ref = o_all[:, L:].float()
+    assert ((out.float() - ref).norm() / ref.norm()).item() <= 5e-3
+    assert ((pool[2] - s_all[0]).norm() / s_all[0].norm()).item() <= 5e-3
+
+
+def test_decode_logit_inputs(kda):
+    import torch
+    x, pool, idx, ntok = make_case(R=5, T=4, H=2, D=128, dtype="bf16", pool_dtype="f32", seed=54)
+    before = pool.clone()
+    out = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], pool, idx, ntok, out=out,
+               gate_logits=True, beta_logits=True, gate_lower_bound=-5.0)
+    torch.cuda.synchronize()
+    g64, b64 = oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), -5.0)
+    check(x, out, before, pool, idx, ntok, 5e-3, g=g64, beta=b64)
