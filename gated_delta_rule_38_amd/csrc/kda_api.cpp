@@ -561,6 +561,17 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
         if (overlaps(so, span_of(ins[i]))) return fail(KDA_ERR_ALIAS, "out overlaps %s", names[i]);
     }
     if (overlaps(so, sp)) return fail(KDA_ERR_ALIAS, "out overlaps state_pool");
+    // state rows and output rows move as 4-element vectors
+    auto aligned4 = [&](const kda_tensor_t *t) {
+        if (!t || !t->data) return true;
+        const size_t es = elem_size(t->dtype), vec = 4 * es;
+        if ((uintptr_t)t->data % vec) return false;
+        for (int d = 0; d + 1 < t->ndim; ++d)
+            if (t->shape[d] > 1 && (t->stride[d] * es) % vec) return false;
+        return true;
+    };
+    if (!aligned4(state_pool) || !aligned4(out))
+        return fail(KDA_ERR_LAYOUT, "state_pool and out need 4-element-aligned base addresses and strides");
     if (opts && (opts->gate_act < 0 || opts->gate_act > 1 || opts->beta_act < 0 || opts->beta_act > 1))
         return fail(KDA_ERR_UNSUPPORTED, "gate_act %d / beta_act %d (0 or 1)", opts->gate_act, opts->beta_act);
     if (opts && opts->gate_act && !(opts->gate_lower_bound >= -5.f && opts->gate_lower_bound <= 0.f))

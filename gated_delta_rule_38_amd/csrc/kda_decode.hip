@@ -10,14 +10,16 @@
 // to out[r, t] when out is given; the slot is overwritten with the last state
 // when update is set (the pool is only read otherwise: the verify pass).
 //
-// Columns of S evolve independently, so one 256-thread workgroup owns one
-// 32-column value slab of one (request, head): thread (column c, row group j)
-// keeps rows [j D/8, (j+1) D/8) of column c in registers, and the two sums over
-// key channels per token (k^T S and q^T S) are reduced across the 8 row groups
-// in a fixed order (lane pairs, then the 4 waves through LDS), so results do not
-// depend on timing.  The work is the state's round trip through HBM; the few
-// tokens are staged in LDS once.  An index outside [0, P) skips the request (no
-// output rows, no state write), so a bad index can never address memory.
+// Columns of S evolve independently.  One 256-thread workgroup owns one
+// (request, head): lane group c (D/4 lanes) covers four consecutive value
+// columns 4c..4c+3 of the state, the row groups split the key rows, and every
+// thread keeps its rows x 4 columns in registers, so each state row moves
+// through HBM as whole 16-byte (fp32) or 8-byte (bf16) lanes.  The two sums
+// over key channels per token (k^T S and q^T S) are reduced across row groups
+// in a fixed order (lane butterflies inside a wave, then the 4 waves through
+// LDS), so results do not depend on timing.  The few tokens are staged in LDS
+// once.  An index outside [0, P) skips the request (no output rows, no state
+// write), so a bad index can never address memory.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -26,81 +28,111 @@ namespace kda {
 template <typename T> __device__ __forceinline__ float ld(const T *p);
 template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float ld<bf16>(const bf16 *p) { return (float)*p; }
-template <typename T> __device__ __forceinline__ void st(T *p, float x);
-template <> __device__ __forceinline__ void st<float>(float *p, float x) { *p = x; }
-template <> __device__ __forceinline__ void st<bf16>(bf16 *p, float x) { *p = (bf16)x; }   // round to nearest even
+// four consecutive elements: one 16-byte (fp32) or 8-byte (bf16) access
+__device__ __forceinline__ void ld4(const float *p, float (&x)[4])
+{
+    const float4 v = *(const float4 *)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void ld4(const bf16 *p, float (&x)[4]) { Vec4<bf16>::unpack(Vec4<bf16>::load(p), x); }
+__device__ __forceinline__ void st4(float *p, const float (&x)[4]) { *(float4 *)p = make_float4(x[0], x[1], x[2], x[3]); }
+__device__ __forceinline__ void st4(bf16 *p, const float (&x)[4]) { Vec4<bf16>::store(p, Vec4<bf16>::pack(x)); }   // RNE
 
 template <int D, typename IT, typename ST>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
 {
-    constexpr int NSLAB = D / 32, RPG = D / 8, TM = DECODE_MAX_TOKENS;
-    __shared__ float sK[TM][D], sQ[TM][D], sE[TM][D], sV[TM][32], sB[TM];
-    __shared__ float sRed[2][4][32];
-    const int slab = blockIdx.x % NSLAB, rh = blockIdx.x / NSLAB;
-    const int h = rh % p.H, r = rh / p.H;
-    const int tid = threadIdx.x, c = tid & 31, grp = tid >> 5, wave = tid >> 6;
+    constexpr int NCQ = D / 4;            // column quads = lanes per row group
+    constexpr int NRG = 256 / NCQ;        // row groups (8 for D = 128, 16 for D = 64)
+    constexpr int RPG = D / NRG;          // rows per thread
+    constexpr int TM = DECODE_MAX_TOKENS;
+    __shared__ __attribute__((aligned(16))) float sK[TM][D], sQ[TM][D], sE[TM][D], sV[TM][D], sB[TM];
+    __shared__ __attribute__((aligned(16))) float sRed[2][4][D];
+    const int h = blockIdx.x % p.H, r = blockIdx.x / p.H;
+    const int tid = threadIdx.x, lane = tid & 63, cq = tid % NCQ, rg = tid / NCQ, wave = tid >> 6;
     const int slot = p.idx[r];
     if (slot < 0 || slot >= p.P) return;
     const int n = p.ntok ? min(max(p.ntok[r], 0), p.T) : p.T;
-    const int v0 = 32 * slab;
     const IT *q = (const IT *)p.q + r * p.q_sr + h * p.q_sh;
     const IT *k = (const IT *)p.k + r * p.k_sr + h * p.k_sh;
-    const IT *v = (const IT *)p.v + r * p.v_sr + h * p.v_sh + v0;
+    const IT *v = (const IT *)p.v + r * p.v_sr + h * p.v_sh;
     const float *g = p.g + r * p.g_sr + h * p.g_sh;
     for (int e = tid; e < n * D; e += 256) {
         const int t = e / D, ch = e % D;
         sK[t][ch] = ld(k + t * p.k_st + ch);
         sQ[t][ch] = ld(q + t * p.q_st + ch);
+        sV[t][ch] = ld(v + t * p.v_st + ch);
         const float x = g[t * p.g_st + ch];
         sE[t][ch] = fast_exp(p.gate_act ? gate_act(x, p.gate_lb) : x);
     }
-    for (int e = tid; e < n * 32; e += 256) sV[e / 32][e % 32] = ld(v + (e / 32) * p.v_st + e % 32);
     if (tid < n) {
         const float b = p.beta[r * p.b_sr + tid * p.b_st + h * p.b_sh];
         sB[tid] = p.beta_act ? sigmoid_act(b) : b;
     }
-    ST *ps = (ST *)p.pool + slot * p.p_sn + h * p.p_sh + (int64_t)(grp * RPG) * p.p_sr + v0 + c;
-    float s[RPG];
+    ST *ps = (ST *)p.pool + slot * p.p_sn + h * p.p_sh + (int64_t)(rg * RPG) * p.p_sr + 4 * cq;
+    float s[RPG][4];
 #pragma unroll
-    for (int j = 0; j < RPG; ++j) s[j] = ld(ps + j * p.p_sr);
+    for (int j = 0; j < RPG; ++j) ld4(ps + j * p.p_sr, s[j]);
     __syncthreads();
 
-    IT *o = p.o ? (IT *)p.o + r * p.o_sr + h * p.o_sh + v0 + c : nullptr;
+    // sum of x over the row groups, for this lane's 4 columns: butterflies over the row-group
+    // lanes of the wave, then the 4 waves' partials in a fixed order
+    auto reduce = [&](float (&x)[4], float (*red)[D], float (&sum)[4]) {
+#pragma unroll
+        for (int off = NCQ; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] += __shfl_xor(x[e], off);
+        if (lane < NCQ) *(float4 *)&red[wave][4 * cq] = make_float4(x[0], x[1], x[2], x[3]);
+        __syncthreads();
+        const float4 a = *(const float4 *)&red[0][4 * cq], b = *(const float4 *)&red[1][4 * cq];
+        const float4 c = *(const float4 *)&red[2][4 * cq], d = *(const float4 *)&red[3][4 * cq];
+        sum[0] = (a.x + b.x) + (c.x + d.x);
+        sum[1] = (a.y + b.y) + (c.y + d.y);
+        sum[2] = (a.z + b.z) + (c.z + d.z);
+        sum[3] = (a.w + b.w) + (c.w + d.w);
+    };
+    IT *o = p.o ? (IT *)p.o + r * p.o_sr + h * p.o_sh + 4 * cq : nullptr;
     for (int t = 0; t < n; ++t) {
         // decay, then the read k^T D S of this thread's rows
-        float pr = 0.f;
+        float pr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RPG; ++j) {
-            const int i = grp * RPG + j;
-            s[j] *= sE[t][i];
-            pr += sK[t][i] * s[j];
+            const int i = rg * RPG + j;
+            const float e = sE[t][i], kk = sK[t][i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                s[j][c] *= e;
+                pr[c] += kk * s[j][c];
+            }
         }
-        pr += __shfl_xor(pr, 32);            // row groups 2w and 2w + 1 of wave w
-        if ((tid & 63) < 32) sRed[0][wave][c] = pr;
-        __syncthreads();
-        const float kS = (sRed[0][0][c] + sRed[0][1][c]) + (sRed[0][2][c] + sRed[0][3][c]);
-        const float u = sB[t] * (sV[t][c] - kS);
-        float po = 0.f;
+        float kS[4];
+        reduce(pr, sRed[0], kS);
+        const float4 v4 = *(const float4 *)&sV[t][4 * cq];
+        const float b = sB[t];
+        const float u[4] = {b * (v4.x - kS[0]), b * (v4.y - kS[1]), b * (v4.z - kS[2]), b * (v4.w - kS[3])};
+        float po[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RPG; ++j) {
-            const int i = grp * RPG + j;
-            s[j] += sK[t][i] * u;
-            po += sQ[t][i] * s[j];
+            const int i = rg * RPG + j;
+            const float kk = sK[t][i], qq = sQ[t][i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                s[j][c] += kk * u[c];
+                po[c] += qq * s[j][c];
+            }
         }
-        po += __shfl_xor(po, 32);
-        if ((tid & 63) < 32) sRed[1][wave][c] = po;
-        __syncthreads();
-        if (o && tid < 32) st(o + t * p.o_st, (sRed[1][0][c] + sRed[1][1][c]) + (sRed[1][2][c] + sRed[1][3][c]));
+        float os[4];
+        reduce(po, sRed[1], os);
+        if (o && tid < NCQ) st4(o + t * p.o_st, os);
     }
     if (p.update) {
 #pragma unroll
-        for (int j = 0; j < RPG; ++j) st(ps + j * p.p_sr, s[j]);
+        for (int j = 0; j < RPG; ++j) st4(ps + j * p.p_sr, s[j]);
     }
 }
 
 hipError_t launch_decode(const DecodeParams &p, int D, bool io_f32, bool state_bf16, hipStream_t stream)
 {
-    const int64_t blocks = (int64_t)p.R * p.H * (D / 32);
+    const int64_t blocks = (int64_t)p.R * p.H;
     if (blocks <= 0) return hipSuccess;
 #define KDA_DECODE(DD, IT, ST) hipLaunchKernelGGL((decode_kernel<DD, IT, ST>), dim3((unsigned)blocks), dim3(256), 0, stream, p)
     if (D == 128 && !io_f32 && !state_bf16) KDA_DECODE(128, bf16, float);

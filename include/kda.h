@@ -170,8 +170,9 @@ kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int
  * opts: NULL, or a kda_options_t whose gate_act / gate_lower_bound / beta_act
  * take g and beta as logits exactly as in kda_prefill_ws (its other fields are
  * ignored here).
- * Strides in elements with unit last stride, as for kda_prefill.  out may not
- * overlap any input or the pool; the pool may not overlap any input.  Two
+ * Strides in elements with unit last stride, as for kda_prefill; state_pool and
+ * out also need base addresses and strides aligned to 4 elements (their rows
+ * move as 4-element vectors).  out may not overlap any input or the pool; the pool may not overlap any input.  Two
  * requests that name the same slot with update_state set race (the result is
  * one of the two); with update_state == 0 any indices may repeat.
  * Enqueues one kernel on `stream`; allocates nothing; never synchronises.

@@ -289,3 +289,14 @@ def test_decode_validation(lib):
     s["state_dummy"] = None
     s["idx"] = None
     assert call_decode(lib, s) == 1
+
+
+def test_decode_vector_alignment(lib):
+    """state_pool and out rows move as 4-element vectors: a row stride or base that
+    is not a multiple of 4 elements is refused before any launch."""
+    s = decode_set()
+    s["pool"] = desc([6, 2, 128, 128], KDA_F32, s["pool"].data, strides=[2 * 128 * 130, 128 * 130, 130, 1])
+    assert call_decode(lib, s) == 4
+    s = decode_set()
+    s["out"] = desc([4, 3, 2, 128], KDA_BF16, s["out"].data + 2)
+    assert call_decode(lib, s) == 4
