@@ -1,6 +1,7 @@
 """KDA chunked-prefill benchmark on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config varlen|large|eqlen|long|varlen_padded|tiny]
+    python bench.py --config decode|decode_bf16|verify4        (the recurrent decode kernel)
 
 One step is one kda_prefill call over the whole workload (every kernel of the
 hot path), with inputs already resident in HBM.  Prints ONE JSON line:
@@ -133,6 +134,82 @@ def correctness_gate(kda, x, w, out, fin):
     return worst
 
 
+DECODE_METRIC = "KDA decode tokens/sec at H=32,d=128 bf16 against a state pool; HBM GB/s"
+
+
+def decode_algorithmic(w):
+    """Bytes the decode method must move per call: every request's state slot read
+    and written back (pool dtype), q, k, v, out (bf16) and g (fp32), beta (fp32) per
+    token-head, and the slot index; flops: 7 D^2 per token-head."""
+    es = 2 if w.pool_dtype == "bf16" else 4
+    th = w.R * w.T * w.H
+    bytes_ = w.R * w.H * 2 * w.D * w.D * es + th * (4 * w.D * 2 + w.D * 4 + 4) + w.R * 4
+    return bytes_, th * 7 * w.D * w.D
+
+
+def decode_main(a, w):
+    import numpy as np
+    import torch
+    import gated_delta_rule_38_amd as kda
+    import oracle
+    import workloads
+    dev = torch.device("cuda:0")
+    x = workloads.make_decode_inputs(w, device=dev)
+    out = torch.empty_like(x["v"])
+    step = lambda pool: kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, x["idx"], None, out=out)
+    # correctness gate on a copy of the pool: every request against the float64 oracle
+    pool0 = x["pool"].clone()
+    step(pool0)
+    torch.cuda.synchronize()
+    idx = x["idx"].cpu().numpy()
+    cat = lambda t: t.cpu().double().reshape(w.R * w.T, w.H, -1) if t.dim() == 4 else t.cpu().double().reshape(w.R * w.T, w.H)
+    s0 = x["pool"].cpu().double()[idx]
+    cu = np.arange(w.R + 1, dtype=np.int64) * w.T
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
+    t = time.perf_counter()
+    o_ref, s_ref, used = oracle.run_c(cat(x["q"]), cat(x["k"]), cat(x["v"]), cat(x["g"]), cat(x["beta"]), s0, cu,
+                                      threads=threads, return_threads=True)
+    dt = time.perf_counter() - t
+    eo = oracle.rel_l2(out.float().cpu().numpy().reshape(o_ref.shape), o_ref)
+    es = oracle.rel_l2(pool0.float().cpu().numpy()[idx], s_ref)
+    if not max(eo, es) <= 5e-3:
+        raise SystemExit(f"correctness gate failed: rel-L2 out {eo:.3e} state {es:.3e}")
+    pool = x["pool"]
+    for _ in range(a.warmup):
+        step(pool)
+    torch.cuda.synchronize()
+    kda.profile_read()
+    kda.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(pool)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kda.profile_enable(False)
+    k_ms, k_n = kda.profile_read("kda_decode")
+    kern_ms = k_ms / max(1, k_n)
+    bytes_, flops = decode_algorithmic(w)
+    achieved = bytes_ / (kern_ms * 1e-3) / 1e9
+    rec = {
+        "metric": DECODE_METRIC, "value": w.tokens * a.steps / (t1 - t0), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": (t1 - t0) / a.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; see workloads.py)",
+        "config": w.describe(),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernel": {"name": "kda_decode", "avg_ms": kern_ms, "launches_per_step": k_n // max(1, a.steps),
+                   "algorithmic_bytes_per_launch": bytes_, "flops_per_launch": flops,
+                   "kernel_source_sha": source_sha()},
+        "correctness": {"rel_l2_out": eo, "rel_l2_state": es},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = {"value": w.tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+                               "sample": f"all {w.R} requests x {w.H} heads, float64 C recurrence from the pool "
+                                         f"slots, {dt:.2f} s (the correctness gate's run)"}
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +244,8 @@ def main():
         print(json.dumps({"copy_calib_bytes_each_way": n * 4, "copies": 5}))
         return
 
+    if a.config in workloads.DECODE_WORKLOADS:
+        return decode_main(a, workloads.DECODE_WORKLOADS[a.config])
     w = workloads.WORKLOADS[a.config]
     x = workloads.make_inputs(w, device=dev)
     torch.cuda.synchronize()

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for KDA chunked prefill (test and bench infrastructure).
+"""Seeded synthetic inputs for KDA chunked prefill and decode (test and bench infrastructure).
 
 This module only draws random tensors with the shapes and value distributions of
 the KDA prefill workloads; it holds no step of the delta-rule arithmetic, so both
@@ -157,3 +157,47 @@ def cu_from_lengths(lengths) -> np.ndarray:
     cu = np.zeros(len(lengths) + 1, dtype=np.int64)
     cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
     return cu
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """R requests of T tokens each against a pool of P state slots (every request
+    names its own slot), the decode / draft-verify shape of KDA serving."""
+    name: str
+    R: int
+    T: int
+    H: int
+    D: int
+    pool_dtype: str         # "f32" or "bf16"
+    P: int
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.R * self.T
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "requests": self.R, "tokens_per_request": self.T, "H": self.H,
+                "d_k": self.D, "d_v": self.D, "dtype": "bf16", "state_pool": self.pool_dtype,
+                "pool_slots": self.P, "state_update": True, "seed": self.seed}
+
+
+DECODE_WORKLOADS = {
+    "decode": DecodeWorkload("decode", R=256, T=1, H=32, D=128, pool_dtype="f32", P=512),
+    "decode_bf16": DecodeWorkload("decode_bf16", R=256, T=1, H=32, D=128, pool_dtype="bf16", P=512),
+    "verify4": DecodeWorkload("verify4", R=256, T=4, H=32, D=128, pool_dtype="f32", P=512),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, device="cpu") -> dict:
+    """q, k, v, g, beta [R, T, H, D] in the prefill recipe (a dense workload of R
+    equal-length sequences), a pool of P states ~ N(0, 0.1^2) in the pool dtype,
+    and a seeded permutation of slots as int32 state indices."""
+    x = make_inputs(custom([w.T] * w.R, H=w.H, D=w.D, dtype="bf16", dense=True, seed=w.seed), device=device)
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 1)
+    pool = 0.1 * torch.randn(w.P, w.H, w.D, w.D, generator=gen, device=dev, dtype=torch.float32)
+    pool = pool.to(_torch_dtype(w.pool_dtype))
+    idx = torch.randperm(w.P, generator=gen, device=dev)[: w.R].to(torch.int32)
+    return {"q": x["q"], "k": x["k"], "v": x["v"], "g": x["g"], "beta": x["beta"], "pool": pool, "idx": idx}
