@@ -143,7 +143,7 @@ kda_status_t tok_view(const kda_tensor_t *t, const char *name, const Problem &P,
 
 kda_status_t state_view(const kda_tensor_t *t, const char *name, const Problem &P, int64_t &sn, int64_t &sh, int64_t &sr)
 {
-    if (t->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "%s must be fp32", name);
+    if (t->dtype != KDA_F32 && t->dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "%s must be fp32 or bf16", name);
     if (t->ndim != 4) return fail(KDA_ERR_SHAPE, "%s must be [N, H, K, V]", name);
     if (t->shape[0] != P.N || t->shape[1] != P.H || t->shape[2] != P.D || t->shape[3] != P.D)
         return fail(KDA_ERR_SHAPE, "%s: shape must be [%lld, %lld, %lld, %lld]", name, (long long)P.N,
@@ -360,9 +360,11 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     kda::ChunkParams cp{};
     cp.q = P.tq->data; cp.k = P.tk->data; cp.v = P.tv->data;
     cp.g = (const float *)P.tg->data; cp.beta = (const float *)P.tb->data;
-    cp.s0 = P.ts0 ? (const float *)P.ts0->data : nullptr;
+    cp.s0 = (P.ts0 && P.ts0->dtype == KDA_F32) ? (const float *)P.ts0->data : nullptr;
+    cp.s0h = (P.ts0 && P.ts0->dtype == KDA_BF16) ? (const kda::bf16 *)P.ts0->data : nullptr;
     cp.o = P.tout->data;
-    cp.sT = P.tsT ? (float *)P.tsT->data : nullptr;
+    cp.sT = (P.tsT && P.tsT->dtype == KDA_F32) ? (float *)P.tsT->data : nullptr;
+    cp.sTh = (P.tsT && P.tsT->dtype == KDA_BF16) ? (kda::bf16 *)P.tsT->data : nullptr;
     cp.cu = P.tcu ? (const int32_t *)P.tcu->data : nullptr;
     cp.q_sb = P.q.sb; cp.q_st = P.q.st; cp.q_sh = P.q.sh;
     cp.k_sb = P.k.sb; cp.k_st = P.k.st; cp.k_sh = P.k.sh;
@@ -421,7 +423,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
         return hip_fail(e, "segment-build launch");
     kda::CombineParams mp{};
     mp.maps = cp.ws_maps; mp.start = (float *)(wsb + pl.off_start);
-    mp.s0 = cp.s0; mp.s0_sn = P.s0_sn; mp.s0_sh = P.s0_sh; mp.s0_sr = P.s0_sr;
+    mp.s0 = cp.s0; mp.s0h = cp.s0h; mp.s0_sn = P.s0_sn; mp.s0_sh = P.s0_sh; mp.s0_sr = P.s0_sr;
     mp.N = (int32_t)P.N; mp.H = (int32_t)P.H; mp.nseg = pl.nseg;
     if ((e = timed("kda_combine", st, [&] { return kda::launch_combine(mp, D, (int)chains, st); })) != hipSuccess)
         return hip_fail(e, "combine launch");

@@ -173,6 +173,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
         } else if (role == ROLE_SEG_OUT) {
             src = p.ws_start + ((int64_t)chain * p.nseg + seg) * D * D;
         }
+        const bf16 *srch = (role == ROLE_OUT && p.s0h) ? p.s0h + n * p.s0_sn + h * p.s0_sh : nullptr;
         const float one = (role == ROLE_SEG_M) ? 1.f : 0.f;
         if (src) {                  // one straight-line block of loads
 #pragma unroll
@@ -181,6 +182,13 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) S[m][4 * q + r] = src[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol];
+        } else if (srch) {        // bf16 initial state, widened
+#pragma unroll
+            for (int m = 0; m < NMT; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[m][4 * q + r] = (float)srch[(32 * m + 8 * q + 4 * g2 + r) * p.s0_sr + vcol];
         } else {
 #pragma unroll
             for (int m = 0; m < NMT; ++m)
@@ -623,9 +631,11 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
 
     // ------------------------------------------------ end state
     float *dst = nullptr;
+    bf16 *dsth = nullptr;         // bf16 final state (rounded to nearest even)
     int64_t rs = D;
     if (role == ROLE_OUT || (role == ROLE_SEG_OUT && seg == p.nseg - 1)) {
         if (p.sT) { dst = p.sT + n * p.sT_sn + h * p.sT_sh; rs = p.sT_sr; }
+        if (p.sTh) dsth = p.sTh + n * p.sT_sn + h * p.sT_sh;
     } else if (role == ROLE_SEG_M || role == ROLE_SEG_C) {
         dst = p.ws_maps + (((int64_t)chain * p.nseg + seg) * 2 + (role == ROLE_SEG_C)) * D * D;
     }
@@ -637,6 +647,15 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     dst[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol] = S[m][4 * q + r];
+    }
+    if (dsth) {
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dsth[(32 * m + 8 * q + 4 * g2 + r) * p.sT_sr + vcol] = (bf16)S[m][4 * q + r];
     }
 }
 

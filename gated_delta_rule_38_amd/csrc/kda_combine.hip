@@ -33,7 +33,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
 
     for (int e = tid; e < D * SL; e += NT) {
         const int ch = e / SL, v = e % SL;
-        const float x = p.s0 ? p.s0[n * p.s0_sn + h * p.s0_sh + ch * p.s0_sr + v0 + v] : 0.f;
+        const int64_t at = n * p.s0_sn + h * p.s0_sh + ch * p.s0_sr + v0 + v;
+        const float x = p.s0 ? p.s0[at] : p.s0h ? (float)p.s0h[at] : 0.f;
         sS[0][v * ST_LD + ch] = x;
         start[ch * D + v0 + v] = x;
     }

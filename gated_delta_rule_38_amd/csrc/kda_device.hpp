@@ -194,9 +194,11 @@ struct ChunkParams {
     const void *q, *k, *v;     // ET
     const float *g;            // raw log decays, or in-chunk cumsums (g_is_gamma)
     const float *beta;
-    const float *s0;           // initial state or NULL
+    const float *s0;           // initial state or NULL (fp32)
+    const bf16 *s0h;           // initial state or NULL (bf16; s0 is then NULL)
     void *o;                   // ET
-    float *sT;                 // final state or NULL
+    float *sT;                 // final state or NULL (fp32)
+    bf16 *sTh;                 // final state or NULL (bf16; sT is then NULL)
     const int32_t *cu;         // NULL: dense layout
     float *ws_maps;            // [chain][seg][2][D][D] segment operators (M, C)
     const float *ws_start;     // [chain][seg][D][D] segment start states
@@ -249,7 +251,8 @@ struct DecodeParams {
 struct CombineParams {
     const float *maps;         // [chain][seg][2][D][D]
     float *start;              // [chain][seg][D][D]
-    const float *s0;
+    const float *s0;           // initial state (fp32), or NULL
+    const bf16 *s0h;           // initial state (bf16), or NULL
     int64_t s0_sn, s0_sh, s0_sr;
     int32_t N, H, nseg;
 };

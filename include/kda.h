@@ -31,7 +31,9 @@
  *   K == V, K in {64, 128}; H >= 1; T >= 0; zero-length sequences allowed
  *   (no output rows; final_state == initial_state bit for bit).
  * Dtypes: q, k, v, out all KDA_BF16, or all KDA_F32 (the fp32 debug mode,
- *   K == 64 only); g, beta, initial_state, final_state KDA_F32.
+ *   K == 64 only); g, beta KDA_F32; initial_state and final_state each KDA_F32
+ *   or KDA_BF16 (a bf16 state pool: widened to fp32 on load, the arithmetic in
+ *   fp32, the final state rounded to nearest even).
  * Strides are in ELEMENTS; every tensor needs a unit last-dimension stride and
  *   all other strides are honoured (row-padded views give the same bits as
  *   contiguous tensors).

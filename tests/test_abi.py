@@ -300,3 +300,18 @@ def test_decode_vector_alignment(lib):
     s = decode_set()
     s["out"] = desc([4, 3, 2, 128], KDA_BF16, s["out"].data + 2)
     assert call_decode(lib, s) == 4
+
+
+def test_state_dtypes(lib):
+    """Initial and final states may each be fp32 or bf16; other dtypes are refused.
+    (Workspace sizing runs the full validation and launches nothing.)"""
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    n = ctypes.c_size_t(0)
+    for s0_dt, sT_dt, want in [(KDA_BF16, KDA_BF16, 0), (KDA_BF16, KDA_F32, 0), (KDA_F32, KDA_BF16, 0),
+                               (KDA_I32, KDA_F32, 3), (KDA_F32, KDA_I32, 3)]:
+        s = packed_set()
+        s["s0"] = desc([3, 2, 128, 128], s0_dt, s["s0"].data)
+        s["sT"] = desc([3, 2, 128, 128], sT_dt, s["sT"].data)
+        st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                            None, ctypes.byref(n))
+        assert st == want, (s0_dt, sT_dt, st, lib.kda_last_error())

@@ -439,3 +439,59 @@ def test_standalone_prep_with_gate_logits_equals_fused(kda, variant):
     o2, s2 = kda.prefill(x["q"], x["k"], x["v"], x["g_logits"], x["beta_logits"], x["initial_state"],
                          x["cu_seqlens"], prep=2, **kw)
     assert torch_equal(o1, o2) and torch_equal(s1, s2)
+
+
+# ------------------------------------------------ bf16 state I/O (fp32 arithmetic inside)
+@pytest.mark.parametrize("nseg", [1, 4])
+@pytest.mark.parametrize("variant", [1, 2])
+def test_bf16_states_match_oracle(kda, variant, nseg):
+    """bf16 initial and final states: the oracle starts from the bf16 values (widened
+    exactly) and the final state is compared after its one rounding to bf16.  A
+    zero-length sequence keeps its bf16 state bit for bit."""
+    import torch
+    w = workloads.custom([700, 0, 64, 1, 300], H=2, D=128, seed=31)
+    x = gen(w)
+    s0 = x["initial_state"].to(torch.bfloat16)
+    fin = torch.empty_like(s0)
+    say("bf16 states nseg", nseg, "variant", variant)
+    out, _ = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], s0, x["cu_seqlens"], final_state=fin,
+                         nseg=nseg, variant=variant)
+    o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["g"].cpu(), x["beta"].cpu(),
+                                s0.float().cpu(), x["cu_seqlens"].cpu())
+    eo = oracle.rel_l2(out.float().cpu().numpy().reshape(o_ref.shape), o_ref)
+    es = oracle.rel_l2(fin.float().cpu().numpy(), s_ref)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], f"rel-L2 out {eo:.3e} state {es:.3e}"
+    assert torch.equal(fin[1].view(torch.int16), s0[1].view(torch.int16))
+
+
+def test_bf16_state_in_place_and_mixed(kda):
+    """In-place bf16 state update gives the bits of a separate final state; a bf16
+    final state is the fp32 final state rounded once (same arithmetic, one store)."""
+    import torch
+    w = workloads.custom([300, 45], H=2, D=128, seed=32)
+    x = gen(w)
+    s0 = x["initial_state"].to(torch.bfloat16)
+    fin = torch.empty_like(s0)
+    o1, _ = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], s0, x["cu_seqlens"], final_state=fin)
+    f32 = torch.empty(s0.shape, dtype=torch.float32, device="cuda")
+    o2, _ = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], s0, x["cu_seqlens"], final_state=f32)
+    st = s0.clone()
+    o3, _ = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], st, x["cu_seqlens"], final_state=st)
+    torch.cuda.synchronize()
+    assert torch_equal(o1, o2) and torch_equal(o1, o3)
+    assert torch.equal(fin.view(torch.int16), st.view(torch.int16))
+    assert torch.equal(fin.view(torch.int16), f32.to(torch.bfloat16).view(torch.int16))
+
+
+def test_bf16_states_fp32_d64(kda):
+    import torch
+    w = workloads.custom([130, 7, 0, 64], H=2, D=64, dtype="f32", dense=False, seed=33)
+    x = gen(w)
+    s0 = x["initial_state"].to(torch.bfloat16)
+    fin = torch.empty_like(s0)
+    out, _ = kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], s0, x["cu_seqlens"], final_state=fin, nseg=3)
+    o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["g"].cpu(), x["beta"].cpu(),
+                                s0.float().cpu(), x["cu_seqlens"].cpu())
+    eo = oracle.rel_l2(out.cpu().numpy().reshape(o_ref.shape), o_ref)
+    es = oracle.rel_l2(fin.float().cpu().numpy(), s_ref)
+    assert eo <= TOL["f32"] and es <= TOL["bf16"], f"rel-L2 out {eo:.3e} state {es:.3e}"
