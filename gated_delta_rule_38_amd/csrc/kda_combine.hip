@@ -11,8 +11,8 @@
 // start[s+1] = M_s start[s] + C_s, in fp32 on the fp32 matrix cores (M_s and
 // C_s stay fp32: they compose many chunk maps).  Narrow slabs put D/16
 // workgroups on every chain, so a handful of chains still spreads over many
-// CUs; M_s and C_s do not depend on the scan, so each wave loads the next
-// segment's operands while it multiplies the current one.
+// CUs; M_s and C_s do not depend on the scan, so each wave loads the operands
+// of the segments up to three steps ahead while it multiplies the current one.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -42,38 +42,46 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
     // channels k is taken in the order k = 16j + 4(lane/16) + e for MFMA 4j + e, so each lane
     // feeds four consecutive MFMAs from one 16-byte read of its M row and one of the slab.
     const int mrow = 16 * wave + l16;
-    float4 m[KB];
-    float c[4];
-    auto load_maps = [&](int s) {
+    // M_s and C_s of the next PF segments wait in registers (a ring indexed at compile time by
+    // unrolling the segment loop PF times)
+    constexpr int PF = 3;
+    float4 m[PF][KB];
+    float c[PF][4];
+    auto load_maps = [&](int s, float4 (&mm)[KB], float (&cc)[4]) {
         const float *M = maps + (int64_t)s * 2 * D * D, *C = M + D * D;
 #pragma unroll
-        for (int j = 0; j < KB; ++j) m[j] = *(const float4 *)(M + mrow * D + 16 * j + 4 * g4);
+        for (int j = 0; j < KB; ++j) mm[j] = *(const float4 *)(M + mrow * D + 16 * j + 4 * g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) c[r] = C[(16 * wave + 4 * g4 + r) * D + v0 + l16];
+        for (int r = 0; r < 4; ++r) cc[r] = C[(16 * wave + 4 * g4 + r) * D + v0 + l16];
     };
-    if (p.nseg > 1) load_maps(0);
+    const int steps = p.nseg - 1;        // start[s + 1] = M_s start[s] + C_s for s < steps
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        if (u < steps) load_maps(u, m[u], c[u]);
     __syncthreads();
-    for (int s = 0; s + 1 < p.nseg; ++s) {
-        const float *cur = sS[s & 1];
-        f32x4 acc = {c[0], c[1], c[2], c[3]};
-        float4 a[KB];
+    for (int s0 = 0; s0 < steps; s0 += PF) {
 #pragma unroll
-        for (int j = 0; j < KB; ++j) a[j] = m[j];
-        if (s + 2 < p.nseg) load_maps(s + 1);
+        for (int u = 0; u < PF; ++u) {
+            const int s = s0 + u;
+            if (s >= steps) break;
+            const float *cur = sS[s & 1];
+            f32x4 acc = {c[u][0], c[u][1], c[u][2], c[u][3]};
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const float4 b = *(const float4 *)(cur + l16 * ST_LD + 16 * j + 4 * g4);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].x, b.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].y, b.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].z, b.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j].w, b.w, acc, 0, 0, 0);
+            for (int j = 0; j < KB; ++j) {
+                const float4 b = *(const float4 *)(cur + l16 * ST_LD + 16 * j + 4 * g4);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].x, b.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].y, b.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].z, b.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].w, b.w, acc, 0, 0, 0);
+            }
+            if (s + PF < steps) load_maps(s + PF, m[u], c[u]);
+            // lane (column l16, group g4) holds rows 16w + 4 g4 + r of start[s+1]
+            *(float4 *)(sS[(s + 1) & 1] + l16 * ST_LD + 16 * wave + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            float *st = start + (int64_t)(s + 1) * D * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[(16 * wave + 4 * g4 + r) * D + v0 + l16] = acc[r];
+            __syncthreads();
         }
-        // lane (column l16, group g4) holds rows 16w + 4 g4 + r of start[s+1]
-        *(float4 *)(sS[(s + 1) & 1] + l16 * ST_LD + 16 * wave + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        float *st = start + (int64_t)(s + 1) * D * D;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[(16 * wave + 4 * g4 + r) * D + v0 + l16] = acc[r];
-        __syncthreads();
     }
 }
 
