@@ -43,24 +43,28 @@ def algorithmic(w):
     return bytes_, flops, per_th
 
 
-def source_sha():
-    """Hash of every kernel source: a traffic figure taken on other sources is stale."""
+KERNEL_SOURCES = {"chunk_kernel": ("kda_chunk_pipe.hip", "kda_device.hpp"),
+                  "decode_kernel": ("kda_decode.hip", "kda_device.hpp")}
+
+
+def source_sha(kernel="chunk_kernel"):
+    """Hash of the sources a kernel is built from: a traffic figure taken on other
+    sources is stale."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(config, launches_per_step):
-    """HBM bytes per launch of the chunk kernel from the committed rocprofv3
-    PMC summary, or None when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{config}_traffic.json")
+def traffic_from_profile(config, kernel="chunk_kernel"):
+    """HBM bytes per launch of the kernel from the committed rocprofv3 PMC
+    summary, or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha") != source_sha():
+    if rec.get("kernel_source_sha") != source_sha(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -197,10 +201,10 @@ def decode_main(a, w):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; see workloads.py)",
         "config": w.describe(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(w.name, "decode_kernel")},
         "kernel": {"name": "kda_decode", "avg_ms": kern_ms, "launches_per_step": k_n // max(1, a.steps),
                    "algorithmic_bytes_per_launch": bytes_, "flops_per_launch": flops,
-                   "kernel_source_sha": source_sha()},
+                   "kernel_source_sha": source_sha("decode_kernel")},
         "correctness": {"rel_l2_out": eo, "rel_l2_state": es},
     }
     if not a.no_cpu_baseline:
@@ -280,7 +284,7 @@ def main():
     # the whole workload in one launch
     bytes_launch = bytes_ / launches_per_step
     achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
-    tr = traffic_from_profile(a.config, launches_per_step)
+    tr = traffic_from_profile(a.config) if launches_per_step == 1 else None
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     tflops = flops / launches_per_step / (kern_ms * 1e-3) / 1e12
     rec = {
@@ -294,7 +298,7 @@ def main():
                  "flops_per_launch": flops / launches_per_step},
         "kernel": {"name": "kda_chunk", "avg_ms": kern_ms, "launches_per_step": launches_per_step,
                    "algorithmic_bytes_per_launch": bytes_launch, "bytes_per_token_head": per_th,
-                   "kernel_source_sha": source_sha()},
+                   "kernel_source_sha": source_sha("chunk_kernel")},
         "correctness": {"sampled_rel_l2_max": gate},
     }
     if not a.no_cpu_baseline:
