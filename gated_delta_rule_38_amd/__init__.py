@@ -205,7 +205,7 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
 
 def decode(q, k, v, g, beta, state_pool, state_indices, num_tokens=None, out=None, update_state: bool = True,
            write_out: bool = True, gate_logits: bool = False, gate_lower_bound: float = -5.0,
-           beta_logits: bool = False, stream=None):
+           beta_logits: bool = False, stall_wave: int = -1, stall_cycles: int = 0, stream=None):
     """Recurrent decode / draft verify against a state pool (kda_decode).
 
     q, k, g [R, T, H, K]; v [R, T, H, V]; beta [R, T, H]; 1 <= T <= 8.
@@ -221,7 +221,8 @@ def decode(q, k, v, g, beta, state_pool, state_indices, num_tokens=None, out=Non
     if out is None and write_out:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    opts = options(gate_logits=gate_logits, gate_lower_bound=gate_lower_bound, beta_logits=beta_logits)
+    opts = options(stall_wave=stall_wave, stall_cycles=stall_cycles, gate_logits=gate_logits,
+                   gate_lower_bound=gate_lower_bound, beta_logits=beta_logits)
     do = describe(out) if out is not None else None
     dn = describe(num_tokens) if num_tokens is not None else None
     _check(lib.kda_decode(ctypes.byref(describe(q)), ctypes.byref(describe(k)), ctypes.byref(describe(v)),

@@ -599,6 +599,8 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
     dp.gate_act = (opts && opts->gate_act) ? 1 : 0;
     dp.gate_lb = opts ? opts->gate_lower_bound : 0.f;
     dp.beta_act = (opts && opts->beta_act) ? 1 : 0;
+    dp.stall_wave = (opts && opts->stall_wave > 0) ? opts->stall_wave - 1 : -1;
+    dp.stall_iters = (opts && opts->stall_cycles > 0) ? std::max(1, opts->stall_cycles / 127) : 0;
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = timed("kda_decode", s, [&] {
         return kda::launch_decode(dp, (int)D, q->dtype == KDA_F32, state_pool->dtype == KDA_BF16, s);

@@ -38,7 +38,8 @@ __device__ __forceinline__ void ld4(const bf16 *p, float (&x)[4]) { Vec4<bf16>::
 __device__ __forceinline__ void st4(float *p, const float (&x)[4]) { *(float4 *)p = make_float4(x[0], x[1], x[2], x[3]); }
 __device__ __forceinline__ void st4(bf16 *p, const float (&x)[4]) { Vec4<bf16>::store(p, Vec4<bf16>::pack(x)); }   // RNE
 
-template <int D, typename IT, typename ST>
+// STALL: the test build with one wave stalled after every barrier (the results must not change).
+template <int D, typename IT, typename ST, bool STALL>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
 {
     constexpr int NCQ = D / 4;            // column quads = lanes per row group
@@ -72,7 +73,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
     float s[RPG][4];
 #pragma unroll
     for (int j = 0; j < RPG; ++j) ld4(ps + j * p.p_sr, s[j]);
-    __syncthreads();
+    auto sync = [&]() {
+        __syncthreads();
+        if constexpr (STALL) {
+            if (wave == p.stall_wave)
+                for (int i = 0; i < p.stall_iters; ++i) __builtin_amdgcn_s_sleep(127);
+        }
+    };
+    sync();
 
     // sum of x over the row groups, for this lane's 4 columns: butterflies over the row-group
     // lanes of the wave, then the 4 waves' partials in a fixed order
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] += __shfl_xor(x[e], off);
         if (lane < NCQ) *(float4 *)&red[wave][4 * cq] = make_float4(x[0], x[1], x[2], x[3]);
-        __syncthreads();
+        sync();
         const float4 a = *(const float4 *)&red[0][4 * cq], b = *(const float4 *)&red[1][4 * cq];
         const float4 c = *(const float4 *)&red[2][4 * cq], d = *(const float4 *)&red[3][4 * cq];
         sum[0] = (a.x + b.x) + (c.x + d.x);
@@ -130,11 +138,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
     }
 }
 
+template <int D, typename IT, typename ST>
+static void launch_decode_t(const DecodeParams &p, unsigned blocks, hipStream_t stream)
+{
+    if (p.stall_wave >= 0 && p.stall_iters > 0)
+        hipLaunchKernelGGL((decode_kernel<D, IT, ST, true>), dim3(blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, IT, ST, false>), dim3(blocks), dim3(256), 0, stream, p);
+}
+
 hipError_t launch_decode(const DecodeParams &p, int D, bool io_f32, bool state_bf16, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)p.R * p.H;
     if (blocks <= 0) return hipSuccess;
-#define KDA_DECODE(DD, IT, ST) hipLaunchKernelGGL((decode_kernel<DD, IT, ST>), dim3((unsigned)blocks), dim3(256), 0, stream, p)
+#define KDA_DECODE(DD, IT, ST) launch_decode_t<DD, IT, ST>(p, (unsigned)blocks, stream)
     if (D == 128 && !io_f32 && !state_bf16) KDA_DECODE(128, bf16, float);
     else if (D == 128 && !io_f32 && state_bf16) KDA_DECODE(128, bf16, bf16);
     else if (D == 128 && io_f32 && !state_bf16) KDA_DECODE(128, float, float);

@@ -246,6 +246,8 @@ struct DecodeParams {
     int32_t gate_act;
     float gate_lb;
     int32_t beta_act;
+    int32_t stall_wave;        // test hook: wave index to stall after every barrier, or -1
+    int32_t stall_iters;       // s_sleep(127) repetitions per stall
 };
 
 struct CombineParams {

@@ -170,8 +170,9 @@ kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int
  * request (no output rows, no state write).  num_tokens: int32 [R], device
  * memory, or NULL.  Both are read on the device only.
  * opts: NULL, or a kda_options_t whose gate_act / gate_lower_bound / beta_act
- * take g and beta as logits exactly as in kda_prefill_ws (its other fields are
- * ignored here).
+ * take g and beta as logits exactly as in kda_prefill_ws, and whose stall_wave /
+ * stall_cycles test hook stalls one of the kernel's 4 waves after every barrier
+ * (the results must not change); nseg, prep and variant are ignored here.
  * Strides in elements with unit last stride, as for kda_prefill; state_pool and
  * out also need base addresses and strides aligned to 4 elements (their rows
  * move as 4-element vectors).  out may not overlap any input or the pool; the pool may not overlap any input.  Two

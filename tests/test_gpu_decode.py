@@ -188,3 +188,39 @@ def test_decode_logit_inputs(kda):
     torch.cuda.synchronize()
     g64, b64 = oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), -5.0)
     check(x, out, before, pool, idx, ntok, 5e-3, g=g64, beta=b64)
+
+
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("wave", [0, 1, 2, 3])
+def test_decode_stalled_wave_gives_same_bits(kda, wave, pool_dtype):
+    """A copy of the decode kernel with one of its 4 waves stalled ~20 us after every
+    barrier reproduces the unstalled bits (its cross-wave reductions go through LDS)."""
+    import torch
+    x, pool, idx, ntok = make_case(R=5, T=4, H=2, D=128, dtype="bf16", pool_dtype=pool_dtype, seed=55)
+    say("decode stall wave", wave, pool_dtype)
+    p1, p2 = pool.clone(), pool.clone()
+    o1 = torch.full_like(x["v"], -512.0)
+    o2 = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], p1, idx, ntok, out=o1)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], p2, idx, ntok, out=o2, stall_wave=wave,
+               stall_cycles=127 * 6)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(p1.view(torch.int16) if p1.dtype == torch.bfloat16 else p1.view(torch.int32),
+                       p2.view(torch.int16) if p2.dtype == torch.bfloat16 else p2.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_bf16", "verify4"])
+def test_decode_bench_workloads(kda, name):
+    """The bench's decode workloads at full size (256 requests x 32 heads), every
+    request against the float64 oracle, in the launch the bench times."""
+    import torch
+    w = workloads.DECODE_WORKLOADS[name]
+    x = workloads.make_decode_inputs(w, device="cuda")
+    say("decode workload", name)
+    pool = x["pool"].clone()
+    out = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, x["idx"], None, out=out)
+    torch.cuda.synchronize()
+    ntok = torch.full((w.R,), w.T, dtype=torch.int32, device="cuda")
+    check(x, out, x["pool"], pool, x["idx"], ntok, 5e-3)
