@@ -36,7 +36,9 @@ class KdaTensor(ctypes.Structure):
 class KdaOptions(ctypes.Structure):
     _fields_ = [("nseg", ctypes.c_int32), ("prep", ctypes.c_int32),
                 ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32), ("variant", ctypes.c_int32),
-                ("gate_act", ctypes.c_int32), ("gate_lower_bound", ctypes.c_float), ("beta_act", ctypes.c_int32)]
+                ("gate_act", ctypes.c_int32), ("gate_lower_bound", ctypes.c_float), ("beta_act", ctypes.c_int32),
+                ("out_gate", ctypes.POINTER(KdaTensor)), ("norm_weight", ctypes.POINTER(KdaTensor)),
+                ("norm_eps", ctypes.c_float)]
 
 
 class KdaError(RuntimeError):
@@ -129,10 +131,20 @@ def _require_gpu(*tensors):
 
 
 def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0, variant: int = 0,
-            gate_logits: bool = False, gate_lower_bound: float = -5.0, beta_logits: bool = False) -> KdaOptions:
+            gate_logits: bool = False, gate_lower_bound: float = -5.0, beta_logits: bool = False,
+            out_gate=None, norm_weight=None, norm_eps: float = 1e-6) -> KdaOptions:
     o = KdaOptions()
     o.nseg, o.prep, o.variant = nseg, prep, variant
     o.gate_act, o.gate_lower_bound, o.beta_act = int(bool(gate_logits)), gate_lower_bound, int(bool(beta_logits))
+    o.norm_eps = norm_eps
+    if out_gate is not None or norm_weight is not None:
+        # the descriptors live as long as the options object
+        o._norm = (describe(out_gate) if out_gate is not None else None,
+                   describe(norm_weight) if norm_weight is not None else None)
+        if o._norm[0] is not None:
+            o.out_gate = ctypes.pointer(o._norm[0])
+        if o._norm[1] is not None:
+            o.norm_weight = ctypes.pointer(o._norm[1])
     o.stall_wave = stall_wave + 1 if stall_wave >= 0 else 0
     o.stall_cycles = stall_cycles
     return o
@@ -165,7 +177,8 @@ def workspace_size(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=No
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
             output_final_state: bool = True, nseg: int = 0, prep: int = 0, stall_wave: int = -1,
             stall_cycles: int = 0, variant: int = 0, gate_logits: bool = False, gate_lower_bound: float = -5.0,
-            beta_logits: bool = False, workspace=None, stream=None) -> Tuple:
+            beta_logits: bool = False, out_gate=None, norm_weight=None, norm_eps: float = 1e-6,
+            workspace=None, stream=None) -> Tuple:
     """KDA chunked prefill.  Returns (out, final_state).
 
     Dense layout: q, k, g [B, T, H, K], v [B, T, H, V], beta [B, T, H].
@@ -173,6 +186,8 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     ``cu_seqlens`` [N + 1] on the GPU.  States are fp32 [N, H, K, V].
     ``gate_logits``: g holds logits x, the log decay is gate_lower_bound * sigmoid(x);
     ``beta_logits``: beta holds logits, beta = sigmoid(beta) (both fused into the gate scan).
+    ``out_gate``, ``norm_weight``, ``norm_eps``: the gated RMS norm output epilogue,
+    out = o * rsqrt(mean(o^2) + eps) * norm_weight * sigmoid(out_gate) per (token, head).
     With the default knobs this calls ``kda_prefill`` (library-cached
     workspace); any knob or a ``workspace`` tensor routes through
     ``kda_prefill_ws`` with a torch-allocated workspace.
@@ -184,11 +199,12 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     plain = (nseg == 0 and prep == 0 and stall_wave < 0 and variant == 0 and workspace is None
-             and not gate_logits and not beta_logits)
+             and not gate_logits and not beta_logits and out_gate is None and norm_weight is None)
     if plain:
         _check(lib.kda_prefill(*[_ptr(d) for d in ds], ctypes.c_void_p(st)))
         return out, final_state
-    opts = options(nseg, prep, stall_wave, stall_cycles, variant, gate_logits, gate_lower_bound, beta_logits)
+    opts = options(nseg, prep, stall_wave, stall_cycles, variant, gate_logits, gate_lower_bound, beta_logits,
+                   out_gate, norm_weight, norm_eps)
     need = ctypes.c_size_t(0)
     _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value:
@@ -205,7 +221,8 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
 
 def decode(q, k, v, g, beta, state_pool, state_indices, num_tokens=None, out=None, update_state: bool = True,
            write_out: bool = True, gate_logits: bool = False, gate_lower_bound: float = -5.0,
-           beta_logits: bool = False, stall_wave: int = -1, stall_cycles: int = 0, stream=None):
+           beta_logits: bool = False, stall_wave: int = -1, stall_cycles: int = 0, out_gate=None,
+           norm_weight=None, norm_eps: float = 1e-6, stream=None):
     """Recurrent decode / draft verify against a state pool (kda_decode).
 
     q, k, g [R, T, H, K]; v [R, T, H, V]; beta [R, T, H]; 1 <= T <= 8.
@@ -222,7 +239,8 @@ def decode(q, k, v, g, beta, state_pool, state_indices, num_tokens=None, out=Non
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     opts = options(stall_wave=stall_wave, stall_cycles=stall_cycles, gate_logits=gate_logits,
-                   gate_lower_bound=gate_lower_bound, beta_logits=beta_logits)
+                   gate_lower_bound=gate_lower_bound, beta_logits=beta_logits, out_gate=out_gate,
+                   norm_weight=norm_weight, norm_eps=norm_eps)
     do = describe(out) if out is not None else None
     dn = describe(num_tokens) if num_tokens is not None else None
     _check(lib.kda_decode(ctypes.byref(describe(q)), ctypes.byref(describe(k)), ctypes.byref(describe(v)),

@@ -234,6 +234,34 @@ kda_status_t validate(const kda_tensor_t *q, const kda_tensor_t *k, const kda_te
     return KDA_OK;
 }
 
+// Output-norm options: out_gate like out (same shape, dtype; rows 4-element aligned), weight
+// fp32 [D] contiguous, eps > 0; neither may overlap out.
+kda_status_t check_out_norm(const kda_options_t *o, const kda_tensor_t *out, int64_t D)
+{
+    if (!o || (!o->out_gate && !o->norm_weight)) return KDA_OK;
+    kda_status_t st;
+    if ((st = check_basic(o->out_gate, "out_gate", false)) || (st = check_basic(o->norm_weight, "norm_weight", false)))
+        return st;
+    if (!out) return fail(KDA_ERR_NULL, "the output norm needs out");
+    const kda_tensor_t *z = o->out_gate, *w = o->norm_weight;
+    if (z->dtype != out->dtype) return fail(KDA_ERR_DTYPE, "out_gate must have out's dtype");
+    if (z->ndim != out->ndim) return fail(KDA_ERR_SHAPE, "out_gate must have out's shape");
+    for (int d = 0; d < z->ndim; ++d)
+        if (z->shape[d] != out->shape[d]) return fail(KDA_ERR_SHAPE, "out_gate must have out's shape");
+    const int64_t es = (int64_t)elem_size(z->dtype);
+    if ((uintptr_t)z->data % (4 * es)) return fail(KDA_ERR_LAYOUT, "out_gate needs a 4-element-aligned base");
+    for (int d = 0; d + 1 < z->ndim; ++d)
+        if (z->shape[d] > 1 && (z->stride[d] * es) % (4 * es))
+            return fail(KDA_ERR_LAYOUT, "out_gate needs 4-element-aligned strides");
+    if (w->dtype != KDA_F32 || w->ndim != 1 || w->shape[0] != D)
+        return fail(KDA_ERR_SHAPE, "norm_weight must be fp32 [%lld]", (long long)D);
+    if ((uintptr_t)w->data % 16) return fail(KDA_ERR_LAYOUT, "norm_weight needs a 16-byte-aligned base");
+    if (!(o->norm_eps > 0.f) || !(o->norm_eps < 1e30f)) return fail(KDA_ERR_UNSUPPORTED, "norm_eps must be positive");
+    const Span so = span_of(out);
+    if (overlaps(so, span_of(z)) || overlaps(so, span_of(w))) return fail(KDA_ERR_ALIAS, "out overlaps out_gate or norm_weight");
+    return KDA_OK;
+}
+
 // ------------------------------------------------------------------ plan
 struct Plan {
     int nseg = 1;
@@ -286,6 +314,12 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
         return fail(KDA_ERR_UNSUPPORTED, "gate_act %d / beta_act %d (0 or 1)", o->gate_act, o->beta_act);
     if (o && o->gate_act && !(o->gate_lower_bound >= -5.f && o->gate_lower_bound <= 0.f))
         return fail(KDA_ERR_UNSUPPORTED, "gate_lower_bound %g outside [-5, 0]", (double)o->gate_lower_bound);
+    kda_status_t st;
+    if ((st = check_out_norm(o, P.tout, P.D))) return st;
+    if (o && o->out_gate && !pl.pipe)
+        return fail(KDA_ERR_UNSUPPORTED, "the output norm runs on the pipelined kernel (head size 128, bf16)");
+    if (o && o->out_gate && 32 * o->out_gate->stride[o->out_gate->ndim - 3] * 2 + 1024 > (int64_t)INT32_MAX)
+        return fail(KDA_ERR_UNSUPPORTED, "out_gate token stride too large for the pipelined kernel");
     pl.standalone_prep = prep == 1;   // otherwise every chunk-kernel pass scans its own chunks
     size_t off = 0;
     if (pl.standalone_prep) {
@@ -382,6 +416,17 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     cp.gate_act = (o && o->gate_act) ? 1 : 0;
     cp.gate_lb = o ? o->gate_lower_bound : 0.f;
     cp.beta_act = (o && o->beta_act) ? 1 : 0;
+    if (o && o->out_gate) {
+        cp.z = o->out_gate->data;
+        cp.nw = (const float *)o->norm_weight->data;
+        cp.eps = o->norm_eps;
+        const int nd = o->out_gate->ndim;
+        const int64_t *zs = o->out_gate->stride;
+        // out_gate shares out's layout: dense [B, T, H, V] or packed [T, H, V] / [1, T, H, V]
+        cp.z_sb = P.dense ? zs[0] : 0;
+        cp.z_st = zs[nd - 3];
+        cp.z_sh = zs[nd - 2];
+    }
     const bool stall = cp.stall_wave >= 0 && cp.stall_iters > 0;
     const int D = (int)P.D;
     hipError_t e;
@@ -578,6 +623,9 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
         return fail(KDA_ERR_UNSUPPORTED, "gate_act %d / beta_act %d (0 or 1)", opts->gate_act, opts->beta_act);
     if (opts && opts->gate_act && !(opts->gate_lower_bound >= -5.f && opts->gate_lower_bound <= 0.f))
         return fail(KDA_ERR_UNSUPPORTED, "gate_lower_bound %g outside [-5, 0]", (double)opts->gate_lower_bound);
+    if ((st = check_out_norm(opts, out, D))) return st;
+    if (opts && opts->out_gate && overlaps(sp, span_of(opts->out_gate)))
+        return fail(KDA_ERR_ALIAS, "state_pool overlaps out_gate");
     if (R == 0 || (!out && !update_state)) return KDA_OK;
 
     kda::DecodeParams dp{};
@@ -601,6 +649,12 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
     dp.beta_act = (opts && opts->beta_act) ? 1 : 0;
     dp.stall_wave = (opts && opts->stall_wave > 0) ? opts->stall_wave - 1 : -1;
     dp.stall_iters = (opts && opts->stall_cycles > 0) ? std::max(1, opts->stall_cycles / 127) : 0;
+    if (opts && opts->out_gate) {
+        dp.z = opts->out_gate->data;
+        dp.z_sr = opts->out_gate->stride[0]; dp.z_st = opts->out_gate->stride[1]; dp.z_sh = opts->out_gate->stride[2];
+        dp.nw = (const float *)opts->norm_weight->data;
+        dp.eps = opts->norm_eps;
+    }
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = timed("kda_decode", s, [&] {
         return kda::launch_decode(dp, (int)D, q->dtype == KDA_F32, state_pool->dtype == KDA_BF16, s);

@@ -79,7 +79,11 @@ constexpr int S_SC = S_TB + 2 * 16 * A_LD * 2;
 constexpr int S_DEC = S_SC + 2 * D * 4;       // chunk decays e^{G_L}: a ring of 3 chunks
 constexpr int S_BETA = S_DEC + 3 * D * 4;     // beta: a ring of 3 chunks
 constexpr int SMEM = S_BETA + 3 * C * 4;
-static_assert(SMEM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+// output norm: per-token partial sums of squares of the 4 consumer waves, and the norm weight
+constexpr int S_NRM = SMEM;
+constexpr int S_NW = S_NRM + C * 4 * 4;
+constexpr int SMEM_NORM = S_NW + D * 4;
+static_assert(SMEM_NORM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
 static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TB % 16 == 0 &&
               S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
 
@@ -159,10 +163,14 @@ __device__ __forceinline__ void decay_tile(f32x16 &s, const float4 dd)
 
 // OUT: the launch's roles store outputs (ROLE_OUT, ROLE_SEG_OUT); the segment-map roles do
 // not, and skip everything that only feeds O: q, Qt, the P tiles and the O products.
-template <bool STALL, bool OUT>
+// NORM (with OUT): the output rows pass through the gated RMS norm before they are written.
+// A token's row spans the 4 consumer waves, so each wave leaves its partial sum of squares
+// in LDS and keeps its O tile in registers across the step's barrier; the next interval 1
+// (or, for the last chunk, the end of the chain) normalises and stores it.
+template <bool STALL, bool OUT, bool NORM>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ __attribute__((aligned(16))) char smem[NORM ? SMEM_NORM : SMEM];
     float *sG = (float *)(smem + S_G), *sGraw = (float *)(smem + S_GRAW);
     bf16 *sX = (bf16 *)(smem + S_X), *sY = (bf16 *)(smem + S_Y), *sZ = (bf16 *)(smem + S_Z);
     bf16 *sKb = (bf16 *)(smem + S_KB), *sA10 = (bf16 *)(smem + S_A10);
@@ -567,6 +575,42 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         const uint32_t ost = 2 * (uint32_t)p.o_st, oro = l32 * ost + 2 * (32 * cw + 4 * g2);
         f32x16 S[4];
         const int vcol = 32 * cw + l32;
+        // output norm: the pending O tile of the previous chunk, its gate factors w * sigmoid(z),
+        // its token range, and the gate rows of the chunk after it (loaded a step ahead)
+        float *sNrm = (float *)(smem + S_NRM), *sNw = (float *)(smem + S_NW);
+        f32x16 Opend = {}, gw = {};
+        uint2 zr[4];
+        int pend_tok0 = 0, pend_L = 0;
+        const char *zb = nullptr;
+        uint32_t zst = 0;
+        // gate rows of chunk c: row l32 (rows past the chunk's end re-read its last row), this
+        // lane's 16 columns
+        auto load_gate = [&](int c) {
+            const int L = min(C, len - c * C);
+            const char *zc = zb + (int64_t)(c * C) * zst + min(l32, L - 1) * zst + 2 * (32 * cw + 4 * g2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) zr[q] = *(const uint2 *)(zc + 16 * q);
+        };
+        if constexpr (NORM) {
+            zb = (const char *)p.z + 2 * (bsel * p.z_sb + h * p.z_sh + t0 * p.z_st);
+            zst = 2 * (uint32_t)p.z_st;
+            if (tid < D) sNw[tid] = p.nw[tid];
+            if (nck > 0) load_gate(c_begin);
+        }
+        // O row l32 of the pending chunk: o * rsqrt(mean(o^2) + eps) * (w * sigmoid(z))
+        auto norm_store = [&]() {
+            const float4 nr = *(const float4 *)(sNrm + 4 * l32);
+            const float rn = __builtin_amdgcn_rsqf(((nr.x + nr.y) + (nr.z + nr.w)) * (1.f / D) + p.eps);
+            if (l32 < pend_L) {
+                bf16 *dst = (bf16 *)(ob + (int64_t)pend_tok0 * ost + oro);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float o4[4] = {Opend[4 * q] * rn * gw[4 * q], Opend[4 * q + 1] * rn * gw[4 * q + 1],
+                                         Opend[4 * q + 2] * rn * gw[4 * q + 2], Opend[4 * q + 3] * rn * gw[4 * q + 3]};
+                    V4::store(dst + 8 * q, V4::pack(o4));
+                }
+            }
+        };
         {
             const float *src = nullptr;
             int64_t rs = D;
@@ -664,6 +708,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 }
             }
             if (cact && cw == 0) build_T_off(sBeta + ((t + 2) % 3) * C, (bf16 *)(CB + B_T));
+            if constexpr (NORM) {
+                if (t >= 2) norm_store();     // O of chunk t-2, formed in the last interval 2
+            }
             sync();
             // ---------------- interval 2: U = (T diag(beta)) R; O = Qt S + P U, stored
             if (cact) {
@@ -721,7 +768,29 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                         mma32(S[m], fa, UB[s]);
                     }
                 }
-                if (OUT && l32 < cL) {
+                if constexpr (NORM) {
+                    // this wave's 32 columns of each token's sum of squares; the gate factors of
+                    // this chunk, then the gate rows of the next
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) ss += O[e] * O[e];
+                    ss += __shfl_xor(ss, 32);
+                    if (g2 == 0) sNrm[4 * l32 + cw] = ss;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float zf[4];
+                        V4::unpack(zr[q], zf);
+                        const float4 w4 = *(const float4 *)(sNw + 32 * cw + 4 * g2 + 8 * q);
+                        gw[4 * q] = w4.x * sigmoid_act(zf[0]);
+                        gw[4 * q + 1] = w4.y * sigmoid_act(zf[1]);
+                        gw[4 * q + 2] = w4.z * sigmoid_act(zf[2]);
+                        gw[4 * q + 3] = w4.w * sigmoid_act(zf[3]);
+                    }
+                    load_gate(min(cc + 1, c_last));
+                    Opend = O;
+                    pend_tok0 = ctok0;
+                    pend_L = cL;
+                } else if (OUT && l32 < cL) {
                     bf16 *dst = (bf16 *)(ob + (int64_t)ctok0 * ost + oro);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -731,6 +800,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 }
             }
             sync();
+        }
+        if constexpr (NORM) {
+            if (nck > 0) norm_store();        // O of the last chunk
         }
         float *dst = nullptr;
         bf16 *dsth = nullptr;         // bf16 final state (rounded to nearest even)
@@ -766,10 +838,15 @@ hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStre
 {
     if (grid <= 0) return hipSuccess;
     const bool out = p.role == ROLE_OUT || p.role == ROLE_SEG_OUT;
-    if (stall && out) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<true, true>), dim3(grid), dim3(pipe::NT), 0, st, p);
-    else if (stall) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<true, false>), dim3(grid), dim3(pipe::NT), 0, st, p);
-    else if (out) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<false, true>), dim3(grid), dim3(pipe::NT), 0, st, p);
-    else hipLaunchKernelGGL((pipe::chunk_pipe_kernel<false, false>), dim3(grid), dim3(pipe::NT), 0, st, p);
+    const bool norm = out && p.z;
+#define KDA_PIPE(S, O, N) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<S, O, N>), dim3(grid), dim3(pipe::NT), 0, st, p)
+    if (stall && norm) KDA_PIPE(true, true, true);
+    else if (stall && out) KDA_PIPE(true, true, false);
+    else if (stall) KDA_PIPE(true, false, false);
+    else if (norm) KDA_PIPE(false, true, true);
+    else if (out) KDA_PIPE(false, true, false);
+    else KDA_PIPE(false, false, false);
+#undef KDA_PIPE
     return hipGetLastError();
 }
 

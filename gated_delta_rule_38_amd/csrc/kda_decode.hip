@@ -19,7 +19,9 @@
 // in a fixed order (lane butterflies inside a wave, then the 4 waves through
 // LDS), so results do not depend on timing.  The few tokens are staged in LDS
 // once.  An index outside [0, P) skips the request (no output rows, no state
-// write), so a bad index can never address memory.
+// write), so a bad index can never address memory.  With an output gate the
+// output row is normalised before it is written (gated RMS norm over the D
+// value channels: o * rsqrt(mean(o^2) + eps) * weight * sigmoid(gate)).
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -130,6 +132,23 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
         }
         float os[4];
         reduce(po, sRed[1], os);
+        if (p.z) {
+            // gated RMS norm of the output row: every lane holds the sums of its 4 columns, and a
+            // butterfly over the lanes of one row group adds the D/4 lane groups in a fixed order
+            float ss = (os[0] * os[0] + os[1] * os[1]) + (os[2] * os[2] + os[3] * os[3]);
+#pragma unroll
+            for (int off = 1; off < NCQ; off <<= 1) ss += __shfl_xor(ss, off);
+            const float rn = __builtin_amdgcn_rsqf(ss * (1.f / D) + p.eps);
+            if (o && tid < NCQ) {
+                float zz[4];
+                ld4((const IT *)p.z + r * p.z_sr + h * p.z_sh + t * p.z_st + 4 * cq, zz);
+                const float4 w4 = *(const float4 *)(p.nw + 4 * cq);
+                os[0] = os[0] * rn * w4.x * sigmoid_act(zz[0]);
+                os[1] = os[1] * rn * w4.y * sigmoid_act(zz[1]);
+                os[2] = os[2] * rn * w4.z * sigmoid_act(zz[2]);
+                os[3] = os[3] * rn * w4.w * sigmoid_act(zz[3]);
+            }
+        }
         if (o && tid < NCQ) st4(o + t * p.o_st, os);
     }
     if (p.update) {

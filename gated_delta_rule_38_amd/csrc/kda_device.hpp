@@ -215,6 +215,10 @@ struct ChunkParams {
     int32_t gate_act;          // g holds logits: log decay = gate_lb * sigmoid(g)
     float gate_lb;
     int32_t beta_act;          // beta holds logits: beta = sigmoid(beta)
+    const void *z;             // output gate (out's layout and dtype), or NULL: no output norm
+    int64_t z_sb, z_st, z_sh;
+    const float *nw;           // norm weight [D]
+    float eps;
 };
 
 struct PrepParams {
@@ -248,6 +252,10 @@ struct DecodeParams {
     int32_t beta_act;
     int32_t stall_wave;        // test hook: wave index to stall after every barrier, or -1
     int32_t stall_iters;       // s_sleep(127) repetitions per stall
+    const void *z;             // output gate [R][T][H][D] (out's dtype), or NULL: no output norm
+    int64_t z_sr, z_st, z_sh;
+    const float *nw;           // norm weight [D]
+    float eps;
 };
 
 struct CombineParams {

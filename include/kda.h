@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -102,6 +102,16 @@ typedef struct {
     int32_t gate_act;
     float gate_lower_bound;
     int32_t beta_act;
+    /* Output epilogue: the gated RMS normalisation of every (token, head) output row
+     * (the fused output norm of TensorRT-LLM PR #19960), applied before out is written:
+     *     out_c = o_c / sqrt(mean_c(o_c^2) + norm_eps) * norm_weight[c] * sigmoid(out_gate_c)
+     * over the value channels c.  out_gate: out's shape, layout and dtype (4-element
+     * aligned rows); norm_weight: fp32 [V], contiguous; norm_eps > 0.  NULL out_gate (the
+     * default) writes o itself.  Prefill supports it on the pipelined kernel (head size
+     * 128, bf16); kda_decode supports every shape it takes. */
+    const kda_tensor_t *out_gate;
+    const kda_tensor_t *norm_weight;
+    float norm_eps;
 } kda_options_t;
 
 /*

@@ -13,7 +13,10 @@ Contents
                            to pin the oracle and the chunk algebra (pin P7);
   * ``activations``     -- float64 gate and beta activations for inputs given
                            as logits (g = lower_bound * sigmoid(x), beta =
-                           sigmoid(b)), applied before the recurrence.
+                           sigmoid(b)), applied before the recurrence;
+  * ``gated_rmsnorm``   -- the float64 output epilogue: RMS normalisation of
+                           each (token, head) output row, a per-channel weight
+                           and a sigmoid output gate.
 
 The method (the reading of the pages, which name Kimi Delta Attention and its
 "WY-form chunk" but never print the recurrence): per sequence n and head h,
@@ -152,6 +155,20 @@ def activations(g_logits=None, beta_logits=None, lower_bound: float = -5.0):
     g = None if g_logits is None else float(lower_bound) * sigmoid(g_logits)
     beta = None if beta_logits is None else sigmoid(beta_logits)
     return g, beta
+
+
+def gated_rmsnorm(o, z, weight, eps: float):
+    """Float64 gated RMS normalisation of output rows.
+
+    TensorRT-LLM PR #19960 lists a fused attention epilogue with a gated RMSNorm
+    on the KDA output but prints no formula; the reading taken here is the plain
+    gated RMSNorm: for every token and head, over the value channels c,
+        y_c = o_c / sqrt(mean_c(o_c^2) + eps) * weight_c * sigmoid(z_c).
+    o, z: [..., V] (any leading shape); weight: [V].  Returns float64 [..., V].
+    """
+    o, z, w = _f64(o), _f64(z), _f64(weight)
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + float(eps))
+    return o * r * w * (1.0 / (1.0 + np.exp(-z)))
 
 
 def rel_l2(x, ref) -> float:

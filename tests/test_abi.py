@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(5) == b"KDA_ERR_ALIAS"
     assert lib.kda_status_string(8) == b"KDA_ERR_HIP"
@@ -315,3 +315,38 @@ def test_state_dtypes(lib):
         st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
                                             None, ctypes.byref(n))
         assert st == want, (s0_dt, sT_dt, st, lib.kda_last_error())
+
+
+def test_output_norm_options_validated(lib):
+    """The gated RMS norm epilogue's descriptors: out_gate like out, fp32 [V] weight,
+    positive eps, no overlap with out, and only on the pipelined kernel; checked on
+    the host (workspace sizing launches nothing)."""
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    n = ctypes.c_size_t(0)
+    gap = 1 << 32
+
+    def size(z, w, eps=1e-6, variant=0, dt=KDA_BF16, D=128):
+        s = packed_set(D=D, dt=dt)
+        opts = kda.options(variant=variant)
+        opts.norm_eps = eps
+        keep = (z, w)
+        if z is not None:
+            opts.out_gate = ctypes.pointer(z)
+        if w is not None:
+            opts.norm_weight = ctypes.pointer(w)
+        st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                            ctypes.byref(opts), ctypes.byref(n))
+        del keep
+        return st
+    z = lambda shape=(100, 2, 128), dt=KDA_BF16, base=FAKE + 10 * gap: desc(list(shape), dt, base)
+    w = lambda D=128, dt=KDA_F32, base=FAKE + 11 * gap: desc([D], dt, base)
+    assert size(z(), w()) == 0
+    assert size(z(), None) == 1
+    assert size(z(dt=KDA_F32), w()) == 3
+    assert size(z(shape=(100, 2, 64)), w()) == 2
+    assert size(z(), w(D=64)) == 2
+    assert size(z(), w(dt=KDA_BF16)) == 2
+    assert size(z(), w(), eps=0.0) == 6
+    assert size(z(base=FAKE + 7 * gap), w()) == 5          # out_gate is out
+    assert size(z(base=FAKE + 10 * gap + 2), w()) == 4     # misaligned rows
+    assert size(z(), w(), variant=1) == 6                   # single-role kernel: unsupported

@@ -224,3 +224,28 @@ def test_decode_bench_workloads(kda, name):
     torch.cuda.synchronize()
     ntok = torch.full((w.R,), w.T, dtype=torch.int32, device="cuda")
     check(x, out, x["pool"], pool, x["idx"], ntok, 5e-3)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_output_norm(kda, D):
+    """The gated RMS norm epilogue in decode: outputs equal the float64 oracle's
+    outputs through the float64 gated RMS norm; the pool update is unchanged."""
+    import torch
+    x, pool, idx, ntok = make_case(R=6, T=3, H=2, D=D, dtype="bf16", pool_dtype="f32", seed=56)
+    gen = torch.Generator(device="cuda").manual_seed(57)
+    z = torch.randn(x["v"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn(D, generator=gen, device="cuda")
+    before = pool.clone()
+    out = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, idx, ntok, out=out, out_gate=z, norm_weight=nw,
+               norm_eps=1e-6)
+    torch.cuda.synchronize()
+    outs, states = oracle_decode(x, before, idx, ntok)
+    zc, o_gpu = z.float().cpu().numpy(), out.float().cpu().numpy()
+    got = np.concatenate([o_gpu[r, : outs[r].shape[0]] for r in outs])
+    want = np.concatenate([oracle.gated_rmsnorm(outs[r], zc[r, : outs[r].shape[0]], nw.cpu().numpy(), 1e-6)
+                           for r in outs])
+    assert oracle.rel_l2(got, want) <= 5e-3
+    idx_h = idx.cpu().numpy()
+    s_gpu = np.stack([pool[int(idx_h[r])].cpu().numpy() for r in states])
+    assert oracle.rel_l2(s_gpu, np.stack([states[r] for r in states])) <= 5e-3

@@ -495,3 +495,78 @@ def test_bf16_states_fp32_d64(kda):
     eo = oracle.rel_l2(out.cpu().numpy().reshape(o_ref.shape), o_ref)
     es = oracle.rel_l2(fin.float().cpu().numpy(), s_ref)
     assert eo <= TOL["f32"] and es <= TOL["bf16"], f"rel-L2 out {eo:.3e} state {es:.3e}"
+
+
+# ------------------------------------------------ gated RMS norm output epilogue
+# Tolerance of the normalised output against the oracle.  The norm is scale-free per
+# (token, head) row, so its error is each row's relative error of o, and a whole-tensor
+# relative L2 then weights every row alike instead of by |o|^2: it tracks the row-RMS of
+# o's per-row relative error, which on these workloads is about twice o's magnitude-
+# weighted relative L2 (0.8-1.0e-2 against 4.0-4.2e-3).  Hence 2 x the 5e-3 budget of o.
+# The epilogue itself is held to 5e-3 against the exact norm of the kernel's own output.
+TOL_NORM = 1e-2
+
+
+def _norm_inputs(x, seed):
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    z = torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype)
+    w = 1.0 + 0.1 * torch.randn(x["v"].shape[-1], generator=gen, device="cuda")
+    return z, w
+
+
+@pytest.mark.parametrize("layout", ["varlen", "padded_eqlen"])
+@pytest.mark.parametrize("nseg", [1, 4])
+def test_output_norm_matches_oracle(kda, nseg, layout):
+    """out = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z) per (token, head), fused into
+    the pipelined kernel's output store, against the float64 oracle's o passed
+    through the float64 gated RMS norm."""
+    if layout == "varlen":
+        w = workloads.custom([700, 0, 64, 1, 300], H=2, D=128, seed=41)
+    else:
+        w = workloads.custom([200] * 3, H=2, D=128, dense=True, seed=41)
+    x = gen(w)
+    z, nw = _norm_inputs(x, 41)
+    say("output norm", layout, "nseg", nseg)
+    out, sT = run(kda, x, nseg=nseg, out_gate=z, norm_weight=nw, norm_eps=1e-6)
+    o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["g"].cpu(), x["beta"].cpu(),
+                                x["initial_state"].cpu(), None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu())
+    zz = z.float().cpu().numpy().reshape(o_ref.shape)
+    y_ref = oracle.gated_rmsnorm(o_ref, zz, nw.cpu().numpy(), 1e-6)
+    ey = oracle.rel_l2(out.float().cpu().numpy().reshape(y_ref.shape), y_ref)
+    es = oracle.rel_l2(sT.cpu().numpy(), s_ref)
+    assert ey <= TOL_NORM and es <= TOL["bf16"], f"rel-L2 out {ey:.3e} state {es:.3e}"
+    # the epilogue against the float64 norm of the same kernel's unnormalised output: they
+    # differ by two bf16 roundings (o before the norm, y after it)
+    o, _ = run(kda, x, nseg=nseg)
+    y_own = oracle.gated_rmsnorm(o.float().cpu().numpy().reshape(y_ref.shape), zz, nw.cpu().numpy(), 1e-6)
+    eo = oracle.rel_l2(out.float().cpu().numpy().reshape(y_ref.shape), y_own)
+    assert eo <= TOL["bf16"], f"epilogue vs the norm of the kernel's own output {eo:.3e}"
+
+
+def test_output_norm_fused_matches_unfused(kda):
+    """The fused epilogue against torch's gated RMS norm (float32) of the kernel's
+    own bf16 output: they differ by the rounding of o to bf16 before the norm."""
+    import torch
+    w = workloads.custom([300, 64, 45], H=2, D=128, seed=42)
+    x = gen(w)
+    z, nw = _norm_inputs(x, 42)
+    y1, _ = run(kda, x, out_gate=z, norm_weight=nw, norm_eps=1e-6)
+    o, _ = run(kda, x)
+    of = o.float()
+    y2 = of * torch.rsqrt(of.pow(2).mean(-1, keepdim=True) + 1e-6) * nw * torch.sigmoid(z.float())
+    d = ((y1.float() - y2).norm() / y2.norm()).item()
+    assert d <= TOL["bf16"], f"fused vs unfused {d:.2e}"
+
+
+@pytest.mark.parametrize("wave", list(range(8)))
+def test_output_norm_stalled_wave_gives_same_bits(kda, wave):
+    """The epilogue's per-token sums cross the 4 consumer waves through LDS: a wave
+    stalled after every barrier must not change a bit."""
+    w = workloads.custom([130, 1, 77, 64], H=2, D=128, seed=43)
+    x = gen(w)
+    z, nw = _norm_inputs(x, 43)
+    say("output norm stall wave", wave)
+    o0, s0 = run(kda, x, nseg=1, out_gate=z, norm_weight=nw)
+    o1, s1 = run(kda, x, nseg=1, out_gate=z, norm_weight=nw, stall_wave=wave, stall_cycles=127 * 6)
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)

@@ -364,3 +364,49 @@ def test_activation_pins_catch_planted_mistake(kind):
         return (f(gx) * (1.0 if kind == "no_bound" else lower_bound)), f(bx)
     with pytest.raises(AssertionError):
         _activation_closed_forms(bad)
+
+
+# ----------------------------------------------------------- gated RMSNorm epilogue (NEXT-4)
+def _gated_rmsnorm_pins(fn):
+    rng = np.random.default_rng(7)
+    o = rng.normal(size=(5, 3, 16))
+    z = rng.normal(size=(5, 3, 16))
+    w = rng.normal(size=16)
+    # a constant row c * 1 has mean square c^2: with eps = 0 the row maps to sign(c) * w * sigmoid(z)
+    c = np.full((2, 16), -3.0)
+    y = fn(c, np.zeros((2, 16)), np.ones(16), 0.0)
+    np.testing.assert_allclose(y, -0.5, rtol=1e-15)
+    # scale invariance at eps = 0
+    np.testing.assert_allclose(fn(7.5 * o, z, w, 0.0), fn(o, z, w, 0.0), rtol=1e-13)
+    # an open gate (z -> +inf) leaves the library RMS norm (torch, float64) times the weight
+    import torch
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(o), (16,), weight=torch.from_numpy(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(fn(o, np.full_like(z, 800.0), w, 1e-6), ref, rtol=1e-12, atol=1e-15)
+    # the gate is the logistic function: z = 0 halves the open-gate result
+    np.testing.assert_allclose(fn(o, np.zeros_like(z), w, 1e-6), 0.5 * ref, rtol=1e-12, atol=1e-15)
+
+
+def test_gated_rmsnorm_pins():
+    """Closed forms (a constant row; scale invariance), the library RMS norm
+    (torch.nn.functional.rms_norm in float64) for an open gate, and the logistic
+    gate at z = 0."""
+    _gated_rmsnorm_pins(oracle.gated_rmsnorm)
+
+
+@pytest.mark.parametrize("kind", ["mean_not_rms", "no_eps_inside_root", "gate_sign", "sum_not_mean"])
+def test_gated_rmsnorm_pins_catch_planted_mistake(kind):
+    def bad(o, z, w, eps):
+        o, z, w = (np.asarray(a, dtype=np.float64) for a in (o, z, w))
+        ms = np.mean(o * o, axis=-1, keepdims=True)
+        if kind == "mean_not_rms":
+            r = 1.0 / (np.abs(np.mean(o, axis=-1, keepdims=True)) + eps)
+        elif kind == "no_eps_inside_root":
+            r = 1.0 / (np.sqrt(ms) + eps)
+        elif kind == "sum_not_mean":
+            r = 1.0 / np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps)
+        else:
+            r = 1.0 / np.sqrt(ms + eps)
+        gate = 1.0 / (1.0 + np.exp(z if kind == "gate_sign" else -z))
+        return o * r * w * gate
+    with pytest.raises(AssertionError):
+        _gated_rmsnorm_pins(bad)
