@@ -114,6 +114,22 @@ def cpu_baseline(x, w, budget_s):
                       f"float64 C recurrence, {dt:.1f} s; tokens/s = token-heads / H / seconds"}
 
 
+def work_balance(w, cus=256, chunk=32):
+    """How evenly the single-segment plan loads the CUs: one workgroup runs each
+    (sequence, head) chain start to end, chunk after chunk, so the launch lasts as
+    long as the longest chain.  occupancy_bound = mean chunks per CU / chunks of the
+    longest chain is the fraction of the roofline that imbalance alone leaves."""
+    chunks = [-(-L // chunk) for L in w.lengths]
+    chains = w.n_seq * w.H
+    rounds = -(-chains // cus)
+    total = sum(chunks) * w.H
+    longest = max(chunks) if chunks else 0
+    per_cu = total / min(cus, chains) if chains else 0.0
+    return {"chains": chains, "chunk_tokens": chunk, "longest_chain_chunks": longest,
+            "mean_chunks_per_cu": per_cu,
+            "occupancy_bound": (per_cu / (longest * rounds)) if longest else None}
+
+
 def correctness_gate(kda, x, w, out, fin):
     import numpy as np
     import oracle
@@ -300,6 +316,7 @@ def main():
                    "algorithmic_bytes_per_launch": bytes_launch, "bytes_per_token_head": per_th,
                    "kernel_source_sha": source_sha("chunk_kernel")},
         "correctness": {"sampled_rel_l2_max": gate},
+        "work_balance": work_balance(w) if launches_per_step == 1 else None,
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, w, a.cpu_budget)
