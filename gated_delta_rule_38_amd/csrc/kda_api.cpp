@@ -262,6 +262,43 @@ kda_status_t check_out_norm(const kda_options_t *o, const kda_tensor_t *out, int
     return KDA_OK;
 }
 
+// ------------------------------------------------------------------ environment
+// KDA_LOG=1: every plan to stderr.  KDA_CHECK=1: cu_seqlens checked on the device before
+// anything else is launched (one small kernel, a stream sync and a 4-byte read back).
+bool env_on(const char *name)
+{
+    const char *v = getenv(name);
+    return v && *v && strcmp(v, "0") != 0;
+}
+
+std::mutex g_check_mu;
+std::vector<int32_t *> g_check_flag;   // per device, allocated on first use
+
+kda_status_t check_cu_device(const int32_t *cu, int64_t N, int64_t Ttot, hipStream_t st)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int32_t *flag = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_check_mu);
+        if ((int)g_check_flag.size() <= dev) g_check_flag.resize(dev + 1, nullptr);
+        if (!g_check_flag[dev] && (e = hipMalloc(&g_check_flag[dev], 256)) != hipSuccess) {
+            g_check_flag[dev] = nullptr;
+            return hip_fail(e, "cu_seqlens check buffer");
+        }
+        flag = g_check_flag[dev];
+    }
+    int32_t h = 1;
+    if ((e = kda::launch_check_cu(cu, (int32_t)N, Ttot, flag, st)) != hipSuccess) return hip_fail(e, "cu_seqlens check");
+    if ((e = hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess)
+        return hip_fail(e, "cu_seqlens check read-back");
+    if (h) return fail(KDA_ERR_SHAPE, "cu_seqlens is not an offset array (cu[0] == 0, non-decreasing, cu[N] == %lld)",
+                       (long long)Ttot);
+    return KDA_OK;
+}
+
 // ------------------------------------------------------------------ plan
 struct Plan {
     int nseg = 1;
@@ -334,6 +371,11 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
         off += align256((size_t)chains * pl.nseg * dd);
     }
     pl.bytes = off;
+    if (env_on("KDA_LOG"))
+        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d kernel=%s chunk=%d prep=%s workspace=%zu B\n",
+                (long long)P.N, (long long)P.H, (long long)P.D, P.dense ? "dense" : "packed", (long long)chains,
+                pl.nseg, pl.pipe ? "pipelined" : "single-role", pl.chunk, pl.standalone_prep ? "standalone" : "in-chunk",
+                pl.bytes);
     return KDA_OK;
 }
 
@@ -390,6 +432,10 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     const int64_t chains = P.N * P.H;
     if (chains == 0) return KDA_OK;
     char *wsb = (char *)ws;
+    if (P.tcu && env_on("KDA_CHECK")) {
+        kda_status_t s = check_cu_device((const int32_t *)P.tcu->data, P.N, P.Ttot, st);
+        if (s) return s;
+    }
 
     kda::ChunkParams cp{};
     cp.q = P.tq->data; cp.k = P.tk->data; cp.v = P.tv->data;
@@ -701,6 +747,10 @@ kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int
     pp.chunk = chunk;
     pp.chunks_per_seq = P.dense ? (int32_t)((P.T + chunk - 1) / chunk) : 0;
     if (P.N == 0 || (P.dense && P.T == 0)) return KDA_OK;
+    if (cu_seqlens && env_on("KDA_CHECK")) {
+        kda_status_t s = check_cu_device(pp.cu, P.N, P.Ttot, (hipStream_t)stream);
+        if (s) return s;
+    }
     const int64_t nvc = P.dense ? P.B * pp.chunks_per_seq : (P.Ttot + chunk - 1) / chunk + P.N;
     hipError_t e = timed("kda_prep", (hipStream_t)stream, [&] { return kda::launch_prep(pp, (int)nvc, (hipStream_t)stream); });
     return e == hipSuccess ? KDA_OK : hip_fail(e, "PREP launch");

@@ -8,6 +8,8 @@ namespace kda {
 hipError_t launch_chunk(const ChunkParams &p, int D, bool fp32, int grid, bool stall, hipStream_t st);
 // Pipelined CHUNK kernel (d = 128, bf16, 32-token chunks), one 512-thread workgroup per chain / segment.
 hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStream_t st);
+// Debug-mode check of cu_seqlens: *flag = 0 when cu[0] == 0, cu non-decreasing, cu[N] == Ttot.
+hipError_t launch_check_cu(const int32_t *cu, int32_t N, int64_t Ttot, int32_t *flag, hipStream_t st);
 // PREP kernel over `nvc` virtual chunks x H heads.
 hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st);
 // COMBINE kernel over chains x D/16 value slabs.

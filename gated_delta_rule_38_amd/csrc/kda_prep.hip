@@ -65,6 +65,23 @@ __global__ __launch_bounds__(128) void prep_kernel(const PrepParams p)
     }
 }
 
+// cu_seqlens check (the debug mode): flag = 1 unless cu[0] == 0, cu is non-decreasing and
+// cu[N] == T_tot.  One workgroup; every thread folds a strided share, then one OR across it.
+__global__ __launch_bounds__(256) void check_cu_kernel(const int32_t *cu, int32_t N, int64_t Ttot, int32_t *flag)
+{
+    int bad = 0;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) bad |= cu[i] > cu[i + 1];
+    if (threadIdx.x == 0) bad |= (cu[0] != 0) | ((int64_t)cu[N] != Ttot);
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *flag = bad;
+}
+
+hipError_t launch_check_cu(const int32_t *cu, int32_t N, int64_t Ttot, int32_t *flag, hipStream_t st)
+{
+    hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, st, cu, N, Ttot, flag);
+    return hipGetLastError();
+}
+
 hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st)
 {
     if (nvc <= 0 || p.H <= 0) return hipSuccess;

@@ -47,6 +47,15 @@
  *
  * Asynchrony: calls enqueue on `stream` (a hipStream_t; NULL is the null
  * stream) and return without synchronising or reading device data back.
+ *
+ * Environment (read on every call):
+ *   KDA_CHECK=1  checks cu_seqlens on the device before anything else is enqueued
+ *                (cu[0] == 0, non-decreasing, cu[N] == T_tot): one small kernel, a
+ *                synchronisation of `stream` and a 4-byte read back; an invalid array
+ *                returns KDA_ERR_SHAPE with nothing further launched.  Without it a
+ *                cu_seqlens whose last offset exceeds the token extent makes the kernels
+ *                read past the inputs.
+ *   KDA_LOG=1    prints every plan (layout, chains, segments, kernel, workspace) to stderr.
  */
 #ifndef KDA_H
 #define KDA_H

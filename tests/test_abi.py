@@ -350,3 +350,27 @@ def test_output_norm_options_validated(lib):
     assert size(z(base=FAKE + 7 * gap), w()) == 5          # out_gate is out
     assert size(z(base=FAKE + 10 * gap + 2), w()) == 4     # misaligned rows
     assert size(z(), w(), variant=1) == 6                   # single-role kernel: unsupported
+
+
+def test_plan_log(tmp_path):
+    """KDA_LOG=1 prints each plan to stderr (the planner runs on the host: a
+    workspace-size query shows it without a GPU)."""
+    import subprocess, sys, textwrap
+    code = textwrap.dedent(f"""
+        import ctypes, sys
+        sys.path.insert(0, {ROOT!r}); sys.path.insert(0, {os.path.join(ROOT, 'tests')!r})
+        import test_abi as t
+        import gated_delta_rule_38_amd as kda
+        lib = kda.load_library()
+        s = t.packed_set(T=4096, H=2, N=2)
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        n = ctypes.c_size_t(0)
+        st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                            None, ctypes.byref(n))
+        print("status", st, n.value)
+    """)
+    env = dict(os.environ, KDA_LOG="1")
+    p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stderr[-2000:]
+    assert "status 0" in p.stdout
+    assert "kda: plan N=2 H=2 D=128 packed chains=4 nseg=" in p.stderr and "kernel=pipelined" in p.stderr

@@ -570,3 +570,33 @@ def test_output_norm_stalled_wave_gives_same_bits(kda, wave):
     o0, s0 = run(kda, x, nseg=1, out_gate=z, norm_weight=nw)
     o1, s1 = run(kda, x, nseg=1, out_gate=z, norm_weight=nw, stall_wave=wave, stall_cycles=127 * 6)
     assert torch_equal(o0, o1) and torch_equal(s0, s1)
+
+
+# ------------------------------------------------ KDA_CHECK (device check of cu_seqlens)
+def test_check_rejects_bad_cu_seqlens(kda, monkeypatch):
+    """With KDA_CHECK=1 an offset array that runs past the tokens, or goes backwards, is
+    refused before any prefill kernel runs (outputs untouched); a valid one gives the
+    bits of an unchecked call.  The bad arrays only ever reach the device check."""
+    import torch
+    w = workloads.custom([100, 50, 30], H=2, D=128, seed=60)
+    x = gen(w)
+    o_ref, s_ref = run(kda, x)
+    monkeypatch.setenv("KDA_CHECK", "1")
+    o_chk, s_chk = run(kda, x)
+    assert torch_equal(o_ref, o_chk) and torch_equal(s_ref, s_chk)
+    for kind in ("past_end", "backwards", "nonzero_start"):
+        bad = x["cu_seqlens"].clone()
+        if kind == "past_end":
+            bad[-1] += 7
+        elif kind == "backwards":
+            bad[1], bad[2] = bad[2].clone(), bad[1].clone()
+        else:
+            bad[0] = 1
+        out = torch.full_like(x["v"], -512.0)
+        say("KDA_CHECK", kind)
+        with pytest.raises(kda.KdaError) as e:
+            kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], bad, out=out)
+        assert e.value.status == 2 and "cu_seqlens" in str(e.value)
+        assert torch.all(out.float() == -512.0)
+        with pytest.raises(kda.KdaError):
+            kda.prep(x["g"], bad, chunk=32)
