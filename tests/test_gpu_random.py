@@ -1,0 +1,101 @@
+"""Seeded random configurations of the prefill against the float64 oracle.
+
+Each case draws a batch layout (dense or packed, with empty and ragged sequences),
+a head count, the head size and I/O dtype (d = 128 bf16 or the d = 64 fp32 debug
+mode), a segment count (the planner's or forced), the kernel variant, the state
+dtypes (fp32 or bf16), logit inputs and, on the pipelined kernel, the gated RMS
+norm epilogue — and checks every output and final state with the tolerances of
+the other parity tests.  The cases are drawn once, from a fixed seed, so the set
+is the same on every run.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 5e-3, "f32": 1e-4}
+TOL_NORM = 1e-2        # the gated RMS norm output: see the epilogue tests for the derivation
+
+
+def _draw(i):
+    rng = np.random.default_rng(1000 + i)
+    fp32 = rng.random() < 0.25
+    D = 64 if fp32 else 128
+    dense = rng.random() < 0.3
+    n = int(rng.integers(1, 6))
+    if dense:
+        L = int(rng.integers(1, 700))
+        lengths = [L] * n
+    else:
+        lengths = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 900, n)]
+    H = int(rng.integers(1, 4))
+    variant = 1 if fp32 else int(rng.choice([0, 0, 1, 2]))
+    nseg = int(rng.choice([0, 0, 1, 2, 3, 5]))
+    pipelined = not fp32 and variant != 1
+    return dict(case=i, fp32=fp32, D=D, dense=dense, lengths=lengths, H=H, variant=variant, nseg=nseg,
+                zero_state=bool(rng.random() < 0.2), bf16_state=bool(rng.random() < 0.3),
+                logits=bool(rng.random() < 0.3), norm=bool(pipelined and rng.random() < 0.3),
+                gate=str(rng.choice(["none", "none", "none", "mild", "floor"])))
+
+
+CASES = [_draw(i) for i in range(24)]
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_38_amd as k
+    k.load_library()
+    return k
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"case{c['case']}" for c in CASES])
+def test_random_configuration(kda, c):
+    import torch
+    print("[case]", c, file=sys.stderr, flush=True)
+    w = workloads.custom(c["lengths"], H=c["H"], D=c["D"], dtype="f32" if c["fp32"] else "bf16", dense=c["dense"],
+                         zero_state=c["zero_state"], seed=2000 + c["case"])
+    gate = None if c["gate"] == "none" else c["gate"]
+    x = workloads.make_inputs(w, device="cuda", gate=gate)
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    s0 = x["initial_state"]
+    if s0 is not None and c["bf16_state"]:
+        s0 = s0.to(torch.bfloat16)
+    N = len(c["lengths"])
+    fin = torch.empty((N, c["H"], c["D"], c["D"]), device="cuda",
+                      dtype=torch.bfloat16 if c["bf16_state"] else torch.float32)
+    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    z = nw = None
+    if c["norm"]:
+        gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
+        z = torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype)
+        nw = 1.0 + 0.1 * torch.randn(c["D"], generator=gen, device="cuda")
+        kw.update(out_gate=z, norm_weight=nw, norm_eps=1e-6)
+    out, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], final_state=fin, **kw)
+    torch.cuda.synchronize()
+    if logits:
+        g64, b64 = oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), -5.0)
+    else:
+        g64, b64 = x["g"].cpu(), x["beta"].cpu()
+    o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), g64, b64,
+                                None if s0 is None else s0.float().cpu(),
+                                None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu())
+    tol = TOL["f32"] if c["fp32"] else TOL["bf16"]
+    if c["norm"]:
+        o_ref = oracle.gated_rmsnorm(o_ref, z.float().cpu().numpy().reshape(o_ref.shape), nw.cpu().numpy(), 1e-6)
+        tol = TOL_NORM
+    o_gpu = out.float().cpu().numpy().reshape(o_ref.shape)
+    s_gpu = fin.float().cpu().numpy()
+    assert np.isfinite(o_gpu).all() and np.isfinite(s_gpu).all()
+    eo = oracle.rel_l2(o_gpu, o_ref) if o_ref.size and np.abs(o_ref).sum() > 0 else 0.0
+    es = oracle.rel_l2(s_gpu, s_ref) if np.abs(s_ref).sum() > 0 else float(np.abs(s_gpu).max())
+    tol_s = TOL["bf16"] if (c["bf16_state"] or not c["fp32"]) else TOL["f32"]
+    assert eo <= tol and es <= tol_s, f"rel-L2 out {eo:.3e} state {es:.3e}"
