@@ -252,8 +252,10 @@ def test_dense_equals_packed(kda):
 
 
 @pytest.mark.parametrize("variant", [1, 2])
-@pytest.mark.parametrize("nseg", [1, 2, 4, 8])
+@pytest.mark.parametrize("nseg", [1, 2, 4, 8, 64])
 def test_forced_segments_match_oracle(kda, nseg, variant):
+    """Forced segment counts up to the maximum (64): chains shorter than nseg chunks get
+    empty segments, whose maps are the identity (M = I, C = 0)."""
     w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=12)
     x = gen(w)
     say("nseg", nseg, "variant", variant)
