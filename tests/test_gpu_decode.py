@@ -249,3 +249,48 @@ def test_decode_output_norm(kda, D):
     idx_h = idx.cpu().numpy()
     s_gpu = np.stack([pool[int(idx_h[r])].cpu().numpy() for r in states])
     assert oracle.rel_l2(s_gpu, np.stack([states[r] for r in states])) <= 5e-3
+
+
+def test_decode_graph_replay(kda):
+    """kda_decode captured in a HIP graph (one launch, nothing allocated): q changes
+    between replays and each replay of the verify pass equals a fresh eager call bit
+    for bit; a committing replay advances the pool exactly as an eager call does."""
+    import torch
+    x, pool, idx, ntok = make_case(R=6, T=4, H=2, D=128, dtype="bf16", pool_dtype="f32", seed=58)
+    qbuf = x["q"].clone()
+    out = torch.full_like(x["v"], -512.0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.decode(qbuf, x["k"], x["v"], x["g"], x["beta"], pool, idx, ntok, out=out, update_state=False)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.decode(qbuf, x["k"], x["v"], x["g"], x["beta"], pool, idx, ntok, out=out, update_state=False)
+    gen_ = torch.Generator(device="cuda")
+    for rep in range(4):
+        gen_.manual_seed(200 + rep)
+        newq = torch.randn(qbuf.shape, generator=gen_, device="cuda")
+        qbuf.copy_((newq / newq.norm(dim=-1, keepdim=True)).to(qbuf.dtype))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = torch.full_like(x["v"], -512.0)
+        kda.decode(qbuf.clone(), x["k"], x["v"], x["g"], x["beta"], pool, idx, ntok, out=ref, update_state=False)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+    # a committing graph: two replays advance the pool as two eager calls do
+    p_graph, p_eager = pool.clone(), pool.clone()
+    o_g = torch.empty_like(x["v"])
+    with torch.cuda.stream(s):
+        kda.decode(qbuf, x["k"], x["v"], x["g"], x["beta"], p_graph.clone(), idx, ntok, out=o_g)
+    torch.cuda.current_stream().wait_stream(s)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        kda.decode(qbuf, x["k"], x["v"], x["g"], x["beta"], p_graph, idx, ntok, out=o_g)
+    for _ in range(2):
+        g2.replay()
+        torch.cuda.synchronize()
+        o_e = torch.empty_like(x["v"])
+        kda.decode(qbuf, x["k"], x["v"], x["g"], x["beta"], p_eager, idx, ntok, out=o_e)
+        torch.cuda.synchronize()
+        assert torch.equal(p_graph, p_eager)
