@@ -527,8 +527,13 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
 }
 
 // cached workspace of kda_prefill, per device
+// kda_prefill's workspace cache: one buffer per (device, stream), so calls on different
+// streams never share memory, and a buffer is only replaced after its own stream has
+// finished with it.
 std::mutex g_ws_mu;
 struct CachedWs {
+    int dev = 0;
+    void *stream = nullptr;
     void *p = nullptr;
     size_t bytes = 0;
 };
@@ -582,8 +587,14 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
         std::lock_guard<std::mutex> lk(g_ws_mu);
-        if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-        CachedWs &c = g_ws[dev];
+        CachedWs *cp = nullptr;
+        for (CachedWs &x : g_ws)
+            if (x.dev == dev && x.stream == stream) cp = &x;
+        if (!cp) {
+            g_ws.push_back(CachedWs{dev, stream, nullptr, 0});
+            cp = &g_ws.back();
+        }
+        CachedWs &c = *cp;
         if (c.bytes < pl.bytes) {
             if (c.p) {
                 if ((e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess) return hip_fail(e, "workspace sync");
@@ -761,13 +772,13 @@ void kda_release_cached_workspace(void)
     std::lock_guard<std::mutex> lk(g_ws_mu);
     int cur = 0;
     (void)hipGetDevice(&cur);
-    for (size_t d = 0; d < g_ws.size(); ++d) {
-        if (!g_ws[d].p) continue;
-        (void)hipSetDevice((int)d);
+    for (CachedWs &c : g_ws) {
+        if (!c.p) continue;
+        (void)hipSetDevice(c.dev);
         (void)hipDeviceSynchronize();
-        (void)hipFree(g_ws[d].p);
-        g_ws[d] = CachedWs{};
+        (void)hipFree(c.p);
     }
+    g_ws.clear();
     (void)hipSetDevice(cur);
 }
 

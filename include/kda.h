@@ -128,9 +128,11 @@ typedef struct {
  * q, k, v, g, beta: inputs as above.  initial_state: NULL for zeros.
  * cu_seqlens: NULL for the dense layout.  out: written for every valid token.
  * final_state: NULL to skip.  stream: hipStream_t.
- * Uses (and grows on demand) a per-device workspace cached by the library; the
- * first call for a new size may call hipMalloc, so this entry point is not
- * meant for graph capture -- use kda_prefill_ws there.
+ * Uses (and grows on demand) a workspace cached by the library per (device,
+ * stream), so calls on different streams never share it; the first call for a
+ * new size may call hipMalloc (after synchronising that stream when it replaces
+ * a smaller buffer), so this entry point is not meant for graph capture -- use
+ * kda_prefill_ws there.
  */
 kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
                          const kda_tensor_t *g, const kda_tensor_t *beta,
@@ -205,7 +207,8 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
                         kda_tensor_t *out, int32_t update_state, const kda_options_t *opts,
                         void *stream);
 
-/* Frees the workspace cached by kda_prefill on every device. */
+/* Frees the workspaces cached by kda_prefill on every device and stream (synchronising
+ * each device first). */
 void kda_release_cached_workspace(void);
 
 /* Kernel timing for measurement: when enabled, every kernel the library

@@ -602,3 +602,26 @@ def test_check_rejects_bad_cu_seqlens(kda, monkeypatch):
         assert torch.all(out.float() == -512.0)
         with pytest.raises(kda.KdaError):
             kda.prep(x["g"], bad, chunk=32)
+
+
+def test_cached_workspace_per_stream(kda):
+    """Plain kda_prefill calls on two streams at once, both on the segmented path (so
+    both need the library's cached workspace), give the bits of the same calls made
+    one after the other: each stream has a workspace of its own."""
+    import torch
+    xs = [gen(workloads.custom([600, 200], H=2, D=128, seed=70 + i)) for i in range(2)]
+    refs = []
+    for x in xs:
+        refs.append(run(kda, x))
+        torch.cuda.synchronize()
+    kda.release_cached_workspace()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    res = [None, None]
+    for rep in range(3):
+        for i, (x, s) in enumerate(zip(xs, streams)):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                res[i] = run(kda, x)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch_equal(res[i][0], refs[i][0]) and torch_equal(res[i][1], refs[i][1]), f"rep {rep} stream {i}"
