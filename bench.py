@@ -4,7 +4,13 @@
     python bench.py --config decode|decode_bf16|verify4        (the recurrent decode kernel)
 
 One step is one kda_prefill call over the whole workload (every kernel of the
-hot path), with inputs already resident in HBM.  Prints ONE JSON line:
+hot path), with inputs already resident in HBM; `value` is the back-to-back
+("pipelined") rate, and `timing_modes` adds per-call (synchronised, host
+dispatch included) and HIP-graph times.  The correctness gate runs the oracle
+on the host while the GPU idles; afterwards the step runs untimed for at least
+0.2 s (`settle`) so that the GPU is back in its steady state before the W
+warm-up steps and the K timed steps (with only a few steps of warm-up, the
+first milliseconds after the idle ran ~13% slower on the varlen workload).  Prints ONE JSON line:
 throughput in tokens/s, the roofline of the dominant kernel (its duration from
 HIP events recorded by the library on the launch stream over the timed region),
 and the float64 oracle timed on the host cores on a bounded sample of the same
@@ -195,6 +201,7 @@ def decode_main(a, w):
     if not max(eo, es) <= 5e-3:
         raise SystemExit(f"correctness gate failed: rel-L2 out {eo:.3e} state {es:.3e}")
     pool = x["pool"]
+    settle(lambda: step(pool))
     for _ in range(a.warmup):
         step(pool)
     torch.cuda.synchronize()
@@ -230,11 +237,58 @@ def decode_main(a, w):
     print(json.dumps(rec))
 
 
+def timing_modes(kda, x, w, out, fin, calls=8, reps=5):
+    """The other two timing modes the cudnn-frontend KDA PR quotes beside the
+    back-to-back one: per call (each call synchronised, host dispatch included) and a
+    HIP graph of `calls` kda_prefill_ws launches replayed as one.  Medians in ms."""
+    import statistics
+    import torch
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
+    per_call = []
+    for _ in range(calls * reps):
+        t = time.perf_counter()
+        kda.prefill(*args, out=out, final_state=fin)
+        torch.cuda.synchronize()
+        per_call.append((time.perf_counter() - t) * 1e3)
+    ws_bytes = kda.workspace_size(*args, out=out, final_state=fin)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=out.device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.prefill(*args, out=out, final_state=fin, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            kda.prefill(*args, out=out, final_state=fin, workspace=ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    per_graph = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_graph.append(e0.elapsed_time(e1) / calls)
+    return {"per_call_ms": statistics.median(per_call), "graph_ms": statistics.median(per_graph),
+            "graph_calls": calls}
+
+
+def settle(step, seconds=0.2):
+    """Untimed steps for at least `seconds` of wall time (GPU back to steady state)."""
+    import torch
+    t = time.perf_counter()
+    while time.perf_counter() - t < seconds:
+        step()
+        torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="varlen")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,6 +330,7 @@ def main():
     step()
     torch.cuda.synchronize()
     gate = correctness_gate(kda, x, w, out, fin)
+    settle(step)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -317,6 +372,7 @@ def main():
                    "kernel_source_sha": source_sha("chunk_kernel")},
         "correctness": {"sampled_rel_l2_max": gate},
         "work_balance": work_balance(w) if launches_per_step == 1 else None,
+        "timing_modes": dict(timing_modes(kda, x, w, out, fin), pipelined_ms=ms_step),
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, w, a.cpu_budget)
