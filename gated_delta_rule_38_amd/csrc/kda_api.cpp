@@ -598,9 +598,10 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
         if (c.bytes < pl.bytes) {
             if (c.p) {
                 if ((e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess) return hip_fail(e, "workspace sync");
-                hipFree(c.p);
+                e = hipFree(c.p);
                 c.p = nullptr;
                 c.bytes = 0;
+                if (e != hipSuccess) return hip_fail(e, "workspace free");
             }
             if ((e = hipMalloc(&c.p, pl.bytes)) != hipSuccess) {
                 c.p = nullptr;

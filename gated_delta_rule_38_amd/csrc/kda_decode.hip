@@ -37,8 +37,21 @@ __device__ __forceinline__ void ld4(const float *p, float (&x)[4])
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
 __device__ __forceinline__ void ld4(const bf16 *p, float (&x)[4]) { Vec4<bf16>::unpack(Vec4<bf16>::load(p), x); }
-__device__ __forceinline__ void st4(float *p, const float (&x)[4]) { *(float4 *)p = make_float4(x[0], x[1], x[2], x[3]); }
-__device__ __forceinline__ void st4(bf16 *p, const float (&x)[4]) { Vec4<bf16>::store(p, Vec4<bf16>::pack(x)); }   // RNE
+// State and output rows are written once per launch and not read back by it: non-temporal
+// stores (on the fp32 pool 19% faster than plain stores in an A/B on MI355X; no change on the
+// bf16 pool).
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st4(float *p, const float (&x)[4])
+{
+    const f32x4 v = {x[0], x[1], x[2], x[3]};
+    __builtin_nontemporal_store(v, (f32x4 *)p);
+}
+__device__ __forceinline__ void st4(bf16 *p, const float (&x)[4])    // RNE
+{
+    const uint2 u = Vec4<bf16>::pack(x);
+    const u32x2 w = {u.x, u.y};
+    __builtin_nontemporal_store(w, (u32x2 *)p);
+}
 
 // STALL: the test build with one wave stalled after every barrier (the results must not change).
 template <int D, typename IT, typename ST, bool STALL>
@@ -59,6 +72,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
     const IT *k = (const IT *)p.k + r * p.k_sr + h * p.k_sh;
     const IT *v = (const IT *)p.v + r * p.v_sr + h * p.v_sh;
     const float *g = p.g + r * p.g_sr + h * p.g_sh;
+    // the state rows are requested before the tokens are staged, so that both loads are in
+    // flight together (one memory round trip per workgroup, not two)
+    ST *ps = (ST *)p.pool + slot * p.p_sn + h * p.p_sh + (int64_t)(rg * RPG) * p.p_sr + 4 * cq;
+    float s[RPG][4];
+#pragma unroll
+    for (int j = 0; j < RPG; ++j) ld4(ps + j * p.p_sr, s[j]);
     for (int e = tid; e < n * D; e += 256) {
         const int t = e / D, ch = e % D;
         sK[t][ch] = ld(k + t * p.k_st + ch);
@@ -71,10 +90,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p)
         const float b = p.beta[r * p.b_sr + tid * p.b_st + h * p.b_sh];
         sB[tid] = p.beta_act ? sigmoid_act(b) : b;
     }
-    ST *ps = (ST *)p.pool + slot * p.p_sn + h * p.p_sh + (int64_t)(rg * RPG) * p.p_sr + 4 * cq;
-    float s[RPG][4];
-#pragma unroll
-    for (int j = 0; j < RPG; ++j) ld4(ps + j * p.p_sr, s[j]);
     auto sync = [&]() {
         __syncthreads();
         if constexpr (STALL) {
