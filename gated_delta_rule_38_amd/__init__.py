@@ -92,22 +92,23 @@ def _check(status: int) -> None:
         raise KdaError(status, load_library().kda_last_error().decode())
 
 
+_DTYPE_CODES = None
+_I64x4 = ctypes.c_int64 * 4
+
+
 def describe(t, dtype_code: Optional[int] = None) -> KdaTensor:
     """A torch tensor as a kda_tensor_t (strides in elements)."""
-    import torch
-    d = KdaTensor()
-    if t.dim() > 4:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32, torch.int32: KDA_I32}
+    n = t.dim()
+    if n > 4:
         raise ValueError("at most 4 dimensions")
-    code = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32, torch.int32: KDA_I32}.get(t.dtype)
-    d.data = t.data_ptr() if t.numel() > 0 else None
-    d.dtype = code if dtype_code is None else dtype_code
-    if d.dtype is None:
-        d.dtype = -1
-    d.ndim = t.dim()
-    for i in range(t.dim()):
-        d.shape[i] = t.shape[i]
-        d.stride[i] = t.stride(i)
-    return d
+    code = _DTYPE_CODES.get(t.dtype, -1) if dtype_code is None else dtype_code
+    pad = (0,) * (4 - n)
+    return KdaTensor(t.data_ptr() if t.numel() > 0 else None, code, n,
+                     _I64x4(*t.shape, *pad), _I64x4(*t.stride(), *pad))
 
 
 def _ptr(d: Optional[KdaTensor]):
