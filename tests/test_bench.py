@@ -1,0 +1,92 @@
+"""Host-side logic of bench.py: the algorithmic byte counts behind the roofline
+figures (counted here from the tensors the workloads actually build), the CU
+load balance of the single-segment plan (by simulating the schedule), the
+staleness rule for committed traffic figures, and the one-GPU refusal."""
+import json
+import math
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+@pytest.mark.parametrize("w", [
+    workloads.custom([5, 70, 33], H=3, D=128, seed=1),
+    workloads.custom([40, 40], H=2, D=64, dtype="f32", dense=True, seed=2),
+])
+def test_algorithmic_bytes_are_the_tensors_bytes(w):
+    """Inputs read once (q, k, v, g, beta, initial state) and outputs written once
+    (out shaped like v, final state shaped like the initial state)."""
+    x = workloads.make_inputs(w)
+    read = sum(_nbytes(x[n]) for n in ("q", "k", "v", "g", "beta", "initial_state"))
+    written = _nbytes(x["v"]) + _nbytes(x["initial_state"])
+    bytes_, _, per_th = bench.algorithmic(w)
+    assert bytes_ == read + written
+    assert per_th * w.tokens * w.H + 2 * _nbytes(x["initial_state"]) == bytes_
+
+
+def test_decode_algorithmic_bytes_are_the_tensors_bytes():
+    w = workloads.DecodeWorkload("t", R=5, T=3, H=2, D=64, pool_dtype="bf16", P=9)
+    x = workloads.make_decode_inputs(w)
+    slot_bytes = _nbytes(x["pool"]) // w.P
+    read = sum(_nbytes(x[n]) for n in ("q", "k", "v", "g", "beta", "idx")) + w.R * slot_bytes
+    written = _nbytes(x["v"]) + w.R * slot_bytes
+    assert bench.decode_algorithmic(w)[0] == read + written
+
+
+def _simulate(lengths, H, cus, chunk):
+    """Chains start in launch order on the first free CU and run to the end."""
+    free = [0] * cus
+    for L in lengths:
+        for _ in range(H):
+            i = min(range(cus), key=lambda c: free[c])
+            free[i] += math.ceil(L / chunk)
+    busy = [f for f in free if f]
+    return max(free), sum(busy) / len(busy)
+
+
+@pytest.mark.parametrize("name", ["varlen", "varlen_padded", "large", "long"])
+def test_work_balance_matches_a_simulated_schedule(name):
+    w = workloads.WORKLOADS[name]
+    wb = bench.work_balance(w)
+    makespan, mean_busy = _simulate(w.lengths, w.H, 256, 32)
+    rounds = math.ceil(w.n_seq * w.H / 256)
+    assert wb["chains"] == w.n_seq * w.H
+    assert wb["longest_chain_chunks"] * rounds == makespan
+    assert wb["mean_chunks_per_cu"] == pytest.approx(mean_busy)
+    assert wb["occupancy_bound"] == pytest.approx(mean_busy / makespan)
+
+
+def test_varlen_balance_figures():
+    wb = bench.work_balance(workloads.WORKLOADS["varlen"])
+    assert (wb["chains"], wb["longest_chain_chunks"]) == (256, 221)
+    assert wb["occupancy_bound"] == pytest.approx(1027 * 32 / 256 / 221)
+
+
+def test_traffic_figure_is_dropped_when_the_kernel_source_changes(monkeypatch):
+    for kernel, config in (("chunk_kernel", "varlen"), ("decode_kernel", "decode")):
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")))
+        assert rec["kernel"] in ("chunk_pipe_kernel", "decode_kernel")
+        if rec["kernel_source_sha"] == bench.source_sha(kernel):
+            assert bench.traffic_from_profile(config, kernel) == rec["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench, "source_sha", lambda kernel="chunk_kernel": "0" * 16)
+    assert bench.traffic_from_profile("varlen") is None
+    assert bench.traffic_from_profile("no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
