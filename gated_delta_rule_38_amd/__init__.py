@@ -271,7 +271,8 @@ def profile_enable(on: bool = True) -> None:
 
 def profile_read(kernel: Optional[str] = None) -> Tuple[float, int]:
     """(summed milliseconds, launches) of the library's kernels whose name
-    contains ``kernel`` since the last read; synchronises their events."""
+    contains ``kernel`` (None: all) since the last read; synchronises their
+    events.  Every read clears all recorded launches, counted or not."""
     ms = ctypes.c_double(0.0)
     n = ctypes.c_int64(0)
     _check(load_library().kda_profile_read(kernel.encode() if kernel else None, ctypes.byref(ms), ctypes.byref(n)))

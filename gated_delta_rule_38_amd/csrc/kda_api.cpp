@@ -271,7 +271,7 @@ bool env_on(const char *name)
     return v && *v && strcmp(v, "0") != 0;
 }
 
-std::mutex g_check_mu;
+std::mutex g_check_mu;                 // held for a whole check: one flag per device
 std::vector<int32_t *> g_check_flag;   // per device, allocated on first use
 
 kda_status_t check_cu_device(const int32_t *cu, int64_t N, int64_t Ttot, hipStream_t st)
@@ -279,16 +279,15 @@ kda_status_t check_cu_device(const int32_t *cu, int64_t N, int64_t Ttot, hipStre
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    int32_t *flag = nullptr;
-    {
-        std::lock_guard<std::mutex> lk(g_check_mu);
-        if ((int)g_check_flag.size() <= dev) g_check_flag.resize(dev + 1, nullptr);
-        if (!g_check_flag[dev] && (e = hipMalloc(&g_check_flag[dev], 256)) != hipSuccess) {
-            g_check_flag[dev] = nullptr;
-            return hip_fail(e, "cu_seqlens check buffer");
-        }
-        flag = g_check_flag[dev];
+    // the lock covers the launch and the read-back, so that checks on other streams of the
+    // device never write the flag in between
+    std::lock_guard<std::mutex> lk(g_check_mu);
+    if ((int)g_check_flag.size() <= dev) g_check_flag.resize(dev + 1, nullptr);
+    if (!g_check_flag[dev] && (e = hipMalloc(&g_check_flag[dev], 256)) != hipSuccess) {
+        g_check_flag[dev] = nullptr;
+        return hip_fail(e, "cu_seqlens check buffer");
     }
+    int32_t *flag = g_check_flag[dev];
     int32_t h = 1;
     if ((e = kda::launch_check_cu(cu, (int32_t)N, Ttot, flag, st)) != hipSuccess) return hip_fail(e, "cu_seqlens check");
     if ((e = hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, st)) != hipSuccess ||
@@ -526,10 +525,10 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     return KDA_OK;
 }
 
-// cached workspace of kda_prefill, per device
 // kda_prefill's workspace cache: one buffer per (device, stream), so calls on different
 // streams never share memory, and a buffer is only replaced after its own stream has
-// finished with it.
+// finished with it.  The lock is held until the call has enqueued its kernels: a call
+// from another thread on the same stream that grows the buffer then waits for them.
 std::mutex g_ws_mu;
 struct CachedWs {
     int dev = 0;
@@ -581,8 +580,8 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
     if (st) return st;
     Plan pl;
     if ((st = make_plan(P, nullptr, pl))) return st;
-    void *ws = nullptr;
-    if (pl.bytes) {
+    if (pl.bytes == 0) return run(P, pl, nullptr, nullptr, 0, (hipStream_t)stream);
+    {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -609,9 +608,8 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
             }
             c.bytes = pl.bytes;
         }
-        ws = c.p;
+        return run(P, pl, nullptr, c.p, pl.bytes, (hipStream_t)stream);
     }
-    return run(P, pl, nullptr, ws, pl.bytes, (hipStream_t)stream);
 }
 
 kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v, const kda_tensor_t *g,

@@ -132,7 +132,8 @@ typedef struct {
  * stream), so calls on different streams never share it; the first call for a
  * new size may call hipMalloc (after synchronising that stream when it replaces
  * a smaller buffer), so this entry point is not meant for graph capture -- use
- * kda_prefill_ws there.
+ * kda_prefill_ws there.  Calls from several host threads are safe: the cache
+ * stays locked until a call has enqueued its kernels.
  */
 kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
                          const kda_tensor_t *g, const kda_tensor_t *beta,
@@ -213,8 +214,9 @@ void kda_release_cached_workspace(void);
 
 /* Kernel timing for measurement: when enabled, every kernel the library
  * enqueues is bracketed by hipEvents on its stream.  kda_profile_read()
- * synchronises those events, returns the summed milliseconds and launch count
- * of kernels whose name contains `kernel` (e.g. "chunk"), and clears them.
+ * synchronises those events and returns the summed milliseconds and launch
+ * count of the kernels whose name contains `kernel` (e.g. "chunk"; NULL: all).
+ * Every read clears all recorded launches, the ones it did not count included.
  * Enabling creates a pool of events on the current device (reused across
  * reads), so timed launches create none; call it with that device current. */
 void kda_profile_enable(int on);

@@ -625,3 +625,43 @@ def test_cached_workspace_per_stream(kda):
         torch.cuda.synchronize()
         for i in range(2):
             assert torch_equal(res[i][0], refs[i][0]) and torch_equal(res[i][1], refs[i][1]), f"rep {rep} stream {i}"
+
+
+def test_cached_workspace_threads(kda):
+    """Two host threads calling plain kda_prefill on one stream, with workspace needs
+    that grow and shrink from call to call (segment counts 2 to 18), give the bits of
+    the same calls made from one thread: a call that replaces the cached buffer waits
+    until the other thread's call has enqueued its kernels."""
+    import threading
+    import torch
+    lens = [[600, 200], [1200, 100], [2400, 50], [4800, 10]]
+    xs = [gen(workloads.custom(L, H=2, D=128, seed=80 + i)) for i, L in enumerate(lens)]
+    refs = []
+    for x in xs:
+        refs.append(run(kda, x))
+    torch.cuda.synchronize()
+    kda.release_cached_workspace()
+    results = {0: [], 1: []}
+    errors = []
+
+    def worker(tid):
+        try:
+            order = list(range(len(xs))) if tid == 0 else list(range(len(xs)))[::-1]
+            for _ in range(4):
+                for i in order:
+                    results[tid].append((i, run(kda, xs[i])))
+        except Exception as e:      # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "worker threads did not finish"
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for tid in (0, 1):
+        assert len(results[tid]) == 4 * len(xs)
+        for n, (i, (o, s)) in enumerate(results[tid]):
+            assert torch_equal(o, refs[i][0]) and torch_equal(s, refs[i][1]), f"thread {tid} call {n} workload {i}"
