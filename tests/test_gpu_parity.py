@@ -500,13 +500,27 @@ def test_bf16_states_fp32_d64(kda):
 
 
 # ------------------------------------------------ gated RMS norm output epilogue
-# Tolerance of the normalised output against the oracle.  The norm is scale-free per
-# (token, head) row, so its error is each row's relative error of o, and a whole-tensor
-# relative L2 then weights every row alike instead of by |o|^2: it tracks the row-RMS of
-# o's per-row relative error, which on these workloads is about twice o's magnitude-
-# weighted relative L2 (0.8-1.0e-2 against 4.0-4.2e-3).  Hence 2 x the 5e-3 budget of o.
-# The epilogue itself is held to 5e-3 against the exact norm of the kernel's own output.
-TOL_NORM = 1e-2
+# How the normalised output y is checked.  The norm is scale-free per (token, head) row,
+# so y inherits each row's relative error of o, and a whole-tensor relative L2 of y
+# weights every row alike: rows whose |o| is small (fast-decaying gates make many) carry
+# relative errors of o far above o's magnitude-weighted 4e-3 (up to 8x the row norm was
+# measured on tokens under gates at the -5 floor).  No fixed figure bounds y against the
+# oracle's y, so the check has two parts, each with the bf16 budget: the same call
+# without the epilogue gives o within 5e-3 of the oracle, and y is within 5e-3 of the
+# float64 norm of that o (the epilogue's own two bf16 roundings).  Against the oracle's
+# y, y may then be no worse than the exact norm of the kernel's own o plus that 5e-3.
+
+
+def check_norm(y, o, y_ref, o_ref, z, nw):
+    """The two-part check of a normalised output (torch y, o on the GPU; float64 refs)."""
+    og = o.float().cpu().numpy().reshape(o_ref.shape)
+    yg = y.float().cpu().numpy().reshape(y_ref.shape)
+    y_own = oracle.gated_rmsnorm(og, z.float().cpu().numpy().reshape(o_ref.shape), nw.cpu().numpy(), 1e-6)
+    e_o, e_epi = oracle.rel_l2(og, o_ref), oracle.rel_l2(yg, y_own)
+    ey, e_own = oracle.rel_l2(yg, y_ref), oracle.rel_l2(y_own, y_ref)
+    assert e_o <= TOL["bf16"], f"o (no epilogue) against the oracle {e_o:.3e}"
+    assert e_epi <= TOL["bf16"], f"epilogue against the norm of the kernel's own o {e_epi:.3e}"
+    assert ey <= e_own + TOL["bf16"], f"y against the oracle {ey:.3e}, the norm of its own o {e_own:.3e}"
 
 
 def _norm_inputs(x, seed):
@@ -533,17 +547,11 @@ def test_output_norm_matches_oracle(kda, nseg, layout):
     out, sT = run(kda, x, nseg=nseg, out_gate=z, norm_weight=nw, norm_eps=1e-6)
     o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["g"].cpu(), x["beta"].cpu(),
                                 x["initial_state"].cpu(), None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu())
-    zz = z.float().cpu().numpy().reshape(o_ref.shape)
-    y_ref = oracle.gated_rmsnorm(o_ref, zz, nw.cpu().numpy(), 1e-6)
-    ey = oracle.rel_l2(out.float().cpu().numpy().reshape(y_ref.shape), y_ref)
+    y_ref = oracle.gated_rmsnorm(o_ref, z.float().cpu().numpy().reshape(o_ref.shape), nw.cpu().numpy(), 1e-6)
     es = oracle.rel_l2(sT.cpu().numpy(), s_ref)
-    assert ey <= TOL_NORM and es <= TOL["bf16"], f"rel-L2 out {ey:.3e} state {es:.3e}"
-    # the epilogue against the float64 norm of the same kernel's unnormalised output: they
-    # differ by two bf16 roundings (o before the norm, y after it)
+    assert es <= TOL["bf16"], f"state {es:.3e}"
     o, _ = run(kda, x, nseg=nseg)
-    y_own = oracle.gated_rmsnorm(o.float().cpu().numpy().reshape(y_ref.shape), zz, nw.cpu().numpy(), 1e-6)
-    eo = oracle.rel_l2(out.float().cpu().numpy().reshape(y_ref.shape), y_own)
-    assert eo <= TOL["bf16"], f"epilogue vs the norm of the kernel's own output {eo:.3e}"
+    check_norm(out, o, y_ref, o_ref, z, nw)
 
 
 def test_output_norm_fused_matches_unfused(kda):

@@ -6,8 +6,10 @@ mode), a segment count (the planner's or forced), the kernel variant, the state
 dtypes (fp32 or bf16), logit inputs and, on the pipelined kernel, the gated RMS
 norm epilogue — and checks every output and final state with the tolerances of
 the other parity tests.  The cases are drawn once, from a fixed seed, so the set
-is the same on every run.
+is the same on every run.  KDA_RANDOM_CASES=n widens the sweep to the first n
+cases (24 by default).
 """
+import os
 import sys
 
 import numpy as np
@@ -19,7 +21,6 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 5e-3, "f32": 1e-4}
-TOL_NORM = 1e-2        # the gated RMS norm output: see the epilogue tests for the derivation
 
 
 def _draw(i):
@@ -43,7 +44,7 @@ def _draw(i):
                 gate=str(rng.choice(["none", "none", "none", "mild", "floor"])))
 
 
-CASES = [_draw(i) for i in range(24)]
+CASES = [_draw(i) for i in range(int(os.environ.get("KDA_RANDOM_CASES", "24")))]
 
 
 @pytest.fixture(scope="module")
@@ -89,13 +90,26 @@ def test_random_configuration(kda, c):
                                 None if s0 is None else s0.float().cpu(),
                                 None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu())
     tol = TOL["f32"] if c["fp32"] else TOL["bf16"]
-    if c["norm"]:
-        o_ref = oracle.gated_rmsnorm(o_ref, z.float().cpu().numpy().reshape(o_ref.shape), nw.cpu().numpy(), 1e-6)
-        tol = TOL_NORM
     o_gpu = out.float().cpu().numpy().reshape(o_ref.shape)
     s_gpu = fin.float().cpu().numpy()
     assert np.isfinite(o_gpu).all() and np.isfinite(s_gpu).all()
-    eo = oracle.rel_l2(o_gpu, o_ref) if o_ref.size and np.abs(o_ref).sum() > 0 else 0.0
     es = oracle.rel_l2(s_gpu, s_ref) if np.abs(s_ref).sum() > 0 else float(np.abs(s_gpu).max())
     tol_s = TOL["bf16"] if (c["bf16_state"] or not c["fp32"]) else TOL["f32"]
-    assert eo <= tol and es <= tol_s, f"rel-L2 out {eo:.3e} state {es:.3e}"
+    assert es <= tol_s, f"rel-L2 state {es:.3e}"
+    if c["norm"]:
+        # the two-part check of the normalised output (see the epilogue tests): o from the
+        # same call without the epilogue against the oracle, y against the exact norm of o
+        plain = {k: v for k, v in kw.items() if k not in ("out_gate", "norm_weight", "norm_eps")}
+        o_plain, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], **plain)
+        y_ref = oracle.gated_rmsnorm(o_ref, z.float().cpu().numpy().reshape(o_ref.shape), nw.cpu().numpy(), 1e-6)
+        og = o_plain.float().cpu().numpy().reshape(o_ref.shape)
+        y_own = oracle.gated_rmsnorm(og, z.float().cpu().numpy().reshape(o_ref.shape), nw.cpu().numpy(), 1e-6)
+        e_o = oracle.rel_l2(og, o_ref) if np.abs(o_ref).sum() > 0 else 0.0
+        e_epi = oracle.rel_l2(o_gpu, y_own) if np.abs(y_own).sum() > 0 else 0.0
+        ey = oracle.rel_l2(o_gpu, y_ref) if np.abs(y_ref).sum() > 0 else 0.0
+        e_own = oracle.rel_l2(y_own, y_ref) if np.abs(y_ref).sum() > 0 else 0.0
+        assert e_o <= tol and e_epi <= tol and ey <= e_own + tol, \
+            f"o {e_o:.3e}, epilogue {e_epi:.3e}, y {ey:.3e} (norm of own o {e_own:.3e})"
+    else:
+        eo = oracle.rel_l2(o_gpu, o_ref) if o_ref.size and np.abs(o_ref).sum() > 0 else 0.0
+        assert eo <= tol, f"rel-L2 out {eo:.3e}"
