@@ -294,3 +294,84 @@ def test_decode_graph_replay(kda):
         kda.decode(qbuf, x["k"], x["v"], x["g"], x["beta"], p_eager, idx, ntok, out=o_e)
         torch.cuda.synchronize()
         assert torch.equal(p_graph, p_eager)
+
+
+# ------------------------------------------------ seeded random configurations
+def _draw_decode(i):
+    rng = np.random.default_rng(5000 + i)
+    return dict(case=i, R=int(rng.integers(1, 12)), T=int(rng.integers(1, 9)), H=int(rng.integers(1, 5)),
+                D=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "bf16", "f32"])),
+                pool_dtype=str(rng.choice(["f32", "bf16"])), extra_slots=int(rng.integers(0, 6)),
+                bad_idx=bool(rng.random() < 0.5), ntok_null=bool(rng.random() < 0.25),
+                update=bool(rng.random() < 0.8), write_out=bool(rng.random() < 0.85),
+                logits=bool(rng.random() < 0.3), norm=bool(rng.random() < 0.25),
+                gate=str(rng.choice(["none", "none", "mild", "floor"])))
+
+
+DECODE_CASES = [_draw_decode(i) for i in range(int(__import__("os").environ.get("KDA_RANDOM_CASES", "24")))]
+
+
+@pytest.mark.parametrize("c", DECODE_CASES, ids=[f"case{c['case']}" for c in DECODE_CASES])
+def test_decode_random_configuration(kda, c):
+    """Seeded random decode calls: request and token counts (including requests with no
+    tokens), head size, I/O and pool dtypes, slot indices below 0 or past the pool
+    (skipped), verify (no state update) or commit, outputs written or not, logit inputs,
+    the output norm, and the gate distributions; every output row, every pool slot
+    (written or required unchanged) and the rows left alone are checked."""
+    import torch
+    say("decode random", c)
+    R, T, H, D = c["R"], c["T"], c["H"], c["D"]
+    w = workloads.custom([T] * R, H=H, D=D, dtype=c["dtype"], dense=True, seed=6000 + c["case"])
+    x = workloads.make_inputs(w, device="cuda", gate=None if c["gate"] == "none" else c["gate"])
+    P = R + c["extra_slots"]
+    gen = torch.Generator().manual_seed(7000 + c["case"])
+    pool = (0.1 * torch.randn(P, H, D, D, generator=gen)).to(
+        {"f32": torch.float32, "bf16": torch.bfloat16}[c["pool_dtype"]]).cuda()
+    idx = torch.randperm(P, generator=gen)[:R].to(torch.int32)
+    if c["bad_idx"] and R > 1:
+        idx[R - 1] = -3
+        idx[0] = P + 2 if R > 2 else idx[0]
+    ntok = None if c["ntok_null"] else torch.randint(0, T + 1, (R,), generator=gen, dtype=torch.int32)
+    n_eff = torch.full((R,), T, dtype=torch.int32) if ntok is None else ntok
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    z = nw = None
+    norm = c["norm"] and c["write_out"]      # the norm needs out
+    if norm:
+        gz = torch.Generator(device="cuda").manual_seed(8000 + c["case"])
+        z = torch.randn(x["v"].shape, generator=gz, device="cuda").to(x["v"].dtype)
+        nw = 1.0 + 0.1 * torch.randn(D, generator=gz, device="cuda")
+    before = pool.clone()
+    out = torch.full_like(x["v"], -512.0) if c["write_out"] else None
+    kda.decode(x["q"], x["k"], x["v"], g_in, b_in, pool, idx.cuda(), None if ntok is None else ntok.cuda(), out=out,
+               update_state=c["update"], write_out=c["write_out"], gate_logits=logits, beta_logits=logits,
+               out_gate=z, norm_weight=nw, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    valid = (idx >= 0) & (idx < P)
+    idx_o = torch.where(valid, idx, torch.full_like(idx, -1))
+    g64, b64 = (oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), -5.0) if logits else (None, None))
+    outs, states = oracle_decode(x, before, idx_o, n_eff, g=g64, beta=b64)
+    tol = 1e-4 if c["dtype"] == "f32" and c["pool_dtype"] == "f32" else 5e-3
+    if out is not None:
+        o_gpu = out.float().cpu().numpy()
+        for r in range(R):
+            n = int(n_eff[r]) if valid[r] else 0
+            assert torch.all(out[r, n:].float() == -512.0), f"request {r}: rows past {n} written"
+        if outs and sum(v.shape[0] for v in outs.values()):
+            want = np.concatenate([outs[r] for r in outs])
+            if norm:
+                zc = z.float().cpu().numpy()
+                want = np.concatenate([oracle.gated_rmsnorm(outs[r], zc[r, : outs[r].shape[0]], nw.cpu().numpy(), 1e-6)
+                                       for r in outs])
+            got = np.concatenate([o_gpu[r, : outs[r].shape[0]] for r in outs])
+            eo = oracle.rel_l2(got, want) if np.abs(want).sum() > 0 else float(np.abs(got).max())
+            assert eo <= tol, f"out {eo:.3e}"
+    written = {int(idx[r]) for r in states} if c["update"] else set()
+    for sl in range(P):
+        if sl not in written:
+            assert torch.equal(pool[sl].cpu(), before[sl].cpu()), f"slot {sl} changed"
+    if written:
+        s_gpu = np.stack([pool[int(idx[r])].float().cpu().numpy() for r in states])
+        s_ref = np.stack([states[r] for r in states])
+        es = oracle.rel_l2(s_gpu, s_ref)
+        assert es <= tol, f"state {es:.3e}"
