@@ -113,3 +113,34 @@ def test_random_configuration(kda, c):
     else:
         eo = oracle.rel_l2(o_gpu, o_ref) if o_ref.size and np.abs(o_ref).sum() > 0 else 0.0
         assert eo <= tol, f"rel-L2 out {eo:.3e}"
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"case{c['case']}" for c in CASES])
+def test_random_configuration_stalled_wave(kda, c):
+    """The same configurations with one wave (chosen by the case) stalled ~20 us after
+    every workgroup barrier give the unstalled bits: outputs and final states."""
+    import torch
+    w = workloads.custom(c["lengths"], H=c["H"], D=c["D"], dtype="f32" if c["fp32"] else "bf16", dense=c["dense"],
+                         zero_state=c["zero_state"], seed=2000 + c["case"])
+    x = workloads.make_inputs(w, device="cuda", gate=None if c["gate"] == "none" else c["gate"])
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    s0 = x["initial_state"]
+    if s0 is not None and c["bf16_state"]:
+        s0 = s0.to(torch.bfloat16)
+    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    if c["norm"]:
+        gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
+        kw.update(out_gate=torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype),
+                  norm_weight=1.0 + 0.1 * torch.randn(c["D"], generator=gen, device="cuda"), norm_eps=1e-6)
+    waves = 8 if (not c["fp32"] and c["variant"] != 1) else 4
+    wave = c["case"] % waves
+    print("[case]", c, "stalled wave", wave, file=sys.stderr, flush=True)
+    fins = [torch.empty((len(c["lengths"]), c["H"], c["D"], c["D"]), device="cuda",
+                        dtype=torch.bfloat16 if c["bf16_state"] else torch.float32) for _ in range(2)]
+    o0, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], final_state=fins[0], **kw)
+    o1, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], final_state=fins[1],
+                        stall_wave=wave, stall_cycles=127 * 6, **kw)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(fins[0]), bits(fins[1]))
