@@ -144,3 +144,54 @@ def test_random_configuration_stalled_wave(kda, c):
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
     assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(fins[0]), bits(fins[1]))
+
+
+def _padded(t, rng, align):
+    """The same values in a view with padded strides: every dimension but the last gets
+    a larger stride (extra channels per row, extra heads per token, ...), each a multiple
+    of `align` elements so that vector rows stay aligned."""
+    import torch
+    shape = list(t.shape)
+    pad = [int(rng.integers(0, 3)) * align for _ in shape]
+    pad[-1] = int(rng.integers(0, 3)) * align
+    big = torch.full([s + p for s, p in zip(shape, pad)], float("nan"), dtype=t.dtype, device=t.device)
+    view = big[tuple(slice(0, s) for s in shape)]
+    view.copy_(t)
+    return view
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"case{c['case']}" for c in CASES])
+def test_random_configuration_padded_views(kda, c):
+    """The same configurations with every tensor (q, k, v, g, beta, states, out, output
+    gate) passed as a view with padded strides give the bits of the contiguous call;
+    the padding holds NaN, so any read of it would show."""
+    import torch
+    w = workloads.custom(c["lengths"], H=c["H"], D=c["D"], dtype="f32" if c["fp32"] else "bf16", dense=c["dense"],
+                         zero_state=c["zero_state"], seed=2000 + c["case"])
+    x = workloads.make_inputs(w, device="cuda", gate=None if c["gate"] == "none" else c["gate"])
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    s0 = x["initial_state"]
+    if s0 is not None and c["bf16_state"]:
+        s0 = s0.to(torch.bfloat16)
+    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    z = nw = None
+    if c["norm"]:
+        gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
+        z = torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype)
+        nw = 1.0 + 0.1 * torch.randn(c["D"], generator=gen, device="cuda")
+        kw.update(norm_weight=nw, norm_eps=1e-6)
+    print("[case]", c, "padded views", file=sys.stderr, flush=True)
+    N = len(c["lengths"])
+    sdt = torch.bfloat16 if c["bf16_state"] else torch.float32
+    fin0 = torch.empty((N, c["H"], c["D"], c["D"]), device="cuda", dtype=sdt)
+    o0, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], final_state=fin0, out_gate=z, **kw)
+    rng = np.random.default_rng(4000 + c["case"])
+    P = lambda t, a=4: None if t is None else _padded(t, rng, a)
+    out1 = P(torch.empty_like(x["v"]))
+    fin1 = P(torch.empty((N, c["H"], c["D"], c["D"]), device="cuda", dtype=sdt), 1)
+    o1, _ = kda.prefill(P(x["q"]), P(x["k"]), P(x["v"]), P(g_in), P(b_in, 1), P(s0, 1), x["cu_seqlens"],
+                        out=out1, final_state=fin1, out_gate=P(z), **kw)
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
+    assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(fin0), bits(fin1))
