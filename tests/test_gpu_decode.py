@@ -375,3 +375,52 @@ def test_decode_random_configuration(kda, c):
         s_ref = np.stack([states[r] for r in states])
         es = oracle.rel_l2(s_gpu, s_ref)
         assert es <= tol, f"state {es:.3e}"
+
+
+def _padded(t, rng, align):
+    """The same values in a view with padded strides (NaN in the padding), each stride a
+    multiple of `align` elements."""
+    import torch
+    shape = list(t.shape)
+    pad = [int(rng.integers(0, 3)) * align for _ in shape]
+    big = torch.full([s + p for s, p in zip(shape, pad)], float("nan"), dtype=t.dtype, device=t.device)
+    view = big[tuple(slice(0, s) for s in shape)]
+    view.copy_(t)
+    return view
+
+
+@pytest.mark.parametrize("c", DECODE_CASES, ids=[f"case{c['case']}" for c in DECODE_CASES])
+def test_decode_random_padded_views(kda, c):
+    """The random decode configurations with q, k, v, g, beta, out, the output gate and
+    the state pool passed as NaN-padded strided views give the contiguous call's bits,
+    in the outputs and in every pool slot."""
+    import torch
+    R, T, H, D = c["R"], c["T"], c["H"], c["D"]
+    w = workloads.custom([T] * R, H=H, D=D, dtype=c["dtype"], dense=True, seed=6000 + c["case"])
+    x = workloads.make_inputs(w, device="cuda", gate=None if c["gate"] == "none" else c["gate"])
+    P = R + c["extra_slots"]
+    gen = torch.Generator().manual_seed(7000 + c["case"])
+    pool = (0.1 * torch.randn(P, H, D, D, generator=gen)).to(
+        {"f32": torch.float32, "bf16": torch.bfloat16}[c["pool_dtype"]]).cuda()
+    idx = torch.randperm(P, generator=gen)[:R].to(torch.int32).cuda()
+    ntok = None if c["ntok_null"] else torch.randint(0, T + 1, (R,), generator=gen, dtype=torch.int32).cuda()
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    z = nw = None
+    if c["norm"]:
+        gz = torch.Generator(device="cuda").manual_seed(8000 + c["case"])
+        z = torch.randn(x["v"].shape, generator=gz, device="cuda").to(x["v"].dtype)
+        nw = 1.0 + 0.1 * torch.randn(D, generator=gz, device="cuda")
+    say("decode padded views", c)
+    kw = dict(update_state=c["update"], gate_logits=logits, beta_logits=logits, norm_weight=nw, norm_eps=1e-6)
+    p0 = pool.clone()
+    o0 = torch.full_like(x["v"], -512.0)
+    kda.decode(x["q"], x["k"], x["v"], g_in, b_in, p0, idx, ntok, out=o0, out_gate=z, **kw)
+    rng = np.random.default_rng(9000 + c["case"])
+    pad = lambda t, a=4: None if t is None else _padded(t, rng, a)
+    p1 = pad(pool)
+    o1 = pad(torch.full_like(x["v"], -512.0))
+    kda.decode(pad(x["q"]), pad(x["k"]), pad(x["v"]), pad(g_in), pad(b_in, 1), p1, idx, ntok, out=o1, out_gate=pad(z), **kw)
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
+    assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(p0), bits(p1))
