@@ -366,7 +366,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": tr},
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
-                 "flops_per_launch": flops / launches_per_step},
+                 "flops_per_launch": flops / launches_per_step,
+                 # the most the matrix cores can be fed when the launch moves its
+                 # algorithmic bytes at the HBM peak (flops / bytes x 8 TB/s)
+                 "frac_ceiling_at_hbm_peak": (flops / bytes_) * HBM_PEAK_GBS * 1e9 / (mfma_peak * 1e12)},
         "kernel": {"name": "kda_chunk", "avg_ms": kern_ms, "launches_per_step": launches_per_step,
                    "algorithmic_bytes_per_launch": bytes_launch, "bytes_per_token_head": per_th,
                    "kernel_source_sha": source_sha("chunk_kernel")},
