@@ -424,3 +424,38 @@ def test_decode_random_padded_views(kda, c):
     torch.cuda.synchronize()
     bits = lambda t: t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
     assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(p0), bits(p1))
+
+
+@pytest.mark.parametrize("c", DECODE_CASES, ids=[f"case{c['case']}" for c in DECODE_CASES])
+def test_decode_random_stalled_wave(kda, c):
+    """The random decode configurations with one of the 4 waves (chosen by the case)
+    stalled after every barrier give the unstalled bits, in the outputs and the pool."""
+    import torch
+    R, T, H, D = c["R"], c["T"], c["H"], c["D"]
+    w = workloads.custom([T] * R, H=H, D=D, dtype=c["dtype"], dense=True, seed=6000 + c["case"])
+    x = workloads.make_inputs(w, device="cuda", gate=None if c["gate"] == "none" else c["gate"])
+    P = R + c["extra_slots"]
+    gen = torch.Generator().manual_seed(7000 + c["case"])
+    pool = (0.1 * torch.randn(P, H, D, D, generator=gen)).to(
+        {"f32": torch.float32, "bf16": torch.bfloat16}[c["pool_dtype"]]).cuda()
+    idx = torch.randperm(P, generator=gen)[:R].to(torch.int32).cuda()
+    ntok = None if c["ntok_null"] else torch.randint(0, T + 1, (R,), generator=gen, dtype=torch.int32).cuda()
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    z = nw = None
+    if c["norm"]:
+        gz = torch.Generator(device="cuda").manual_seed(8000 + c["case"])
+        z = torch.randn(x["v"].shape, generator=gz, device="cuda").to(x["v"].dtype)
+        nw = 1.0 + 0.1 * torch.randn(D, generator=gz, device="cuda")
+    wave = c["case"] % 4
+    say("decode stalled wave", wave, c)
+    kw = dict(update_state=c["update"], gate_logits=logits, beta_logits=logits, out_gate=z, norm_weight=nw, norm_eps=1e-6)
+    res = []
+    for stall in (dict(), dict(stall_wave=wave, stall_cycles=127 * 6)):
+        p = pool.clone()
+        o = torch.full_like(x["v"], -512.0)
+        kda.decode(x["q"], x["k"], x["v"], g_in, b_in, p, idx, ntok, out=o, **kw, **stall)
+        res.append((o, p))
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    assert torch.equal(bits(res[0][0]), bits(res[1][0])) and torch.equal(bits(res[0][1]), bits(res[1][1]))
