@@ -344,6 +344,9 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
         }
         pl.nseg = (int)std::max<int64_t>(1, nseg);
     }
+    // the segment-build launch has chains * nseg * 2 workgroups (a 32-bit grid)
+    if (chains * pl.nseg * 2 > (int64_t)INT32_MAX)
+        return fail(KDA_ERR_UNSUPPORTED, "%lld chains x %d segments exceed one launch", (long long)chains, pl.nseg);
     const int prep = o ? o->prep : 0;
     if (prep < 0 || prep > 2) return fail(KDA_ERR_UNSUPPORTED, "prep mode %d", prep);
     if (o && (o->gate_act < 0 || o->gate_act > 1 || o->beta_act < 0 || o->beta_act > 1))

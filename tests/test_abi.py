@@ -374,3 +374,19 @@ def test_plan_log(tmp_path):
     assert p.returncode == 0, p.stderr[-2000:]
     assert "status 0" in p.stdout
     assert "kda: plan N=2 H=2 D=128 packed chains=4 nseg=" in p.stderr and "kernel=pipelined" in p.stderr
+
+
+def test_segment_grid_beyond_one_launch_is_refused(lib):
+    """2^25 chains (B = 2^20 dense sequences of one token, H = 32) with 64 forced segments
+    would need 2^32 segment-build workgroups: refused before any launch."""
+    B, T, H, D = 1 << 20, 1, 32, 128
+    gap = 1 << 36
+    s = [desc([B, T, H, D]), desc([B, T, H, D], base=FAKE + gap), desc([B, T, H, D], base=FAKE + 2 * gap),
+         desc([B, T, H, D], KDA_F32, FAKE + 3 * gap), desc([B, T, H], KDA_F32, FAKE + 4 * gap), None, None,
+         desc([B, T, H, D], base=FAKE + 5 * gap), None]
+    n = ctypes.c_size_t(0)
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    st = lib.kda_prefill_workspace_size(*(r(d) for d in s), ctypes.byref(kda.options(nseg=64)), ctypes.byref(n))
+    assert st == 6 and "segments" in lib.kda_last_error().decode()
+    st = lib.kda_prefill_workspace_size(*(r(d) for d in s), ctypes.byref(kda.options(nseg=0)), ctypes.byref(n))
+    assert st == 0 and n.value == 0       # the planner's choice: one segment, no workspace
