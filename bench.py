@@ -1,6 +1,6 @@
 """KDA chunked-prefill benchmark on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config varlen|large|eqlen|long|varlen_padded|tiny]
+    python bench.py [--steps K] [--warmup W] [--config varlen|large|eqlen|long|varlen_padded|varlen_h64|tiny]
     python bench.py --config decode|decode_bf16|verify4        (the recurrent decode kernel)
 
 One step is one kda_prefill call over the whole workload (every kernel of the

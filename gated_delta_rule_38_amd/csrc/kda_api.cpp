@@ -304,6 +304,7 @@ struct Plan {
     bool pipe = false;          // pipelined 32-token kernel (d = 128, bf16)
     int chunk = 64;
     bool standalone_prep = false;
+    bool lpt = false;           // chains started longest sequence first
     size_t off_gamma = 0, off_maps = 0, off_start = 0, bytes = 0;
 };
 
@@ -360,6 +361,16 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     if (o && o->out_gate && 32 * o->out_gate->stride[o->out_gate->ndim - 3] * 2 + 1024 > (int64_t)INT32_MAX)
         return fail(KDA_ERR_UNSUPPORTED, "out_gate token stride too large for the pipelined kernel");
     pl.standalone_prep = prep == 1;   // otherwise every chunk-kernel pass scans its own chunks
+    // Chain order.  With more chains than CUs, workgroups start in launch order as CUs free up,
+    // so a packed batch of mixed lengths finishes sooner when its longest sequences start first
+    // (longest-processing-time order); with every chain resident at once the order is moot.
+    // The lengths are on the device: the kernel ranks them (pipelined kernel, one segment,
+    // at most LPT_MAX_SEQ sequences).  KDA_ORDER=natural or =longest overrides the choice.
+    const char *ord = getenv("KDA_ORDER");
+    const bool lpt_ok = pl.pipe && pl.nseg == 1 && !P.dense && P.N > 1 && P.N <= kda::LPT_MAX_SEQ;
+    if (ord && strcmp(ord, "natural") == 0) pl.lpt = false;
+    else if (ord && strcmp(ord, "longest") == 0) pl.lpt = lpt_ok;
+    else pl.lpt = lpt_ok && chains > device_cus();
     size_t off = 0;
     if (pl.standalone_prep) {
         pl.off_gamma = off;
@@ -374,10 +385,10 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     }
     pl.bytes = off;
     if (env_on("KDA_LOG"))
-        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d kernel=%s chunk=%d prep=%s workspace=%zu B\n",
+        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d kernel=%s chunk=%d prep=%s order=%s workspace=%zu B\n",
                 (long long)P.N, (long long)P.H, (long long)P.D, P.dense ? "dense" : "packed", (long long)chains,
                 pl.nseg, pl.pipe ? "pipelined" : "single-role", pl.chunk, pl.standalone_prep ? "standalone" : "in-chunk",
-                pl.bytes);
+                pl.lpt ? "longest-first" : "natural", pl.bytes);
     return KDA_OK;
 }
 
@@ -464,6 +475,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     cp.gate_act = (o && o->gate_act) ? 1 : 0;
     cp.gate_lb = o ? o->gate_lower_bound : 0.f;
     cp.beta_act = (o && o->beta_act) ? 1 : 0;
+    cp.lpt = pl.lpt ? 1 : 0;
     if (o && o->out_gate) {
         cp.z = o->out_gate->data;
         cp.nw = (const float *)o->norm_weight->data;

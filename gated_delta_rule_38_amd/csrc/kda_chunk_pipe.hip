@@ -84,6 +84,7 @@ constexpr int S_NRM = SMEM;
 constexpr int S_NW = S_NRM + C * 4 * 4;
 constexpr int SMEM_NORM = S_NW + D * 4;
 static_assert(SMEM_NORM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+static_assert(4 * (LPT_MAX_SEQ + 1) <= B_SIZE, "longest-first scratch fits in operand buffer 0");
 static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TB % 16 == 0 &&
               S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
 
@@ -92,6 +93,31 @@ typedef Vec4<float> V4f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Index of the sequence of rank r when the N sequences of a packed batch are ordered longest
+// first (ties: lower index first), so that a launch with more chains than CUs starts its
+// longest chains first and its short ones fill in behind them.  Every thread of the workgroup
+// calls it (it holds three barriers) and gets the result.  Its scratch, the first 4 (N + 1)
+// bytes of LDS, is written next only after the barriers that start the main loop.
+__device__ int longest_first(const int32_t *cu, int N, int r, char *smem)
+{
+    int *sLen = (int *)smem;
+    for (int i = threadIdx.x; i < N; i += NT) sLen[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < N; i += NT) {
+        const int li = sLen[i];
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = sLen[j];
+            rank += (lj > li) | ((lj == li) & (j < i));
+        }
+        if (rank == r) sLen[N] = i;     // the ranks are a permutation: exactly one writer
+    }
+    __syncthreads();
+    const int n = sLen[N];
+    __syncthreads();
+    return n;
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4a+b receives
 // 16-bit element b of the 8-byte words addressed by lanes a, a+4, a+8, a+12 of the group.
@@ -261,7 +287,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     }
     const int seg = wg % p.nseg;
     const int chain = wg / p.nseg;
-    const int n = chain / p.H, h = chain % p.H;
+    const int h = chain % p.H;
+    const int n = p.lpt ? longest_first(p.cu, p.N, chain / p.H, smem) : chain / p.H;
     int64_t t0, bsel;
     int len;
     seq_range(p.cu, n, p.T, t0, len, bsel);

@@ -219,7 +219,12 @@ struct ChunkParams {
     int64_t z_sb, z_st, z_sh;
     const float *nw;           // norm weight [D]
     float eps;
+    int32_t lpt;               // packed layout, one segment: workgroup rank r runs the r-th
+                               // longest sequence (ties: lower index first); N <= LPT_MAX_SEQ
 };
+
+// Longest-first chain order: at most this many sequences (one launch ranks them all in LDS).
+constexpr int LPT_MAX_SEQ = 512;
 
 struct PrepParams {
     const float *g;

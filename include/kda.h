@@ -55,7 +55,14 @@
  *                returns KDA_ERR_SHAPE with nothing further launched.  Without it a
  *                cu_seqlens whose last offset exceeds the token extent makes the kernels
  *                read past the inputs.
- *   KDA_LOG=1    prints every plan (layout, chains, segments, kernel, workspace) to stderr.
+ *   KDA_LOG=1    prints every plan (layout, chains, segments, kernel, chain order,
+ *                workspace) to stderr.
+ *   KDA_ORDER    chain order of a packed single-segment launch.  By default, when there
+ *                are more (sequence, head) chains than compute units and at most 512
+ *                sequences, the kernel starts the longest sequences' chains first (it
+ *                ranks the lengths on the device); results are the same bits in any
+ *                order.  KDA_ORDER=natural keeps launch order, KDA_ORDER=longest ranks
+ *                whenever the plan allows it.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -390,3 +390,38 @@ def test_segment_grid_beyond_one_launch_is_refused(lib):
     assert st == 6 and "segments" in lib.kda_last_error().decode()
     st = lib.kda_prefill_workspace_size(*(r(d) for d in s), ctypes.byref(kda.options(nseg=0)), ctypes.byref(n))
     assert st == 0 and n.value == 0       # the planner's choice: one segment, no workspace
+
+
+def test_plan_chain_order(tmp_path):
+    """The planner starts the longest sequences first exactly when a packed single-segment
+    launch has more chains than CUs (256 without a GPU) and at most 512 sequences;
+    KDA_ORDER overrides it."""
+    import subprocess, sys, textwrap
+    code = textwrap.dedent(f"""
+        import ctypes, os, sys
+        sys.path.insert(0, {ROOT!r}); sys.path.insert(0, {os.path.join(ROOT, 'tests')!r})
+        import test_abi as t
+        import gated_delta_rule_38_amd as kda
+        lib = kda.load_library()
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        def plan(T, H, N, env=None, nseg=0):
+            os.environ.pop("KDA_ORDER", None)
+            if env: os.environ["KDA_ORDER"] = env
+            s = t.packed_set(T=T, H=H, N=N)
+            n = ctypes.c_size_t(0)
+            st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                                ctypes.byref(kda.options(nseg=nseg)), ctypes.byref(n))
+            sys.stderr.flush()
+            print("case", T, H, N, env, nseg, "status", st, flush=True)
+        plan(4096, 128, 3)               # 384 chains > 256 CUs: longest first
+        plan(4096, 32, 8)                # 256 chains: every chain resident, natural
+        plan(4096, 1, 600)               # 600 sequences > 512: natural
+        plan(4096, 128, 3, "natural")
+        plan(4096, 2, 2, "longest", 1)   # forced on a small single-segment plan
+        plan(4096, 2, 2, "longest")      # the planner segments it: order not applicable
+    """)
+    env = dict(os.environ, KDA_LOG="1")
+    p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0 and p.stdout.count("status 0") == 6, p.stdout + p.stderr[-2000:]
+    orders = [l.split("order=")[1].split()[0] for l in p.stderr.splitlines() if l.startswith("kda: plan")]
+    assert orders == ["longest-first", "natural", "natural", "natural", "longest-first", "natural"], orders

@@ -673,3 +673,34 @@ def test_cached_workspace_threads(kda):
         assert len(results[tid]) == 4 * len(xs)
         for n, (i, (o, s)) in enumerate(results[tid]):
             assert torch_equal(o, refs[i][0]) and torch_equal(s, refs[i][1]), f"thread {tid} call {n} workload {i}"
+
+
+def test_longest_first_order_same_bits(kda, monkeypatch):
+    """Longest-first chain order (packed, one segment) changes only which workgroup runs
+    which chain: outputs and final states are the bits of the natural order.  A batch of
+    mixed lengths with more chains than CUs takes it by default; smaller batches are forced
+    with KDA_ORDER=longest, also with bf16 states, the output norm and a stalled wave (the
+    ranking adds barriers before the main loop)."""
+    import torch
+    big = workloads.custom([700, 5, 0, 1300, 64, 2100], H=48, D=128, seed=90)     # 288 chains
+    small = workloads.custom([130, 0, 64, 1, 300], H=2, D=128, seed=91)
+    for w, forced in ((big, None), (small, "longest")):
+        x = gen(w)
+        z, nw = _norm_inputs(x, 92)
+        for kw in (dict(nseg=1), dict(nseg=1, out_gate=z, norm_weight=nw, norm_eps=1e-6),
+                   dict(nseg=1, stall_wave=3, stall_cycles=127 * 6)):
+            say("longest first", w.lengths, w.H, sorted(kw))
+            monkeypatch.setenv("KDA_ORDER", "natural")
+            o0, s0 = run(kda, x, **kw)
+            if forced:
+                monkeypatch.setenv("KDA_ORDER", forced)
+            else:
+                monkeypatch.delenv("KDA_ORDER")
+            o1, s1 = run(kda, x, **kw)
+            torch.cuda.synchronize()
+            assert torch_equal(o0, o1) and torch_equal(s0, s1)
+    # the reordered big batch against the oracle on its longest and shortest sequences
+    x = gen(big)
+    monkeypatch.delenv("KDA_ORDER", raising=False)
+    out, sT = run(kda, x)
+    check_chains(x, out, sT, [(5, 47), (1, 0), (3, 20), (2, 5)], TOL["bf16"])

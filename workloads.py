@@ -66,6 +66,8 @@ WORKLOADS = {
     "eqlen": Workload("eqlen", (4096,) * 2, H=16, D=128, dtype="bf16", dense=True),
     "varlen": Workload("varlen", tuple(varlen_lengths()), H=32, D=128, dtype="bf16", dense=False),
     "varlen_padded": Workload("varlen_padded", (4000,) * 8, H=32, D=128, dtype="bf16", dense=True),
+    # the varlen lengths at 64 heads: 512 chains on 256 CUs, where the chain order matters
+    "varlen_h64": Workload("varlen_h64", tuple(varlen_lengths()), H=64, D=128, dtype="bf16", dense=False),
     "long": Workload("long", (65536,), H=8, D=128, dtype="bf16", dense=True, floor_channels=13),
     "large": Workload("large", (8192,) * 16, H=64, D=128, dtype="bf16", dense=True),
 }
