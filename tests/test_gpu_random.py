@@ -195,3 +195,35 @@ def test_random_configuration_padded_views(kda, c):
     torch.cuda.synchronize()
     bits = lambda t: t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
     assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(fin0), bits(fin1))
+
+
+@pytest.mark.parametrize("c", [c for c in CASES if not c["dense"] and not c["fp32"] and c["variant"] != 1],
+                         ids=lambda c: f"case{c['case']}")
+def test_random_configuration_longest_first(kda, c, monkeypatch):
+    """The packed pipelined configurations as one segment, with the chains started longest
+    sequence first (KDA_ORDER=longest) and in launch order: the same bits."""
+    import torch
+    w = workloads.custom(c["lengths"], H=c["H"], D=c["D"], dtype="bf16", dense=False,
+                         zero_state=c["zero_state"], seed=2000 + c["case"])
+    x = workloads.make_inputs(w, device="cuda", gate=None if c["gate"] == "none" else c["gate"])
+    logits = c["logits"] and x["g_logits"] is not None
+    g_in, b_in = (x["g_logits"], x["beta_logits"]) if logits else (x["g"], x["beta"])
+    s0 = x["initial_state"]
+    if s0 is not None and c["bf16_state"]:
+        s0 = s0.to(torch.bfloat16)
+    kw = dict(nseg=1, variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    if c["norm"]:
+        gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
+        kw.update(out_gate=torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype),
+                  norm_weight=1.0 + 0.1 * torch.randn(c["D"], generator=gen, device="cuda"), norm_eps=1e-6)
+    print("[case]", c, "longest first", file=sys.stderr, flush=True)
+    res = []
+    for order in ("natural", "longest"):
+        monkeypatch.setenv("KDA_ORDER", order)
+        fin = torch.empty((len(c["lengths"]), c["H"], c["D"], c["D"]), device="cuda",
+                          dtype=torch.bfloat16 if c["bf16_state"] else torch.float32)
+        o, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], final_state=fin, **kw)
+        res.append((o, fin))
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    assert torch.equal(bits(res[0][0]), bits(res[1][0])) and torch.equal(bits(res[0][1]), bits(res[1][1]))
