@@ -318,6 +318,28 @@ int device_cus()
     return cus;
 }
 
+// Segment count from a cost model in units of one chunk step of a launch that leaves most
+// CUs idle (measured on MI355X).  One segment: C steps (the longest chain's chunks).  nseg
+// segments: the segment-build pass runs 2 chains nseg workgroups, i.e. ceil(2 chains nseg /
+// CUs) rounds of ceil(C / nseg) steps, the output pass ceil(chains nseg / CUs) rounds, and
+// COMBINE one matrix step per segment boundary (~1.35); passes that fill every CU run their
+// steps ~1.3x slower (the clock drops under full load).  The cheapest count wins, ties to
+// fewer segments, keeping >= 8 chunks per segment.  (With every CU already holding a chain,
+// segmenting cannot pay and one segment is kept.)
+int choose_nseg(int64_t chains, int64_t C, int cus)
+{
+    if (chains <= 0 || chains >= cus || C < 16) return 1;
+    double best = (double)C;
+    int pick = 1;
+    for (int nseg = 2; nseg <= 64 && C / nseg >= 8; ++nseg) {
+        const double steps = (double)((C + nseg - 1) / nseg);
+        const double rounds = (double)((2 * chains * nseg + cus - 1) / cus + (chains * nseg + cus - 1) / cus);
+        const double cost = 1.3 * rounds * steps + 1.35 * (nseg - 1);
+        if (cost < best) { best = cost; pick = nseg; }
+    }
+    return pick;
+}
+
 kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
 {
     const int64_t chains = P.N * P.H;
@@ -337,13 +359,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
         if (o->nseg > 64) return fail(KDA_ERR_UNSUPPORTED, "nseg %d > 64", o->nseg);
         pl.nseg = o->nseg;
     } else {
-        const int cus = device_cus();
-        int64_t nseg = 1;
-        if (chains > 0 && chains < cus) {
-            nseg = std::min<int64_t>(cus / chains, 32);
-            nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, max_chunks / 8));   // >= ~8 chunks per segment
-        }
-        pl.nseg = (int)std::max<int64_t>(1, nseg);
+        pl.nseg = choose_nseg(chains, max_chunks, device_cus());
     }
     // the segment-build launch has chains * nseg * 2 workgroups (a 32-bit grid)
     if (chains * pl.nseg * 2 > (int64_t)INT32_MAX)
