@@ -425,3 +425,22 @@ def test_plan_chain_order(tmp_path):
     assert p.returncode == 0 and p.stdout.count("status 0") == 6, p.stdout + p.stderr[-2000:]
     orders = [l.split("order=")[1].split()[0] for l in p.stderr.splitlines() if l.startswith("kda: plan")]
     assert orders == ["longest-first", "natural", "natural", "natural", "longest-first", "natural"], orders
+
+
+@pytest.mark.parametrize("B,H,T,nseg", [(2, 16, 4096, 8), (1, 8, 65536, 32), (3, 32, 4096, 1), (4, 32, 4096, 1),
+                                        (8, 32, 8192, 1), (1, 2, 256, 1), (1, 8, 16384, 16)])
+def test_planner_segment_counts(lib, B, H, T, nseg):
+    """The planner's segment count (read off the workspace size, chains x nseg x 3 states)
+    on 256 CUs: the measured winners on the equal-length and long workloads, one segment
+    where the segment passes would need more rounds than they save (96 and 128 chains)."""
+    D = 128
+    gap = 1 << 36
+    s = [desc([B, T, H, D]), desc([B, T, H, D], base=FAKE + gap), desc([B, T, H, D], base=FAKE + 2 * gap),
+         desc([B, T, H, D], KDA_F32, FAKE + 3 * gap), desc([B, T, H], KDA_F32, FAKE + 4 * gap), None, None,
+         desc([B, T, H, D], base=FAKE + 5 * gap), None]
+    n = ctypes.c_size_t(0)
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    st = lib.kda_prefill_workspace_size(*(r(d) for d in s), None, ctypes.byref(n))
+    assert st == 0, lib.kda_last_error()
+    got = n.value // (B * H * 3 * D * D * 4) if n.value else 1
+    assert got == nseg
