@@ -305,7 +305,8 @@ def _draw_decode(i):
                 bad_idx=bool(rng.random() < 0.5), ntok_null=bool(rng.random() < 0.25),
                 update=bool(rng.random() < 0.8), write_out=bool(rng.random() < 0.85),
                 logits=bool(rng.random() < 0.3), norm=bool(rng.random() < 0.25),
-                gate=str(rng.choice(["none", "none", "mild", "floor"])))
+                gate=str(rng.choice(["none", "none", "mild", "floor"])),
+                lb=float(rng.choice([-5.0, -5.0, -3.0, -1.0, -0.25])))      # gate lower bound with logits
 
 
 DECODE_CASES = [_draw_decode(i) for i in range(int(__import__("os").environ.get("KDA_RANDOM_CASES", "24")))]
@@ -345,11 +346,12 @@ def test_decode_random_configuration(kda, c):
     out = torch.full_like(x["v"], -512.0) if c["write_out"] else None
     kda.decode(x["q"], x["k"], x["v"], g_in, b_in, pool, idx.cuda(), None if ntok is None else ntok.cuda(), out=out,
                update_state=c["update"], write_out=c["write_out"], gate_logits=logits, beta_logits=logits,
+               gate_lower_bound=c["lb"],
                out_gate=z, norm_weight=nw, norm_eps=1e-6)
     torch.cuda.synchronize()
     valid = (idx >= 0) & (idx < P)
     idx_o = torch.where(valid, idx, torch.full_like(idx, -1))
-    g64, b64 = (oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), -5.0) if logits else (None, None))
+    g64, b64 = (oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), c["lb"]) if logits else (None, None))
     outs, states = oracle_decode(x, before, idx_o, n_eff, g=g64, beta=b64)
     tol = 1e-4 if c["dtype"] == "f32" and c["pool_dtype"] == "f32" else 5e-3
     if out is not None:
@@ -412,7 +414,8 @@ def test_decode_random_padded_views(kda, c):
         z = torch.randn(x["v"].shape, generator=gz, device="cuda").to(x["v"].dtype)
         nw = 1.0 + 0.1 * torch.randn(D, generator=gz, device="cuda")
     say("decode padded views", c)
-    kw = dict(update_state=c["update"], gate_logits=logits, beta_logits=logits, norm_weight=nw, norm_eps=1e-6)
+    kw = dict(update_state=c["update"], gate_logits=logits, beta_logits=logits, gate_lower_bound=c["lb"],
+              norm_weight=nw, norm_eps=1e-6)
     p0 = pool.clone()
     o0 = torch.full_like(x["v"], -512.0)
     kda.decode(x["q"], x["k"], x["v"], g_in, b_in, p0, idx, ntok, out=o0, out_gate=z, **kw)
@@ -449,7 +452,8 @@ def test_decode_random_stalled_wave(kda, c):
         nw = 1.0 + 0.1 * torch.randn(D, generator=gz, device="cuda")
     wave = c["case"] % 4
     say("decode stalled wave", wave, c)
-    kw = dict(update_state=c["update"], gate_logits=logits, beta_logits=logits, out_gate=z, norm_weight=nw, norm_eps=1e-6)
+    kw = dict(update_state=c["update"], gate_logits=logits, beta_logits=logits, gate_lower_bound=c["lb"], out_gate=z,
+              norm_weight=nw, norm_eps=1e-6)
     res = []
     for stall in (dict(), dict(stall_wave=wave, stall_cycles=127 * 6)):
         p = pool.clone()

@@ -41,7 +41,8 @@ def _draw(i):
     return dict(case=i, fp32=fp32, D=D, dense=dense, lengths=lengths, H=H, variant=variant, nseg=nseg,
                 zero_state=bool(rng.random() < 0.2), bf16_state=bool(rng.random() < 0.3),
                 logits=bool(rng.random() < 0.3), norm=bool(pipelined and rng.random() < 0.3),
-                gate=str(rng.choice(["none", "none", "none", "mild", "floor"])))
+                gate=str(rng.choice(["none", "none", "none", "mild", "floor"])),
+                lb=float(rng.choice([-5.0, -5.0, -3.0, -1.0, -0.25])))      # gate lower bound with logits
 
 
 CASES = [_draw(i) for i in range(int(os.environ.get("KDA_RANDOM_CASES", "24")))]
@@ -73,7 +74,7 @@ def test_random_configuration(kda, c):
     N = len(c["lengths"])
     fin = torch.empty((N, c["H"], c["D"], c["D"]), device="cuda",
                       dtype=torch.bfloat16 if c["bf16_state"] else torch.float32)
-    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits, gate_lower_bound=c["lb"])
     z = nw = None
     if c["norm"]:
         gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
@@ -83,7 +84,7 @@ def test_random_configuration(kda, c):
     out, _ = kda.prefill(x["q"], x["k"], x["v"], g_in, b_in, s0, x["cu_seqlens"], final_state=fin, **kw)
     torch.cuda.synchronize()
     if logits:
-        g64, b64 = oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), -5.0)
+        g64, b64 = oracle.activations(x["g_logits"].cpu(), x["beta_logits"].cpu(), c["lb"])
     else:
         g64, b64 = x["g"].cpu(), x["beta"].cpu()
     o_ref, s_ref = oracle.run_c(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), g64, b64,
@@ -128,7 +129,7 @@ def test_random_configuration_stalled_wave(kda, c):
     s0 = x["initial_state"]
     if s0 is not None and c["bf16_state"]:
         s0 = s0.to(torch.bfloat16)
-    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits, gate_lower_bound=c["lb"])
     if c["norm"]:
         gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
         kw.update(out_gate=torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype),
@@ -174,7 +175,7 @@ def test_random_configuration_padded_views(kda, c):
     s0 = x["initial_state"]
     if s0 is not None and c["bf16_state"]:
         s0 = s0.to(torch.bfloat16)
-    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    kw = dict(nseg=c["nseg"], variant=c["variant"], gate_logits=logits, beta_logits=logits, gate_lower_bound=c["lb"])
     z = nw = None
     if c["norm"]:
         gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
@@ -211,7 +212,7 @@ def test_random_configuration_longest_first(kda, c, monkeypatch):
     s0 = x["initial_state"]
     if s0 is not None and c["bf16_state"]:
         s0 = s0.to(torch.bfloat16)
-    kw = dict(nseg=1, variant=c["variant"], gate_logits=logits, beta_logits=logits)
+    kw = dict(nseg=1, variant=c["variant"], gate_logits=logits, beta_logits=logits, gate_lower_bound=c["lb"])
     if c["norm"]:
         gen = torch.Generator(device="cuda").manual_seed(3000 + c["case"])
         kw.update(out_gate=torch.randn(x["v"].shape, generator=gen, device="cuda").to(x["v"].dtype),
