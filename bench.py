@@ -122,18 +122,29 @@ def cpu_baseline(x, w, budget_s):
 
 def work_balance(w, cus=256, chunk=32):
     """How evenly the single-segment plan loads the CUs: one workgroup runs each
-    (sequence, head) chain start to end, chunk after chunk, so the launch lasts as
-    long as the longest chain.  occupancy_bound = mean chunks per CU / chunks of the
-    longest chain is the fraction of the roofline that imbalance alone leaves."""
+    (sequence, head) chain start to end, chunk after chunk, and a workgroup starts on the
+    first CU to free up, in launch order -- longest sequence first when the library orders
+    them (packed, more chains than CUs, at most 512 sequences).  The makespan is simulated;
+    occupancy_bound = mean chunks per busy CU / makespan is the fraction of the roofline
+    that the imbalance alone leaves."""
+    import heapq
     chunks = [-(-L // chunk) for L in w.lengths]
     chains = w.n_seq * w.H
-    rounds = -(-chains // cus)
+    order = list(range(w.n_seq))
+    longest_first = (not w.dense) and chains > cus and 1 < w.n_seq <= 512
+    if longest_first:
+        order.sort(key=lambda n: (-chunks[n], n))
+    free = [0] * min(cus, chains) if chains else []
+    heapq.heapify(free)
+    for n in order:
+        for _ in range(w.H):
+            heapq.heappush(free, heapq.heappop(free) + chunks[n])
+    makespan = max(free) if free else 0
     total = sum(chunks) * w.H
-    longest = max(chunks) if chunks else 0
     per_cu = total / min(cus, chains) if chains else 0.0
-    return {"chains": chains, "chunk_tokens": chunk, "longest_chain_chunks": longest,
-            "mean_chunks_per_cu": per_cu,
-            "occupancy_bound": (per_cu / (longest * rounds)) if longest else None}
+    return {"chains": chains, "chunk_tokens": chunk, "longest_chain_chunks": max(chunks) if chunks else 0,
+            "order": "longest-first" if longest_first else "launch", "makespan_chunks": makespan,
+            "mean_chunks_per_cu": per_cu, "occupancy_bound": (per_cu / makespan) if makespan else None}
 
 
 def correctness_gate(kda, x, w, out, fin):

@@ -45,10 +45,12 @@ def test_decode_algorithmic_bytes_are_the_tensors_bytes():
     assert bench.decode_algorithmic(w)[0] == read + written
 
 
-def _simulate(lengths, H, cus, chunk):
-    """Chains start in launch order on the first free CU and run to the end."""
+def _simulate(lengths, H, cus, chunk, longest_first=False):
+    """Chains start in launch order (or longest sequence first) on the first free CU and
+    run to the end."""
     free = [0] * cus
-    for L in lengths:
+    seqs = sorted(lengths, key=lambda L: -L) if longest_first else list(lengths)
+    for L in seqs:
         for _ in range(H):
             i = min(range(cus), key=lambda c: free[c])
             free[i] += math.ceil(L / chunk)
@@ -56,22 +58,27 @@ def _simulate(lengths, H, cus, chunk):
     return max(free), sum(busy) / len(busy)
 
 
-@pytest.mark.parametrize("name", ["varlen", "varlen_padded", "large", "long"])
+@pytest.mark.parametrize("name", ["varlen", "varlen_padded", "varlen_h64", "large", "long"])
 def test_work_balance_matches_a_simulated_schedule(name):
     w = workloads.WORKLOADS[name]
     wb = bench.work_balance(w)
-    makespan, mean_busy = _simulate(w.lengths, w.H, 256, 32)
-    rounds = math.ceil(w.n_seq * w.H / 256)
+    lpt = (not w.dense) and w.n_seq * w.H > 256 and 1 < w.n_seq <= 512
+    makespan, mean_busy = _simulate(w.lengths, w.H, 256, 32, lpt)
     assert wb["chains"] == w.n_seq * w.H
-    assert wb["longest_chain_chunks"] * rounds == makespan
+    assert wb["order"] == ("longest-first" if lpt else "launch")
+    assert wb["makespan_chunks"] == makespan
     assert wb["mean_chunks_per_cu"] == pytest.approx(mean_busy)
     assert wb["occupancy_bound"] == pytest.approx(mean_busy / makespan)
 
 
 def test_varlen_balance_figures():
     wb = bench.work_balance(workloads.WORKLOADS["varlen"])
-    assert (wb["chains"], wb["longest_chain_chunks"]) == (256, 221)
+    assert (wb["chains"], wb["longest_chain_chunks"], wb["makespan_chunks"]) == (256, 221, 221)
     assert wb["occupancy_bound"] == pytest.approx(1027 * 32 / 256 / 221)
+    # the same lengths at 64 heads: 389 chunk-steps in launch order, 270 longest first
+    w = workloads.WORKLOADS["varlen_h64"]
+    assert _simulate(w.lengths, w.H, 256, 32, False)[0] == 389
+    assert bench.work_balance(w)["makespan_chunks"] == 270
 
 
 def test_traffic_figure_is_dropped_when_the_kernel_source_changes(monkeypatch):
