@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 
 KDA_BF16, KDA_F32, KDA_I32 = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_LAYOUT",
-          5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP"}
+          5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP",
+          9: "KDA_ERR_RANGE"}
 EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prep", "kda_decode",
            "kda_release_cached_workspace", "kda_profile_enable", "kda_profile_read",
            "kda_status_string", "kda_last_error", "kda_abi_version")
@@ -131,6 +132,19 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be on the GPU")
 
 
+def _stream(device, stream):
+    """(torch stream, raw hipStream_t) for a call: the current stream when None, else a
+    torch.cuda.Stream or a raw handle (wrapped as an external stream)."""
+    import torch
+    if stream is None:
+        s = torch.cuda.current_stream(device)
+    elif isinstance(stream, torch.cuda.Stream):
+        s = stream
+    else:
+        s = torch.cuda.ExternalStream(int(stream), device=device)
+    return s, s.cuda_stream
+
+
 def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0, variant: int = 0,
             gate_logits: bool = False, gate_lower_bound: float = -5.0, beta_logits: bool = False,
             out_gate=None, norm_weight=None, norm_eps: float = 1e-6) -> KdaOptions:
@@ -192,13 +206,19 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     With the default knobs this calls ``kda_prefill`` (library-cached
     workspace); any knob or a ``workspace`` tensor routes through
     ``kda_prefill_ws`` with a torch-allocated workspace.
+    ``stream``: None (torch's current stream), a torch.cuda.Stream or a raw
+    hipStream_t handle; outputs and workspace this call allocates are allocated
+    on that stream.
     """
     import torch
     lib = load_library()
     _require_gpu(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
-    out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, output_final_state)
+    sobj, st = _stream(q.device, stream)
+    # Everything allocated here is allocated on the stream the kernels run on, so torch's
+    # caching allocator never hands a block to another stream while they may still use it.
+    with torch.cuda.stream(sobj):
+        out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, output_final_state)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
-    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     plain = (nseg == 0 and prep == 0 and stall_wave < 0 and variant == 0 and workspace is None
              and not gate_logits and not beta_logits and out_gate is None and norm_weight is None)
     if plain:
@@ -209,7 +229,8 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
     need = ctypes.c_size_t(0)
     _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value:
-        workspace = torch.empty(need.value + 256, dtype=torch.uint8, device=q.device)
+        with torch.cuda.stream(sobj):
+            workspace = torch.empty(need.value + 256, dtype=torch.uint8, device=q.device)
     wptr, wbytes = None, 0
     if workspace is not None:
         base = workspace.data_ptr()
@@ -236,9 +257,10 @@ def decode(q, k, v, g, beta, state_pool, state_indices, num_tokens=None, out=Non
     import torch
     lib = load_library()
     _require_gpu(q, k, v, g, beta, state_pool, state_indices, num_tokens, out)
+    sobj, st = _stream(q.device, stream)
     if out is None and write_out:
-        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
-    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        with torch.cuda.stream(sobj):
+            out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     opts = options(stall_wave=stall_wave, stall_cycles=stall_cycles, gate_logits=gate_logits,
                    gate_lower_bound=gate_lower_bound, beta_logits=beta_logits, out_gate=out_gate,
                    norm_weight=norm_weight, norm_eps=norm_eps)
@@ -256,9 +278,10 @@ def prep(g, cu_seqlens=None, gamma=None, chunk: int = 64, stream=None):
     import torch
     lib = load_library()
     _require_gpu(g, cu_seqlens, gamma)
+    sobj, st = _stream(g.device, stream)
     if gamma is None:
-        gamma = torch.empty_like(g)
-    st = torch.cuda.current_stream(g.device).cuda_stream if stream is None else stream
+        with torch.cuda.stream(sobj):
+            gamma = torch.empty_like(g)
     dc = describe(cu_seqlens) if cu_seqlens is not None else None
     _check(lib.kda_prep(ctypes.byref(describe(g)), _ptr(dc), ctypes.c_int32(chunk), ctypes.byref(describe(gamma)),
                         ctypes.c_void_p(st)))

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -235,8 +236,10 @@ kda_status_t validate(const kda_tensor_t *q, const kda_tensor_t *k, const kda_te
 }
 
 // Output-norm options: out_gate like out (same shape, dtype; rows 4-element aligned), weight
-// fp32 [D] contiguous, eps > 0; neither may overlap out.
-kda_status_t check_out_norm(const kda_options_t *o, const kda_tensor_t *out, int64_t D)
+// fp32 [D] contiguous, eps > 0; neither may overlap out or the state the call writes
+// (prefill's final state, decode's pool): other workgroups read them while it is written.
+kda_status_t check_out_norm(const kda_options_t *o, const kda_tensor_t *out, int64_t D, const kda_tensor_t *state,
+                            const char *state_name)
 {
     if (!o || (!o->out_gate && !o->norm_weight)) return KDA_OK;
     kda_status_t st;
@@ -259,6 +262,9 @@ kda_status_t check_out_norm(const kda_options_t *o, const kda_tensor_t *out, int
     if (!(o->norm_eps > 0.f) || !(o->norm_eps < 1e30f)) return fail(KDA_ERR_UNSUPPORTED, "norm_eps must be positive");
     const Span so = span_of(out);
     if (overlaps(so, span_of(z)) || overlaps(so, span_of(w))) return fail(KDA_ERR_ALIAS, "out overlaps out_gate or norm_weight");
+    const Span ss = span_of(state);
+    if (overlaps(ss, span_of(z)) || overlaps(ss, span_of(w)))
+        return fail(KDA_ERR_ALIAS, "%s overlaps out_gate or norm_weight", state_name);
     return KDA_OK;
 }
 
@@ -271,31 +277,68 @@ bool env_on(const char *name)
     return v && *v && strcmp(v, "0") != 0;
 }
 
-std::mutex g_check_mu;                 // held for a whole check: one flag per device
+std::mutex g_check_mu;                 // held for a whole check: one flag buffer per device
 std::vector<int32_t *> g_check_flag;   // per device, allocated on first use
 
-kda_status_t check_cu_device(const int32_t *cu, int64_t N, int64_t Ttot, hipStream_t st)
+// The KDA_CHECK=1 device checks, before anything else of the call is enqueued: cu_seqlens
+// (when given: cu[0] == 0, non-decreasing, cu[N] == T_tot), the values of g (when given:
+// within [g.lo, g.hi], NaN refused) and decode's slot indices (when given: no two requests
+// name the same slot in [0, P)).  Zeroes three flags, runs the checks, reads the flags back
+// and synchronises the stream; returns KDA_ERR_SHAPE, KDA_ERR_RANGE or KDA_ERR_ALIAS.
+struct DeviceChecks {
+    const int32_t *cu = nullptr;
+    int64_t N = 0, Ttot = 0;
+    bool check_g = false;
+    kda::CheckG g{};
+    const int32_t *slots = nullptr;
+    int64_t R = 0, P = 0;
+};
+
+kda_status_t run_device_checks(const DeviceChecks &c, hipStream_t st)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    // the lock covers the launch and the read-back, so that checks on other streams of the
-    // device never write the flag in between
+    // the lock covers the launches and the read-back, so that checks on other streams of the
+    // device never write the flags in between
     std::lock_guard<std::mutex> lk(g_check_mu);
     if ((int)g_check_flag.size() <= dev) g_check_flag.resize(dev + 1, nullptr);
     if (!g_check_flag[dev] && (e = hipMalloc(&g_check_flag[dev], 256)) != hipSuccess) {
         g_check_flag[dev] = nullptr;
-        return hip_fail(e, "cu_seqlens check buffer");
+        return hip_fail(e, "device check buffer");
     }
     int32_t *flag = g_check_flag[dev];
-    int32_t h = 1;
-    if ((e = kda::launch_check_cu(cu, (int32_t)N, Ttot, flag, st)) != hipSuccess) return hip_fail(e, "cu_seqlens check");
-    if ((e = hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+    int32_t h[3] = {0, 0, 0};
+    if ((e = hipMemsetAsync(flag, 0, sizeof(h), st)) != hipSuccess) return hip_fail(e, "device check reset");
+    if (c.cu && (e = kda::launch_check_cu(c.cu, (int32_t)c.N, c.Ttot, flag, st)) != hipSuccess)
+        return hip_fail(e, "cu_seqlens check");
+    if (c.check_g && (e = kda::launch_check_g(c.g, flag + 1, st)) != hipSuccess) return hip_fail(e, "g range check");
+    if (c.slots && (e = kda::launch_check_slots(c.slots, (int32_t)c.R, (int32_t)c.P, flag + 2, st)) != hipSuccess)
+        return hip_fail(e, "slot check");
+    if ((e = hipMemcpyAsync(h, flag, sizeof(h), hipMemcpyDeviceToHost, st)) != hipSuccess ||
         (e = hipStreamSynchronize(st)) != hipSuccess)
-        return hip_fail(e, "cu_seqlens check read-back");
-    if (h) return fail(KDA_ERR_SHAPE, "cu_seqlens is not an offset array (cu[0] == 0, non-decreasing, cu[N] == %lld)",
-                       (long long)Ttot);
+        return hip_fail(e, "device check read-back");
+    if (h[0]) return fail(KDA_ERR_SHAPE, "cu_seqlens is not an offset array (cu[0] == 0, non-decreasing, cu[N] == %lld)",
+                          (long long)c.Ttot);
+    if (h[1]) {
+        if (c.g.lo == -INFINITY) return fail(KDA_ERR_RANGE, "g (logits) holds NaN");
+        return fail(KDA_ERR_RANGE, "g holds values outside [%g, %g] (or NaN)", (double)c.g.lo, (double)c.g.hi);
+    }
+    if (h[2]) return fail(KDA_ERR_ALIAS, "two requests name the same state slot with the state update on");
     return KDA_OK;
+}
+
+// The g view of a token-major problem for the range check: raw log decays must lie in the
+// range the kernels are guaranteed on, [-5, 0]; logits (gate_act) may be anything but NaN.
+kda::CheckG g_view(const kda_tensor_t *g, int64_t rows, int64_t rows_per_b, int64_t sb, int64_t st, int64_t sh,
+                   int64_t H, int64_t D, bool logits)
+{
+    kda::CheckG c{};
+    c.g = (const float *)g->data;
+    c.rows = rows; c.rows_per_b = rows_per_b; c.sb = sb; c.st = st; c.sh = sh; c.H = H; c.D = D;
+    c.lo = logits ? -INFINITY : -5.f;
+    c.hi = logits ? INFINITY : 0.f;
+    return c;
 }
 
 // ------------------------------------------------------------------ plan
@@ -371,7 +414,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     if (o && o->gate_act && !(o->gate_lower_bound >= -5.f && o->gate_lower_bound <= 0.f))
         return fail(KDA_ERR_UNSUPPORTED, "gate_lower_bound %g outside [-5, 0]", (double)o->gate_lower_bound);
     kda_status_t st;
-    if ((st = check_out_norm(o, P.tout, P.D))) return st;
+    if ((st = check_out_norm(o, P.tout, P.D, P.tsT, "final_state"))) return st;
     if (o && o->out_gate && !pl.pipe)
         return fail(KDA_ERR_UNSUPPORTED, "the output norm runs on the pipelined kernel (head size 128, bf16)");
     if (o && o->out_gate && 32 * o->out_gate->stride[o->out_gate->ndim - 3] * 2 + 1024 > (int64_t)INT32_MAX)
@@ -461,8 +504,12 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     const int64_t chains = P.N * P.H;
     if (chains == 0) return KDA_OK;
     char *wsb = (char *)ws;
-    if (P.tcu && env_on("KDA_CHECK")) {
-        kda_status_t s = check_cu_device((const int32_t *)P.tcu->data, P.N, P.Ttot, st);
+    if (env_on("KDA_CHECK")) {
+        DeviceChecks dc;
+        if (P.tcu) { dc.cu = (const int32_t *)P.tcu->data; dc.N = P.N; dc.Ttot = P.Ttot; }
+        dc.check_g = true;
+        dc.g = g_view(P.tg, P.Ttot, P.dense ? P.T : P.Ttot, P.g.sb, P.g.st, P.g.sh, P.H, P.D, o && o->gate_act);
+        kda_status_t s = run_device_checks(dc, st);
         if (s) return s;
     }
 
@@ -710,9 +757,7 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
         return fail(KDA_ERR_UNSUPPORTED, "gate_act %d / beta_act %d (0 or 1)", opts->gate_act, opts->beta_act);
     if (opts && opts->gate_act && !(opts->gate_lower_bound >= -5.f && opts->gate_lower_bound <= 0.f))
         return fail(KDA_ERR_UNSUPPORTED, "gate_lower_bound %g outside [-5, 0]", (double)opts->gate_lower_bound);
-    if ((st = check_out_norm(opts, out, D))) return st;
-    if (opts && opts->out_gate && overlaps(sp, span_of(opts->out_gate)))
-        return fail(KDA_ERR_ALIAS, "state_pool overlaps out_gate");
+    if ((st = check_out_norm(opts, out, D, state_pool, "state_pool"))) return st;
     if (R == 0 || (!out && !update_state)) return KDA_OK;
 
     kda::DecodeParams dp{};
@@ -743,6 +788,14 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
         dp.eps = opts->norm_eps;
     }
     const hipStream_t s = (hipStream_t)stream;
+    if (env_on("KDA_CHECK")) {
+        DeviceChecks dc;
+        dc.check_g = true;
+        dc.g = g_view(g, R * T, T, g->stride[0], g->stride[1], g->stride[2], H, D, opts && opts->gate_act);
+        if (update_state) { dc.slots = dp.idx; dc.R = R; dc.P = P; }
+        kda_status_t cs = run_device_checks(dc, s);
+        if (cs) return cs;
+    }
     hipError_t e = timed("kda_decode", s, [&] {
         return kda::launch_decode(dp, (int)D, q->dtype == KDA_F32, state_pool->dtype == KDA_BF16, s);
     });
@@ -789,7 +842,9 @@ kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int
     pp.chunks_per_seq = P.dense ? (int32_t)((P.T + chunk - 1) / chunk) : 0;
     if (P.N == 0 || (P.dense && P.T == 0)) return KDA_OK;
     if (cu_seqlens && env_on("KDA_CHECK")) {
-        kda_status_t s = check_cu_device(pp.cu, P.N, P.Ttot, (hipStream_t)stream);
+        DeviceChecks dc;
+        dc.cu = pp.cu; dc.N = P.N; dc.Ttot = P.Ttot;
+        kda_status_t s = run_device_checks(dc, (hipStream_t)stream);
         if (s) return s;
     }
     const int64_t nvc = P.dense ? P.B * pp.chunks_per_seq : (P.Ttot + chunk - 1) / chunk + P.N;
@@ -863,6 +918,7 @@ const char *kda_status_string(kda_status_t s)
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_RANGE: return "KDA_ERR_RANGE";
     }
     return "KDA_ERR_UNKNOWN";
 }

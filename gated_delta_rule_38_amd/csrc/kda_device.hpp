@@ -272,6 +272,15 @@ struct CombineParams {
     int32_t N, H, nseg;
 };
 
+// A token-major fp32 view for the debug-mode range check of g: element (row r, head h,
+// channel c) at g[b sb + t st + h sh + c] with r = b rows_per_b + t.
+struct CheckG {
+    const float *g;
+    int64_t rows, rows_per_b, sb, st, sh;
+    int64_t H, D;
+    float lo, hi;
+};
+
 // Sequence n's token range in the dense ([B,T,...]) or packed (cu_seqlens) layout.
 __device__ __forceinline__ void seq_range(const int32_t *cu, int n, int T, int64_t &t0, int &len, int64_t &bofs_sel) {
     if (cu) {

@@ -10,6 +10,10 @@ hipError_t launch_chunk(const ChunkParams &p, int D, bool fp32, int grid, bool s
 hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStream_t st);
 // Debug-mode check of cu_seqlens: *flag = 0 when cu[0] == 0, cu non-decreasing, cu[N] == Ttot.
 hipError_t launch_check_cu(const int32_t *cu, int32_t N, int64_t Ttot, int32_t *flag, hipStream_t st);
+// Debug-mode range check of g: *flag = 1 when any element lies outside [c.lo, c.hi] or is NaN.
+hipError_t launch_check_g(const CheckG &c, int32_t *flag, hipStream_t st);
+// Debug-mode check of decode slots: *flag = 1 when two requests name the same slot in [0, P).
+hipError_t launch_check_slots(const int32_t *idx, int32_t R, int32_t P, int32_t *flag, hipStream_t st);
 // PREP kernel over `nvc` virtual chunks x H heads.
 hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st);
 // COMBINE kernel over chains x D/16 value slabs.

@@ -10,6 +10,8 @@
 // sequential order the chunk kernel's fused scan uses, so both produce the same
 // bits.  With gate_act each g is first taken as a logit x and replaced by
 // gate_lb * sigmoid(x) (the same device function the fused scans use).
+#include <algorithm>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -79,6 +81,62 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int32_t *cu, int32_
 hipError_t launch_check_cu(const int32_t *cu, int32_t N, int64_t Ttot, int32_t *flag, hipStream_t st)
 {
     hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, st, cu, N, Ttot, flag);
+    return hipGetLastError();
+}
+
+// g range check (the debug mode): flag = 1 when any element of the token-major view lies
+// outside [lo, hi] or is NaN.  Element i of the view is (row r, head h, channel c) with row
+// r = b * rows_per_b + t.  A grid-stride loop with one element per thread and step; every
+// thread that finds a bad value stores the same 1 (the flag starts at 0).
+__global__ __launch_bounds__(256) void check_g_kernel(const CheckG c, int32_t *flag)
+{
+    const int64_t total = c.rows * c.H * c.D;
+    int bad = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t ch = i % c.D, rh = i / c.D;
+        const int64_t h = rh % c.H, r = rh / c.H;
+        const int64_t b = r / c.rows_per_b, t = r % c.rows_per_b;
+        const float x = c.g[b * c.sb + t * c.st + h * c.sh + ch];
+        bad |= !(x >= c.lo && x <= c.hi);
+    }
+    if (__syncthreads_or(bad) && threadIdx.x == 0) *flag = 1;
+}
+
+hipError_t launch_check_g(const CheckG &c, int32_t *flag, hipStream_t st)
+{
+    const int64_t total = c.rows * c.H * c.D;
+    if (total <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(check_g_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, flag);
+    return hipGetLastError();
+}
+
+// Decode slot check (the debug mode): flag = 1 when two requests name the same slot in
+// [0, P) (with the state update on, both would write it).  Thread i compares its slot with
+// every later request's, the indices staged in LDS 256 at a time: O(R^2) comparisons.
+__global__ __launch_bounds__(256) void check_slots_kernel(const int32_t *idx, int32_t R, int32_t P, int32_t *flag)
+{
+    __shared__ int32_t tile[256];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int vi = (i < R) ? idx[i] : -1;
+    const bool valid = vi >= 0 && vi < P;
+    int bad = 0;
+    for (int base = 0; base < R; base += 256) {
+        __syncthreads();
+        tile[threadIdx.x] = (base + (int)threadIdx.x < R) ? idx[base + threadIdx.x] : -1;
+        __syncthreads();
+        if (valid) {
+            const int jn = min(256, R - base);
+            for (int j = 0; j < jn; ++j) bad |= (base + j > i) & (tile[j] == vi);
+        }
+    }
+    if (__syncthreads_or(bad) && threadIdx.x == 0) *flag = 1;
+}
+
+hipError_t launch_check_slots(const int32_t *idx, int32_t R, int32_t P, int32_t *flag, hipStream_t st)
+{
+    if (R <= 1) return hipSuccess;
+    hipLaunchKernelGGL(check_slots_kernel, dim3((R + 255) / 256), dim3(256), 0, st, idx, R, P, flag);
     return hipGetLastError();
 }
 

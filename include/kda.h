@@ -13,11 +13,16 @@
  * S_{-1} = initial_state (zeros when NULL) and final_state = S after the last
  * token.  g is the per-token, per-channel natural-log decay; the kernels are
  * guaranteed on g in [-5, 0] (the production gate_lower_bound of the
- * cudnn-frontend PR's correctness section) -- values below -5 may overflow
- * the in-chunk gate factorisation.  beta is the value in (0, 1) (no sigmoid
- * is applied).  No scale is applied to q.  The kernels compute the 64-token
+ * cudnn-frontend PR's correctness section).  That range is a precondition the
+ * host cannot see (g is device memory): values below -5 can overflow the
+ * in-chunk gate factorisation to inf/NaN without any error being returned,
+ * unless KDA_CHECK=1 (below) checks them first.  beta is the value in (0, 1)
+ * (no sigmoid is applied).  No scale is applied to q.  The kernels compute the
  * chunked WY/UT form of this recurrence (TensorRT-LLM PR #19960 names the
- * "WY-form chunk"; "v64" in the cudnn-frontend kernel name gives the chunk).
+ * "WY-form chunk"): the production kernel (head size 128, bf16) takes 32-token
+ * chunks, the others (head size 64, the fp32 debug mode, variant 1) 64-token
+ * chunks ("v64" in the cudnn-frontend kernel name); results do not depend on
+ * the chunk length beyond rounding.
  *
  * Tensors (all pointers are DEVICE memory owned by the caller; the library
  * never frees or retains them):
@@ -49,12 +54,17 @@
  * stream) and return without synchronising or reading device data back.
  *
  * Environment (read on every call):
- *   KDA_CHECK=1  checks cu_seqlens on the device before anything else is enqueued
- *                (cu[0] == 0, non-decreasing, cu[N] == T_tot): one small kernel, a
- *                synchronisation of `stream` and a 4-byte read back; an invalid array
- *                returns KDA_ERR_SHAPE with nothing further launched.  Without it a
- *                cu_seqlens whose last offset exceeds the token extent makes the kernels
- *                read past the inputs.
+ *   KDA_CHECK=1  checks the device-side preconditions before anything else is enqueued
+ *                (a few small kernels, a synchronisation of `stream` and a 12-byte read
+ *                back; the first such call on a device allocates a 256-byte flag buffer):
+ *                  - cu_seqlens: cu[0] == 0, non-decreasing, cu[N] == T_tot, else
+ *                    KDA_ERR_SHAPE (without the check a last offset past the token extent
+ *                    makes the kernels read past the inputs);
+ *                  - every element of g in [-5, 0] (with gate_act: not NaN), else
+ *                    KDA_ERR_RANGE (kda_prefill, kda_prefill_ws, kda_decode);
+ *                  - kda_decode with update_state: no two requests name the same slot in
+ *                    [0, P), else KDA_ERR_ALIAS (O(R^2) comparisons on the device).
+ *                Nothing further is launched on a failed check.
  *   KDA_LOG=1    prints every plan (layout, chains, segments, kernel, chain order,
  *                workspace) to stderr.
  *   KDA_ORDER    chain order of a packed single-segment launch.  By default, when there
@@ -74,7 +84,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -85,7 +95,9 @@ typedef enum {
     KDA_ERR_ALIAS = 5,       /* forbidden overlap between outputs and inputs        */
     KDA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement         */
     KDA_ERR_WORKSPACE = 7,   /* workspace too small or allocation failed            */
-    KDA_ERR_HIP = 8          /* HIP runtime error while enqueueing                  */
+    KDA_ERR_HIP = 8,         /* HIP runtime error while enqueueing                  */
+    KDA_ERR_RANGE = 9        /* an input value outside its documented range         */
+                             /* (found by the KDA_CHECK=1 device checks)            */
 } kda_status_t;
 
 typedef enum { KDA_BF16 = 0, KDA_F32 = 1, KDA_I32 = 2 } kda_dtype_t;
@@ -140,7 +152,12 @@ typedef struct {
  * new size may call hipMalloc (after synchronising that stream when it replaces
  * a smaller buffer), so this entry point is not meant for graph capture -- use
  * kda_prefill_ws there.  Calls from several host threads are safe: the cache
- * stays locked until a call has enqueued its kernels.
+ * stays locked until a call has enqueued its kernels.  The workspace is sized
+ * exactly for the plan (segment maps and start states only when chains are cut
+ * into segments, nothing for a single-segment plan): the workspace review of the
+ * cudnn-frontend PR #1056 found that kernel's per-shape cache sized by N*H*nseg
+ * and kept for the process, hundreds of MB at N = 64, H = 32 that its
+ * single-segment path never touched.
  */
 kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
                          const kda_tensor_t *g, const kda_tensor_t *beta,
@@ -148,7 +165,11 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
                          kda_tensor_t *out, kda_tensor_t *final_state, void *stream);
 
 /* Bytes of device workspace kda_prefill_ws needs for these descriptors and
- * options (0 when the plan is a single chunk-kernel launch). */
+ * options: 0 when the plan is a single chunk-kernel launch; with nseg > 1 the
+ * segment maps and segment start states (fp32 K x V each); with the standalone
+ * PREP kernel the in-chunk gate sums (fp32, g's size).  Sized exactly for the
+ * plan, never by N*H alone (the workspace review of the cudnn-frontend PR
+ * #1056).  Validates everything kda_prefill_ws validates and launches nothing. */
 kda_status_t kda_prefill_workspace_size(const kda_tensor_t *q, const kda_tensor_t *k,
                                         const kda_tensor_t *v, const kda_tensor_t *g,
                                         const kda_tensor_t *beta,
@@ -158,8 +179,14 @@ kda_status_t kda_prefill_workspace_size(const kda_tensor_t *q, const kda_tensor_
                                         const kda_options_t *opts, size_t *bytes);
 
 /* kda_prefill with options and a caller-owned device workspace of at least
- * kda_prefill_workspace_size() bytes (256-byte aligned).  Allocates nothing and
- * never synchronises, so it can be captured into a HIP graph. */
+ * kda_prefill_workspace_size() bytes (256-byte aligned; NULL with size 0 when
+ * the plan needs none).  The workspace is scratch: its contents on entry do not
+ * matter and are undefined on return; it may not overlap any tensor argument.
+ * Allocates nothing and never synchronises (unless KDA_CHECK=1), so it can be
+ * captured into a HIP graph.  A workspace smaller than needed, or misaligned,
+ * returns KDA_ERR_WORKSPACE with nothing launched.  (The caller-owned buffer
+ * answers the workspace review of the cudnn-frontend PR #1056: the library
+ * keeps no per-shape buffers alive behind the caller's back.) */
 kda_status_t kda_prefill_ws(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
                             const kda_tensor_t *g, const kda_tensor_t *beta,
                             const kda_tensor_t *initial_state, const kda_tensor_t *cu_seqlens,
@@ -216,7 +243,9 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
                         void *stream);
 
 /* Frees the workspaces cached by kda_prefill on every device and stream (synchronising
- * each device first). */
+ * each device first), so that no scratch outlives the calls that need it (the workspace
+ * review of the cudnn-frontend PR #1056 found a process-lifetime cache there).  Later
+ * kda_prefill calls allocate again on demand. */
 void kda_release_cached_workspace(void);
 
 /* Kernel timing for measurement: when enabled, every kernel the library

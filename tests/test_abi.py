@@ -37,10 +37,11 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(5) == b"KDA_ERR_ALIAS"
     assert lib.kda_status_string(8) == b"KDA_ERR_HIP"
+    assert lib.kda_status_string(9) == b"KDA_ERR_RANGE"
 
 
 FAKE = 1 << 40   # a non-NULL, 256-aligned address; never dereferenced on the error paths
@@ -348,6 +349,8 @@ def test_output_norm_options_validated(lib):
     assert size(z(), w(dt=KDA_BF16)) == 2
     assert size(z(), w(), eps=0.0) == 6
     assert size(z(base=FAKE + 7 * gap), w()) == 5          # out_gate is out
+    assert size(z(base=FAKE + 8 * gap), w()) == 5          # out_gate inside final_state
+    assert size(z(), w(base=FAKE + 8 * gap + 4096)) == 5   # norm_weight inside final_state
     assert size(z(base=FAKE + 10 * gap + 2), w()) == 4     # misaligned rows
     assert size(z(), w(), variant=1) == 6                   # single-role kernel: unsupported
 
@@ -444,3 +447,23 @@ def test_planner_segment_counts(lib, B, H, T, nseg):
     assert st == 0, lib.kda_last_error()
     got = n.value // (B * H * 3 * D * D * 4) if n.value else 1
     assert got == nseg
+
+
+def test_decode_pool_may_not_overlap_norm_operands(lib):
+    """The pool is written while other workgroups read the output gate and the norm
+    weight: an overlap with either is refused on the host."""
+    gap = 1 << 32
+    for which in ("out_gate", "norm_weight"):
+        s = decode_set()
+        z = desc([4, 3, 2, 128], KDA_BF16, FAKE + 10 * gap)
+        w = desc([128], KDA_F32, FAKE + 11 * gap)
+        if which == "out_gate":
+            z = desc([4, 3, 2, 128], KDA_BF16, s["pool"].data + 4096)
+        else:
+            w = desc([128], KDA_F32, s["pool"].data + 4096)
+        opts = kda.options()
+        opts.out_gate, opts.norm_weight, opts.norm_eps = ctypes.pointer(z), ctypes.pointer(w), 1e-6
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        st = lib.kda_decode(r(s["q"]), r(s["k"]), r(s["v"]), r(s["g"]), r(s["beta"]), r(s["pool"]), r(s["idx"]),
+                            r(s["ntok"]), r(s["out"]), 1, ctypes.byref(opts), None)
+        assert st == 5 and b"state_pool" in lib.kda_last_error(), (which, st, lib.kda_last_error())

@@ -463,3 +463,40 @@ def test_decode_random_stalled_wave(kda, c):
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
     assert torch.equal(bits(res[0][0]), bits(res[1][0])) and torch.equal(bits(res[0][1]), bits(res[1][1]))
+
+
+def test_check_rejects_duplicate_slots_and_bad_gates(kda, monkeypatch):
+    """With KDA_CHECK=1 kda_decode refuses, before its kernel runs, two requests naming
+    the same slot when the state update is on (KDA_ERR_ALIAS), and a g outside [-5, 0]
+    (KDA_ERR_RANGE); the pool and out stay untouched.  Repeated slots are fine for the
+    verify pass and for skipped (out-of-range) indices; valid calls give the unchecked
+    bits."""
+    import torch
+    x, pool, idx, ntok = make_case(R=300, T=2, H=2, D=128, dtype="bf16", pool_dtype="f32", seed=71, P=400)
+    args = lambda p, i, g=None: (x["q"], x["k"], x["v"], x["g"] if g is None else g, x["beta"], p, i, ntok)
+    # rows past each request's token count are left untouched: both outputs start as the sentinel
+    p0 = pool.clone()
+    o0 = kda.decode(*args(p0, idx), out=torch.full_like(x["v"], -512.0))
+    monkeypatch.setenv("KDA_CHECK", "1")
+    p1 = pool.clone()
+    o1 = kda.decode(*args(p1, idx), out=torch.full_like(x["v"], -512.0))
+    torch.cuda.synchronize()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(p0.view(torch.int32), p1.view(torch.int32))
+    dup = idx.clone()
+    dup[250] = dup[3]                  # two live requests on one slot
+    say("KDA_CHECK decode duplicate slots")
+    p2 = pool.clone()
+    out = torch.full_like(x["v"], -512.0)
+    with pytest.raises(kda.KdaError) as e:
+        kda.decode(*args(p2, dup), out=out)
+    assert e.value.status == 5 and "slot" in str(e.value)
+    assert torch.all(out.float() == -512.0) and torch.equal(p2.view(torch.int32), pool.view(torch.int32))
+    kda.decode(*args(p2, dup), out=out, update_state=False)      # verify pass: repeats allowed
+    skip = idx.clone()
+    skip[10], skip[20] = -7, -7        # repeated out-of-range indices are skipped requests
+    kda.decode(*args(pool.clone(), skip))
+    g = x["g"].clone()
+    g[5, 1, 1, 3] = -6.0
+    with pytest.raises(kda.KdaError) as e:
+        kda.decode(*args(pool.clone(), idx, g))
+    assert e.value.status == 9

@@ -410,3 +410,124 @@ def test_gated_rmsnorm_pins_catch_planted_mistake(kind):
         return o * r * w * gate
     with pytest.raises(AssertionError):
         _gated_rmsnorm_pins(bad)
+
+
+# ----------------------------------------------------------- the parity metric itself
+def _rel_l2_pins(fn):
+    """Hand-computed values of the whole-tensor relative L2 error ||x - ref|| / ||ref||."""
+    ref = np.array([2.0, 3.0, 6.0])                       # ||ref|| = 7
+    # a difference of norm 0.07 (0.02, 0.03, -0.06) gives 0.01
+    assert abs(fn(ref + np.array([0.02, 0.03, -0.06]), ref) - 0.01) <= 1e-15
+    # x = ref (1 + eps) gives eps, at several scales of eps
+    for eps in (1e-1, 4e-3, 1e-6):
+        assert abs(fn(ref * (1.0 + eps), ref) - eps) <= 1e-12 * max(eps, 1e-3)
+    assert fn(np.zeros(3), ref) == 1.0                    # x = 0: the whole reference is error
+    assert fn(ref, ref) == 0.0
+    # the denominator is the reference's norm, not x's: x = 2 ref gives 1, ref against 2 ref 1/2
+    assert fn(2.0 * ref, ref) == 1.0
+    assert fn(ref, 2.0 * ref) == 0.5
+    # whole tensor, not a mean of per-row ratios: rows of norm 7 and 700 with errors of norm
+    # 0.07 and 0 give 0.07 / sqrt(7^2 + 700^2), not (0.01 + 0) / 2
+    big = np.stack([ref, 100.0 * ref])
+    err = np.stack([ref + np.array([0.02, 0.03, -0.06]), 100.0 * ref])
+    assert abs(fn(err, big) - 0.07 / np.sqrt(49.0 + 490000.0)) <= 1e-15
+    # any shape and dtype is flattened: a 3-D float32 tensor of 3-4-5 triangles
+    x3 = np.zeros((2, 2, 2), dtype=np.float32)
+    r3 = np.zeros((2, 2, 2), dtype=np.float32)
+    r3[0, 0, 0], r3[1, 1, 1] = 3.0, 4.0                   # ||r3|| = 5
+    x3[0, 0, 0], x3[1, 1, 1] = 3.0, 4.0
+    x3[0, 1, 0] = 0.5                                      # error norm 0.5
+    assert abs(fn(x3, r3) - 0.1) <= 1e-15
+
+
+def test_rel_l2_pins():
+    """The metric every parity verdict uses, against values worked by hand (a 2-3-6-7
+    quadruple, x = ref (1 + eps), x = 0, the asymmetry of the denominator, whole-tensor
+    rather than per-row aggregation, and a float32 3-D tensor)."""
+    _rel_l2_pins(oracle.rel_l2)
+    import torch
+    assert abs(oracle.rel_l2(torch.tensor([2.0, 3.0, 6.0]) * 1.004, torch.tensor([2.0, 3.0, 6.0])) - 4e-3) < 1e-6   # float32 inputs
+    # a zero reference: exact agreement is 0, anything else infinite
+    assert oracle.rel_l2(np.zeros(4), np.zeros(4)) == 0.0
+    assert oracle.rel_l2(np.ones(4), np.zeros(4)) == float("inf")
+
+
+@pytest.mark.parametrize("kind", ["no_sqrt", "swapped_arguments", "mean_of_rows", "max_abs", "l1"])
+def test_rel_l2_pins_catch_planted_mistake(kind):
+    """Plausible slips in the metric each fail the pins: a missing square root (which would
+    turn a 4e-3 error into 1.6e-5), the arguments swapped (dividing by ||x||), a mean of
+    per-row ratios, a max-abs ratio and an L1 ratio."""
+    def bad(x, ref):
+        x = np.asarray(x, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        d = x - ref
+        if kind == "no_sqrt":
+            return float(np.sum(d * d) / np.sum(ref * ref))
+        if kind == "swapped_arguments":
+            return float(np.linalg.norm(d) / np.linalg.norm(x)) if np.linalg.norm(x) else 1.0
+        if kind == "mean_of_rows":
+            d2, r2 = d.reshape(-1, d.shape[-1]), ref.reshape(-1, ref.shape[-1])
+            return float(np.mean(np.linalg.norm(d2, axis=-1) / np.linalg.norm(r2, axis=-1)))
+        if kind == "max_abs":
+            return float(np.abs(d).max() / np.abs(ref).max())
+        return float(np.abs(d).sum() / np.abs(ref).sum())
+    with pytest.raises(AssertionError):
+        _rel_l2_pins(bad)
+
+
+# ----------------------------------------------------------- the dense [B, T, H, D] layout
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_dense_layout_equals_packed(impl, oracle_lib):
+    """A dense [B, T, H, D] call gives, bit for bit, the packed call on the same values laid
+    out sequence after sequence (built here by concatenating the batch entries, not by the
+    oracle's own reshape) with cu = [0, T, 2T, ...]; a packed call with 4-D [1, T, H, D]
+    tensors gives the 3-D packed call's bits."""
+    fn = IMPLS[impl]
+    rng = np.random.default_rng(17)
+    B, T, H, DK, DV = 3, 11, 2, 5, 4
+    q, k = rng.standard_normal((B, T, H, DK)), rng.standard_normal((B, T, H, DK))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, DV))
+    g = -5.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, DK))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    s0 = 0.1 * rng.standard_normal((B, H, DK, DV))
+    od, sd = fn(q, k, v, g, beta, s0, None)
+    cat = lambda a: np.concatenate([a[b] for b in range(B)], axis=0)
+    cu = np.arange(B + 1, dtype=np.int64) * T
+    op, sp = fn(cat(q), cat(k), cat(v), cat(g), cat(beta), s0, cu)
+    assert od.shape == (B * T, H, DV) and sd.shape == (B, H, DK, DV)
+    assert np.array_equal(od, op) and np.array_equal(sd, sp)
+    o4, s4 = fn(cat(q)[None], cat(k)[None], cat(v)[None], cat(g)[None], cat(beta)[None], s0, cu)
+    assert np.array_equal(o4, op) and np.array_equal(s4, sp)
+    # and each batch entry alone is the same as its rows of the batched call
+    for b in range(B):
+        ob, sb = fn(q[b], k[b], v[b], g[b], beta[b], s0[b:b + 1], np.array([0, T]))
+        assert np.array_equal(ob, od[b * T:(b + 1) * T]) and np.array_equal(sb[0], sd[b])
+
+
+@pytest.mark.parametrize("kind", ["time_major", "batch_head_swap"])
+def test_dense_layout_pin_catches_planted_mistake(kind):
+    """A dense reshape that interleaves the batch and token axes, or swaps batch and head,
+    fails the dense-layout pin."""
+    def bad(q, k, v, g, beta, s0=None, cu=None):
+        if q.ndim == 4 and cu is None:
+            if kind == "time_major":
+                fix = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1)).reshape(a.shape[0] * a.shape[1], *a.shape[2:])
+            else:
+                fix = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 2)).reshape(a.shape[2] * a.shape[1], *a.shape[2:]) \
+                    if a.ndim == 4 else np.ascontiguousarray(np.swapaxes(a, 0, 2)).reshape(a.shape[2] * a.shape[1], a.shape[0])
+            B, T = q.shape[:2]
+            try:
+                return oracle.recurrence(fix(q), fix(k), fix(v), fix(g), fix(beta), s0, np.arange(B + 1) * T)
+            except (ValueError, IndexError):
+                return np.zeros(1), np.zeros(1)
+        return oracle.recurrence(q, k, v, g, beta, s0, cu)
+    saved = dict(IMPLS)
+    IMPLS["bad"] = bad
+    try:
+        with pytest.raises(AssertionError):
+            test_dense_layout_equals_packed("bad", None)
+    finally:
+        IMPLS.clear()
+        IMPLS.update(saved)
