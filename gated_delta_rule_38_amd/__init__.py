@@ -8,7 +8,8 @@ library's HIP kernels; there is no fallback.  Importing works without a GPU
 raises if the library or a GPU is missing.
 
 Names follow the C ABI: ``prefill`` (kda_prefill / kda_prefill_ws),
-``workspace_size``, ``prep`` (kda_prep), ``decode`` (kda_decode),
+``prefill_noalloc`` (kda_prefill_noalloc), ``workspace_size``, ``prep``
+(kda_prep), ``decode`` (kda_decode),
 ``profile_enable``/``profile_read``.
 """
 from __future__ import annotations
@@ -24,7 +25,7 @@ KDA_BF16, KDA_F32, KDA_I32 = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_LAYOUT",
           5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP",
           9: "KDA_ERR_RANGE"}
-EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prep", "kda_decode",
+EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prefill_noalloc", "kda_prep", "kda_decode",
            "kda_release_cached_workspace", "kda_profile_enable", "kda_profile_read",
            "kda_status_string", "kda_last_error", "kda_abi_version")
 
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill_ws.argtypes = [T, T, T, T, T, T, T, T, T, O, V, ctypes.c_size_t, V]
     lib.kda_prefill_ws.restype = ctypes.c_int
+    lib.kda_prefill_noalloc.argtypes = [T, T, T, T, T, T, T, T, T, O, V]
+    lib.kda_prefill_noalloc.restype = ctypes.c_int
     lib.kda_prefill_workspace_size.argtypes = [T, T, T, T, T, T, T, T, T, O, ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_prefill_workspace_size.restype = ctypes.c_int
     lib.kda_decode.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int32, O, V]
@@ -238,6 +241,28 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
         wptr, wbytes = aligned, workspace.numel() - (aligned - base)
     _check(lib.kda_prefill_ws(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.c_void_p(wptr),
                               ctypes.c_size_t(wbytes), ctypes.c_void_p(st)))
+    return out, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def prefill_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
+                    nseg: int = 0, prep: int = 0, variant: int = 0, gate_logits: bool = False,
+                    gate_lower_bound: float = -5.0, beta_logits: bool = False, out_gate=None, norm_weight=None,
+                    norm_eps: float = 1e-6, stream=None) -> Tuple:
+    """kda_prefill_noalloc: the prefill with its scratch in the library's fixed device array
+    (no allocation in the library).  ``out`` and ``final_state`` must be given: the call
+    allocates nothing, here either.  Returns (out, final_state)."""
+    lib = load_library()
+    _require_gpu(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    if out is None:
+        raise ValueError("prefill_noalloc allocates nothing: pass out (and final_state, or None to skip it)")
+    _, st = _stream(q.device, stream)
+    ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    opts = options(nseg, prep, variant=variant, gate_logits=gate_logits, gate_lower_bound=gate_lower_bound,
+                   beta_logits=beta_logits, out_gate=out_gate, norm_weight=norm_weight, norm_eps=norm_eps)
+    _check(lib.kda_prefill_noalloc(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.c_void_p(st)))
     return out, final_state
 
 

@@ -294,7 +294,9 @@ struct DeviceChecks {
     int64_t R = 0, P = 0;
 };
 
-kda_status_t run_device_checks(const DeviceChecks &c, hipStream_t st)
+// flags: device memory for the three flags, or NULL for the library's own buffer (allocated on
+// a device's first check).
+kda_status_t run_device_checks(const DeviceChecks &c, hipStream_t st, int32_t *flags)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -302,12 +304,15 @@ kda_status_t run_device_checks(const DeviceChecks &c, hipStream_t st)
     // the lock covers the launches and the read-back, so that checks on other streams of the
     // device never write the flags in between
     std::lock_guard<std::mutex> lk(g_check_mu);
-    if ((int)g_check_flag.size() <= dev) g_check_flag.resize(dev + 1, nullptr);
-    if (!g_check_flag[dev] && (e = hipMalloc(&g_check_flag[dev], 256)) != hipSuccess) {
-        g_check_flag[dev] = nullptr;
-        return hip_fail(e, "device check buffer");
+    int32_t *flag = flags;
+    if (!flag) {
+        if ((int)g_check_flag.size() <= dev) g_check_flag.resize(dev + 1, nullptr);
+        if (!g_check_flag[dev] && (e = hipMalloc(&g_check_flag[dev], 256)) != hipSuccess) {
+            g_check_flag[dev] = nullptr;
+            return hip_fail(e, "device check buffer");
+        }
+        flag = g_check_flag[dev];
     }
-    int32_t *flag = g_check_flag[dev];
     int32_t h[3] = {0, 0, 0};
     if ((e = hipMemsetAsync(flag, 0, sizeof(h), st)) != hipSuccess) return hip_fail(e, "device check reset");
     if (c.cu && (e = kda::launch_check_cu(c.cu, (int32_t)c.N, c.Ttot, flag, st)) != hipSuccess)
@@ -383,7 +388,10 @@ int choose_nseg(int64_t chains, int64_t C, int cus)
     return pick;
 }
 
-kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
+// max_bytes > 0 caps the workspace (the no-alloc entry point's fixed scratch): an automatic
+// segment count is lowered until the plan fits (one segment needs none); a forced segment
+// count or standalone PREP that does not fit is refused.
+kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_t max_bytes = 0)
 {
     const int64_t chains = P.N * P.H;
     const int variant = o ? o->variant : 0;
@@ -420,6 +428,30 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     if (o && o->out_gate && 32 * o->out_gate->stride[o->out_gate->ndim - 3] * 2 + 1024 > (int64_t)INT32_MAX)
         return fail(KDA_ERR_UNSUPPORTED, "out_gate token stride too large for the pipelined kernel");
     pl.standalone_prep = prep == 1;   // otherwise every chunk-kernel pass scans its own chunks
+    auto layout = [&](int nseg) {
+        size_t off = 0;
+        if (pl.standalone_prep) {
+            pl.off_gamma = off;
+            off += align256((size_t)P.Ttot * P.H * P.D * 4);
+        }
+        if (nseg > 1) {
+            const size_t dd = (size_t)P.D * P.D * 4;
+            pl.off_maps = off;
+            off += align256((size_t)chains * nseg * 2 * dd);
+            pl.off_start = off;
+            off += align256((size_t)chains * nseg * dd);
+        }
+        return off;
+    };
+    pl.bytes = layout(pl.nseg);
+    if (max_bytes && pl.bytes > max_bytes) {
+        const bool forced = (o && o->nseg > 0) || pl.standalone_prep;
+        if (forced)
+            return fail(KDA_ERR_WORKSPACE, "the plan needs %zu bytes of scratch, more than the %zu the no-alloc entry point has",
+                        pl.bytes, max_bytes);
+        while (pl.nseg > 1 && layout(pl.nseg) > max_bytes) --pl.nseg;
+        pl.bytes = layout(pl.nseg);
+    }
     // Chain order.  With more chains than CUs, workgroups start in launch order as CUs free up,
     // so a packed batch of mixed lengths finishes sooner when its longest sequences start first
     // (longest-processing-time order); with every chain resident at once the order is moot.
@@ -430,19 +462,6 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl)
     if (ord && strcmp(ord, "natural") == 0) pl.lpt = false;
     else if (ord && strcmp(ord, "longest") == 0) pl.lpt = lpt_ok;
     else pl.lpt = lpt_ok && chains > device_cus();
-    size_t off = 0;
-    if (pl.standalone_prep) {
-        pl.off_gamma = off;
-        off += align256((size_t)P.Ttot * P.H * P.D * 4);
-    }
-    if (pl.nseg > 1) {
-        const size_t dd = (size_t)P.D * P.D * 4;
-        pl.off_maps = off;
-        off += align256((size_t)chains * pl.nseg * 2 * dd);
-        pl.off_start = off;
-        off += align256((size_t)chains * pl.nseg * dd);
-    }
-    pl.bytes = off;
     if (env_on("KDA_LOG"))
         fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d kernel=%s chunk=%d prep=%s order=%s workspace=%zu B\n",
                 (long long)P.N, (long long)P.H, (long long)P.D, P.dense ? "dense" : "packed", (long long)chains,
@@ -496,7 +515,10 @@ hipError_t timed(const char *name, hipStream_t st, F &&launch)
 }
 
 // --------------------------------------------------------------- enqueue
-kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void *ws, size_t ws_bytes, hipStream_t st)
+// check_flags: where the KDA_CHECK=1 device checks keep their flags (NULL: the library's own
+// buffer, allocated on a device's first check).
+kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void *ws, size_t ws_bytes, hipStream_t st,
+                 int32_t *check_flags = nullptr)
 {
     if (ws_bytes < pl.bytes || (pl.bytes && !ws))
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.bytes);
@@ -509,7 +531,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
         if (P.tcu) { dc.cu = (const int32_t *)P.tcu->data; dc.N = P.N; dc.Ttot = P.Ttot; }
         dc.check_g = true;
         dc.g = g_view(P.tg, P.Ttot, P.dense ? P.T : P.Ttot, P.g.sb, P.g.st, P.g.sh, P.H, P.D, o && o->gate_act);
-        kda_status_t s = run_device_checks(dc, st);
+        kda_status_t s = run_device_checks(dc, st, check_flags);
         if (s) return s;
     }
 
@@ -616,9 +638,54 @@ struct CachedWs {
 };
 std::vector<CachedWs> g_ws;
 
+// ------------------------------------------------------ the no-alloc entry point's scratch
+// kda_prefill_noalloc keeps its workspace in this fixed array: KDA_NOALLOC_SCRATCH_BYTES for the
+// plan, then 256 bytes for the KDA_CHECK=1 flags.  Every GPU the library runs on holds its own
+// copy, at its own address, from the code object's load until the process ends.  In host code
+// the name `scratch` is a host-side stand-in, not a device address, so it is never passed to a
+// kernel or a copy: the address is asked of the runtime once per device and kept.
+constexpr size_t NOALLOC_FLAGS = 256;
+static __device__ __align__(256) char scratch[(size_t)KDA_NOALLOC_SCRATCH_BYTES + NOALLOC_FLAGS];
+
+std::mutex g_scratch_mu;
+std::vector<char *> g_scratch_ptr;     // per device: scratch's device address
+
+kda_status_t scratch_address(char *&ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return hip_fail(e, "scratch address");
+        if (!p) return fail(KDA_ERR_HIP, "scratch address: the runtime returned NULL");
+        g_scratch_ptr[dev] = (char *)p;
+    }
+    ptr = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kda_status_t kda_prefill_noalloc(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                                 const kda_tensor_t *g, const kda_tensor_t *beta, const kda_tensor_t *initial_state,
+                                 const kda_tensor_t *cu_seqlens, kda_tensor_t *out, kda_tensor_t *final_state,
+                                 const kda_options_t *opts, void *stream)
+{
+    Problem P;
+    kda_status_t st = validate(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, P);
+    if (st) return st;
+    Plan pl;
+    if ((st = make_plan(P, opts, pl, (size_t)KDA_NOALLOC_SCRATCH_BYTES))) return st;
+    char *ws = nullptr;
+    if ((st = scratch_address(ws))) return st;
+    return run(P, pl, opts, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream,
+               (int32_t *)(ws + (size_t)KDA_NOALLOC_SCRATCH_BYTES));
+}
 
 kda_status_t kda_prefill_workspace_size(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
                                         const kda_tensor_t *g, const kda_tensor_t *beta,
@@ -793,7 +860,7 @@ kda_status_t kda_decode(const kda_tensor_t *q, const kda_tensor_t *k, const kda_
         dc.check_g = true;
         dc.g = g_view(g, R * T, T, g->stride[0], g->stride[1], g->stride[2], H, D, opts && opts->gate_act);
         if (update_state) { dc.slots = dp.idx; dc.R = R; dc.P = P; }
-        kda_status_t cs = run_device_checks(dc, s);
+        kda_status_t cs = run_device_checks(dc, s, nullptr);
         if (cs) return cs;
     }
     hipError_t e = timed("kda_decode", s, [&] {
@@ -844,7 +911,7 @@ kda_status_t kda_prep(const kda_tensor_t *g, const kda_tensor_t *cu_seqlens, int
     if (cu_seqlens && env_on("KDA_CHECK")) {
         DeviceChecks dc;
         dc.cu = pp.cu; dc.N = P.N; dc.Ttot = P.Ttot;
-        kda_status_t s = run_device_checks(dc, (hipStream_t)stream);
+        kda_status_t s = run_device_checks(dc, (hipStream_t)stream, nullptr);
         if (s) return s;
     }
     const int64_t nvc = P.dense ? P.B * pp.chunks_per_seq : (P.Ttot + chunk - 1) / chunk + P.N;

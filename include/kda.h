@@ -195,6 +195,28 @@ kda_status_t kda_prefill_ws(const kda_tensor_t *q, const kda_tensor_t *k, const 
                             void *stream);
 
 /*
+ * kda_prefill_noalloc -- kda_prefill_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and options without a workspace, and no allocation of any kind.  Its
+ * scratch (segment maps, segment start states, standalone-PREP gate sums, the KDA_CHECK=1
+ * flags) is a fixed device array of the library's, KDA_NOALLOC_SCRATCH_BYTES (64 MiB) plus
+ * 256 bytes, of which every GPU the library runs on holds one copy until the process ends.
+ * With an automatic segment count the planner lowers the count until the plan fits (a single
+ * segment needs no scratch), so results may then differ from kda_prefill_ws's within the
+ * segmented path's tolerance; a forced segment count or standalone PREP whose scratch does
+ * not fit returns KDA_ERR_WORKSPACE with nothing launched.  Nothing in the scratch needs to
+ * start at zero.  Every call on a GPU shares that GPU's array: two calls whose kernels may
+ * overlap on one GPU (different streams, no ordering between them) race on it and must be
+ * serialised by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kda_status_t kda_prefill_noalloc(const kda_tensor_t *q, const kda_tensor_t *k, const kda_tensor_t *v,
+                                 const kda_tensor_t *g, const kda_tensor_t *beta,
+                                 const kda_tensor_t *initial_state, const kda_tensor_t *cu_seqlens,
+                                 kda_tensor_t *out, kda_tensor_t *final_state,
+                                 const kda_options_t *opts, void *stream);
+
+/*
  * kda_prep -- the standalone PREP kernel: the in-chunk inclusive cumulative sum
  * of g over `chunk`-token chunks (32 or 64) that restart at every sequence
  * start (the "gap-safe virtual chunk mapping" of the cudnn-frontend PR's
