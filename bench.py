@@ -2,20 +2,26 @@
 
     python bench.py [--steps K] [--warmup W] [--config varlen|large|eqlen|long|varlen_padded|varlen_h64|tiny]
     python bench.py --config decode|decode_bf16|verify4        (the recurrent decode kernel)
+    python bench.py --peak                                     (practical HBM and MFMA ceilings)
 
 One step is one kda_prefill call over the whole workload (every kernel of the
-hot path), with inputs already resident in HBM; `value` is the back-to-back
-("pipelined") rate, and `timing_modes` adds per-call (synchronised, host
-dispatch included) and HIP-graph times.  The correctness gate runs the oracle
-on the host while the GPU idles; afterwards the step runs untimed for at least
-0.2 s (`settle`) so that the GPU is back in its steady state before the W
-warm-up steps and the K timed steps (with only a few steps of warm-up, the
-first milliseconds after the idle ran ~13% slower on the varlen workload).  Prints ONE JSON line:
-throughput in tokens/s, the roofline of the dominant kernel (its duration from
-HIP events recorded by the library on the launch stream over the timed region),
-and the float64 oracle timed on the host cores on a bounded sample of the same
-workload.  Correctness is checked against the oracle on sampled chains before
-anything is timed.
+hot path), with inputs already resident in HBM.  Before anything is timed the
+call is checked against the float64 oracle on sampled chains (outputs poisoned
+first; a second call into differently poisoned outputs must give the same
+bits; a HIP-graph replay with a changed q is checked against the oracle on the
+new q).  Then the step runs untimed for at least 0.2 s (`settle`: the GPU
+returns to steady clocks after the host-side oracle), W warm-up steps, and K
+timed steps: `value` is their back-to-back ("pipelined") rate.  `roofline` and
+`mfma` come from the library's HIP events on the launch stream over those K
+steps, summed over every launch of a call (one launch on a single-segment
+plan; segment build, COMBINE and segment output on a segmented one) with the
+per-kernel split in `kernel.split`.  `timing_modes` gives the three modes of
+the cudnn-frontend KDA PR (pipelined, per call, HIP graph of 8 calls), each
+over 7 timing groups as median / p10 / p90.  `cpu_baseline` is the float64
+oracle on the host's cores (and on one thread) over a bounded sample.  The
+default (varlen, the H = 32 workload of the headline metric) also measures the
+large workload (B=16, H=64, T=8192; the roofline workload) the same way, in
+`large`.  Prints ONE JSON line.
 """
 import argparse
 import hashlib
@@ -26,6 +32,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402  (seeded synthetic inputs; no step of the method)
 
 METRIC = "KDA prefill tokens/sec at H=32,d=128 bf16; MFMA util % and HBM GB/s"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
@@ -50,7 +58,9 @@ def algorithmic(w):
 
 
 KERNEL_SOURCES = {"chunk_kernel": ("kda_chunk_pipe.hip", "kda_device.hpp"),
-                  "decode_kernel": ("kda_decode.hip", "kda_device.hpp")}
+                  "decode_kernel": ("kda_decode.hip", "kda_device.hpp"),
+                  # a segmented call: both chunk-kernel passes and COMBINE
+                  "whole_call": ("kda_chunk_pipe.hip", "kda_combine.hip", "kda_device.hpp")}
 
 
 def source_sha(kernel="chunk_kernel"):
@@ -64,8 +74,8 @@ def source_sha(kernel="chunk_kernel"):
 
 
 def traffic_from_profile(config, kernel="chunk_kernel"):
-    """HBM bytes per launch of the kernel from the committed rocprofv3 PMC
-    summary, or None when absent or taken on a different kernel source."""
+    """HBM bytes per launch of the kernel (per call for "whole_call") from the committed
+    rocprofv3 PMC summary, or None when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -75,25 +85,27 @@ def traffic_from_profile(config, kernel="chunk_kernel"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, budget_s):
-    """The float64 oracle (C, OpenMP over chains) on a bounded sample of the
-    workload's chains; returns tokens/s scaled to the whole workload's H."""
+def _host_info():
+    """Host CPU facts for the baseline record: the model name, the logical CPU count and the
+    CPUs this process may run on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": affinity}
+
+
+def _gather_chains(x, w, picked):
+    """The picked (sequence, head) chains as one packed float64-ready problem with H = 1."""
     import numpy as np
-    import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
-    # ~1.5 GFLOP/s per core for the scalar fp64 loop: pick chains worth ~budget_s
-    per_th = 7.0 * w.D * w.D
-    target_th = budget_s * threads * 1.5e9 / per_th
-    rng = np.random.default_rng(0)
-    order = [(n, h) for n in range(w.n_seq) for h in range(w.H)]
-    rng.shuffle(order)
-    picked, th = [], 0
-    for n, h in order:
-        if th >= target_th:
-            break
-        picked.append((n, h))
-        th += w.lengths[n]
-    # gather the picked chains as one packed problem with H = 1
     import torch
     qs, ks, vs, gs, bs, ss, lens = [], [], [], [], [], [], []
     cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu()
@@ -108,16 +120,49 @@ def cpu_baseline(x, w, budget_s):
         ss.append(x["initial_state"][n, h].cpu() if x["initial_state"] is not None else torch.zeros(w.D, w.D))
         lens.append(w.lengths[n])
     cat = lambda lst: torch.cat(lst)[:, None]
-    s0 = torch.stack(ss)[:, None]
     cuh = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    args = (cat(qs), cat(ks), cat(vs), cat(gs), cat(bs), s0)
+    return (cat(qs), cat(ks), cat(vs), cat(gs), cat(bs), torch.stack(ss)[:, None]), cuh, int(sum(lens))
+
+
+def cpu_baseline(x, w, budget_s):
+    """The float64 oracle (C, OpenMP over chains) on a bounded sample of the workload's
+    chains, on the host's cores (OMP_NUM_THREADS when set, else every logical CPU), and
+    on one thread over a smaller sample; tokens/s scaled to the whole workload's H."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    per_th = 7.0 * w.D * w.D             # ~1.5 GFLOP/s per core for the scalar fp64 loop
+
+    def pick(seconds, nthreads, seed):
+        target_th = seconds * nthreads * 1.5e9 / per_th
+        rng = np.random.default_rng(seed)
+        order = [(n, h) for n in range(w.n_seq) for h in range(w.H) if w.lengths[n]]
+        rng.shuffle(order)
+        picked, th = [], 0
+        for n, h in order:
+            if th >= target_th:
+                break
+            picked.append((n, h))
+            th += w.lengths[n]
+        return picked
+
+    picked = pick(budget_s, threads, 0)
+    args, cuh, token_heads = _gather_chains(x, w, picked)
     t = time.perf_counter()
     _, _, used = oracle.run_c(*args, cuh, threads=threads, return_threads=True)
     dt = time.perf_counter() - t
-    token_heads = int(sum(lens))
-    return {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{len(picked)} of {w.n_seq * w.H} (sequence, head) chains, {token_heads} token-heads, "
-                      f"float64 C recurrence, {dt:.1f} s; tokens/s = token-heads / H / seconds"}
+    one = pick(max(1.0, budget_s / 4), 1, 1)
+    args1, cuh1, th1 = _gather_chains(x, w, one)
+    t = time.perf_counter()
+    oracle.run_c(*args1, cuh1, threads=1)
+    dt1 = time.perf_counter() - t
+    rec = {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"{len(picked)} of {w.n_seq * w.H} (sequence, head) chains, {token_heads} token-heads, "
+                     f"float64 C recurrence, {dt:.1f} s on {used} threads; tokens/s = token-heads / H / seconds",
+           "one_thread": {"value": th1 / w.H / dt1, "unit": "tokens/s",
+                          "sample": f"{len(one)} chains, {th1} token-heads, {dt1:.1f} s"}}
+    rec.update(_host_info())
+    return rec
 
 
 def work_balance(w, cus=256, chunk=32):
@@ -147,28 +192,122 @@ def work_balance(w, cus=256, chunk=32):
             "mean_chunks_per_cu": per_cu, "occupancy_bound": (per_cu / makespan) if makespan else None}
 
 
-def correctness_gate(kda, x, w, out, fin):
+def sample_chains(w, count, seed=0):
+    """(sequence, head) chains the oracle checks: the first and the last, the chains on either
+    side of the 2^31-byte offset of g (the first whose g rows start at or past it and the
+    last wholly below it, where 32-bit byte offsets would wrap) and the chain of the highest
+    g offset, then seeded random ones up to `count`."""
+    import numpy as np
+    H, D = w.H, w.D
+    def g_range(n, h):          # byte range of chain (n, h) in a contiguous fp32 g
+        if w.dense:
+            T = w.lengths[0]
+            lo = ((n * T) * H + h) * D * 4
+            hi = ((n * T + T - 1) * H + h) * D * 4 + D * 4
+        else:
+            t0 = int(sum(w.lengths[:n]))
+            lo = (t0 * H + h) * D * 4
+            hi = ((t0 + max(w.lengths[n], 1) - 1) * H + h) * D * 4 + D * 4
+        return lo, hi
+    live = [(n, h) for n in range(w.n_seq) for h in range(H) if w.lengths[n]]
+    chains = [live[0], live[-1]]
+    ranges = {c: g_range(*c) for c in live}
+    above = [c for c in live if ranges[c][0] >= 1 << 31]
+    below = [c for c in live if ranges[c][0] < 1 << 31]
+    if above:
+        chains.append(min(above, key=lambda c: ranges[c][0]))
+        chains.append(max(below, key=lambda c: ranges[c][0]))
+    chains.append(max(live, key=lambda c: ranges[c][1]))
+    rng = np.random.default_rng(seed)
+    out = list(dict.fromkeys(chains))
+    while len(out) < min(count, len(live)):
+        c = live[int(rng.integers(len(live)))]
+        if c not in out:
+            out.append(c)
+    return out
+
+
+def chain_errors(x, w, out, fin, chains, q=None):
+    """Worst rel-L2 (out, final state) against the oracle over the given chains."""
     import numpy as np
     import oracle
     cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu()
-    worst = 0.0
-    for n, h in [(0, 0), (w.n_seq - 1, w.H - 1)]:
+    q_src = x["q"] if q is None else q
+    worst_o = worst_s = 0.0
+    for n, h in chains:
         if cu is None:
-            sl, osl = (lambda t: t[n, :, h:h + 1]), (lambda t: t[n, :, h:h + 1])
+            sl = lambda t: t[n, :, h:h + 1]
         else:
             a, b = int(cu[n]), int(cu[n + 1])
-            sl = osl = (lambda t: t[a:b, h:h + 1])
+            sl = lambda t: t[a:b, h:h + 1]
         s0 = None if x["initial_state"] is None else x["initial_state"][n:n + 1, h:h + 1].cpu()
-        q = sl(x["q"]).cpu()
-        o_ref, s_ref = oracle.run_c(q, sl(x["k"]).cpu(), sl(x["v"]).cpu(), sl(x["g"]).cpu(), sl(x["beta"]).cpu(),
-                                    s0, np.array([0, q.shape[0]]))
-        eo = oracle.rel_l2(osl(out).float().cpu().numpy().reshape(o_ref.shape), o_ref)
-        es = oracle.rel_l2(fin[n:n + 1, h:h + 1].cpu().numpy(), s_ref)
-        worst = max(worst, eo, es)
+        qq = sl(q_src).cpu()
+        o_ref, s_ref = oracle.run_c(qq, sl(x["k"]).cpu(), sl(x["v"]).cpu(), sl(x["g"]).cpu(), sl(x["beta"]).cpu(),
+                                    s0, np.array([0, qq.shape[0]]))
+        og = sl(out).float().cpu().numpy().reshape(o_ref.shape)
+        sg = fin[n:n + 1, h:h + 1].float().cpu().numpy()
+        if not (np.isfinite(og).all() and np.isfinite(sg).all()):
+            return float("inf"), float("inf")
+        worst_o = max(worst_o, oracle.rel_l2(og, o_ref) if o_ref.size else 0.0)
+        worst_s = max(worst_s, oracle.rel_l2(sg, s_ref))
+    return worst_o, worst_s
+
+
+def bits_equal(a, b):
+    import torch
+    view = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    return bool(torch.equal(view(a), view(b)))
+
+
+def pre_timing_checks(kda, x, w, out, fin, chains):
+    """Correctness before anything is timed (the method of the cudnn-frontend KDA PR's review:
+    an fp64 oracle, poisoned outputs and a changed-q replay):
+      1. outputs poisoned with NaN, one call, the sampled chains against the float64 oracle;
+      2. outputs poisoned with another pattern, one more call: the same bits as (1);
+      3. kda_prefill_ws captured in a HIP graph over a q buffer, the buffer refilled with a
+         new q, the graph replayed: its sampled chains against the oracle on the new q."""
+    import torch
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
+    out.fill_(float("nan"))
+    fin.fill_(float("nan"))
+    kda.prefill(*args, out=out, final_state=fin)
+    torch.cuda.synchronize()
+    eo, es = chain_errors(x, w, out, fin, chains)
     tol = 5e-3 if w.dtype == "bf16" else 1e-4
-    if not worst <= tol:
-        raise SystemExit(f"correctness gate failed: sampled rel-L2 {worst:.3e} > {tol}")
-    return worst
+    out2 = torch.full_like(out, -3.0e38)
+    fin2 = torch.full_like(fin, 7.0)
+    kda.prefill(*args, out=out2, final_state=fin2)
+    torch.cuda.synchronize()
+    repeat_bits = bits_equal(out, out2) and bits_equal(fin, fin2)
+    # changed-q replay of a captured call
+    qbuf = x["q"].clone()
+    ws_bytes = kda.workspace_size(qbuf, *args[1:], out=out2, final_state=fin2)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=out.device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.prefill(qbuf, *args[1:], out=out2, final_state=fin2, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.prefill(qbuf, *args[1:], out=out2, final_state=fin2, workspace=ws)
+    gen = torch.Generator(device=out.device).manual_seed(12345)
+    newq = torch.randn(qbuf.shape, generator=gen, device=out.device, dtype=torch.float32)
+    qbuf.copy_((newq / torch.linalg.vector_norm(newq, dim=-1, keepdim=True)).to(qbuf.dtype))
+    del newq
+    out2.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    ro, rs = chain_errors(x, w, out2, fin2, chains[:4], q=qbuf)
+    del graph, qbuf, out2, fin2, ws
+    torch.cuda.empty_cache()
+    ok = eo <= tol and es <= tol and repeat_bits and ro <= tol and rs <= tol
+    rec = {"oracle_chains": len(chains), "rel_l2_out_max": eo, "rel_l2_state_max": es, "tolerance": tol,
+           "poisoned_repeat_bit_identical": repeat_bits, "changed_q_graph_replay": {"chains": min(4, len(chains)),
+           "rel_l2_out_max": ro, "rel_l2_state_max": rs}}
+    if not ok:
+        raise SystemExit(f"correctness checks failed before timing: {json.dumps(rec)}")
+    return rec
 
 
 DECODE_METRIC = "KDA decode tokens/sec at H=32,d=128 bf16 against a state pool; HBM GB/s"
@@ -248,19 +387,38 @@ def decode_main(a, w):
     print(json.dumps(rec))
 
 
-def timing_modes(kda, x, w, out, fin, calls=8, reps=5):
-    """The other two timing modes the cudnn-frontend KDA PR quotes beside the
-    back-to-back one: per call (each call synchronised, host dispatch included) and a
-    HIP graph of `calls` kda_prefill_ws launches replayed as one.  Medians in ms."""
+def _stats(vals):
+    import numpy as np
+    v = np.asarray(vals, dtype=np.float64)
+    return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)), "p90": float(np.percentile(v, 90)),
+            "groups": len(vals)}
+
+
+def timing_modes(kda, x, w, out, fin, steps, groups=7, calls=8):
+    """The three timing modes the cudnn-frontend KDA PR quotes, each over `groups` timing
+    groups, as median / p10 / p90 of the per-call milliseconds:
+      pipelined -- `steps` calls back to back, timed by events on the stream around the group;
+      per_call  -- `calls` calls each synchronised (host dispatch included), the group's median;
+      graph     -- `calls` kda_prefill_ws launches captured in one HIP graph, one replay per group."""
     import statistics
     import torch
     args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
-    per_call = []
-    for _ in range(calls * reps):
-        t = time.perf_counter()
-        kda.prefill(*args, out=out, final_state=fin)
+    pipelined, per_call, per_graph = [], [], []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            kda.prefill(*args, out=out, final_state=fin)
+        e1.record()
         torch.cuda.synchronize()
-        per_call.append((time.perf_counter() - t) * 1e3)
+        pipelined.append(e0.elapsed_time(e1) / steps)
+        one = []
+        for _ in range(calls):
+            t = time.perf_counter()
+            kda.prefill(*args, out=out, final_state=fin)
+            torch.cuda.synchronize()
+            one.append((time.perf_counter() - t) * 1e3)
+        per_call.append(statistics.median(one))
     ws_bytes = kda.workspace_size(*args, out=out, final_state=fin)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=out.device)
     s = torch.cuda.Stream()
@@ -274,16 +432,15 @@ def timing_modes(kda, x, w, out, fin, calls=8, reps=5):
             kda.prefill(*args, out=out, final_state=fin, workspace=ws)
     graph.replay()
     torch.cuda.synchronize()
-    per_graph = []
-    for _ in range(reps):
+    for _ in range(groups):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         graph.replay()
         e1.record()
         torch.cuda.synchronize()
         per_graph.append(e0.elapsed_time(e1) / calls)
-    return {"per_call_ms": statistics.median(per_call), "graph_ms": statistics.median(per_graph),
-            "graph_calls": calls}
+    return {"pipelined_ms": _stats(pipelined), "per_call_ms": _stats(per_call), "graph_ms": _stats(per_graph),
+            "graph_calls": calls, "pipelined_calls_per_group": steps, "per_call_calls_per_group": calls}
 
 
 def settle(step, seconds=0.2):
@@ -295,14 +452,126 @@ def settle(step, seconds=0.2):
         torch.cuda.synchronize()
 
 
+def kernel_record(w, prof, steps):
+    """Roofline, matrix-core rate and per-kernel split of one step from the library's own
+    HIP events: {kernel name: (launches, summed ms)} over `steps` steps.  The whole call is
+    every launch of the step (one launch on a single-segment plan; segment build, COMBINE
+    and segment output on a segmented one), so the HBM and MFMA fractions are those of the
+    call; the split gives each kernel's share."""
+    bytes_, flops, per_th = algorithmic(w)
+    total_ms = sum(ms for _, ms in prof.values()) / steps
+    launches = sum(n for n, _ in prof.values()) // steps
+    achieved = bytes_ / (total_ms * 1e-3) / 1e9
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    tflops = flops / (total_ms * 1e-3) / 1e12
+    split = [{"name": name, "launches_per_step": n // steps, "avg_ms": ms / max(1, n), "ms_per_step": ms / steps,
+              "share": (ms / steps) / total_ms} for name, (n, ms) in prof.items()]
+    tr = traffic_from_profile(w.name) if launches == 1 else traffic_from_profile(w.name, "whole_call")
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": tr}
+    mfma = {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
+            "flops_per_call": flops,
+            # the most the matrix cores can be fed when the call moves its algorithmic bytes at the
+            # HBM peak (flops / bytes x 8 TB/s)
+            "frac_ceiling_at_hbm_peak": (flops / bytes_) * HBM_PEAK_GBS * 1e9 / (mfma_peak * 1e12)}
+    kern = {"name": "kda_chunk" if launches == 1 else "whole call", "scope": "one launch" if launches == 1 else
+            f"{launches} launches per call", "avg_ms": total_ms, "launches_per_step": launches,
+            "algorithmic_bytes_per_launch" if launches == 1 else "algorithmic_bytes_per_call": bytes_,
+            "bytes_per_token_head": per_th, "kernel_source_sha": source_sha("chunk_kernel"), "split": split}
+    return roof, mfma, kern
+
+
+def prefill_record(kda, w, steps, warmup, groups, checks_count):
+    """Everything measured on one prefill workload: the pre-timing checks, the K timed steps
+    (wall clock, and the library's HIP events for the roofline), and the timing groups."""
+    import torch
+    dev = torch.device("cuda:0")
+    x = workloads.make_inputs(w, device=dev)
+    out = torch.empty_like(x["v"])
+    fin = torch.empty((w.n_seq, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    step = lambda: kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"],
+                               out=out, final_state=fin)
+    torch.cuda.synchronize()
+    checks = pre_timing_checks(kda, x, w, out, fin, sample_chains(w, checks_count))
+    settle(step)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    kda.profile_read()            # drop anything recorded so far
+    kda.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kda.profile_enable(False)
+    prof = kda.profile_read_kernels()
+    roof, mfma, kern = kernel_record(w, prof, steps)
+    modes = timing_modes(kda, x, w, out, fin, steps, groups)
+    return {"x": x, "elapsed": t1 - t0, "roofline": roof, "mfma": mfma, "kernel": kern, "checks": checks,
+            "timing_modes": modes}
+
+
+def peak_main(a):
+    """The practical ceilings: the HBM stream with the chunk kernel's read/write mix, sized
+    like the large workload's traffic, and the bf16 MFMA loop, each timed over 7 groups."""
+    import torch
+    import gated_delta_rule_38_amd as kda
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    bytes_large = algorithmic(workloads.WORKLOADS["large"])[0]
+    n16 = int(bytes_large // (6 * 16))
+    ins = [torch.full((n16 * 4,), i + 1, dtype=torch.int32, device=dev) for i in range(5)]
+    out = torch.empty((n16 * 4,), dtype=torch.int32, device=dev)
+    kda.peak_stream(ins, out)
+    torch.cuda.synchronize()
+    assert int(out[0]) == (1 ^ 2 ^ 3 ^ 4 ^ 5) and int(out[-1]) == (1 ^ 2 ^ 3 ^ 4 ^ 5)
+    reps, groups = 5, 7
+    gbs = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            kda.peak_stream(ins, out)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs.append(6 * n16 * 16 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9)
+    del ins, out
+    torch.cuda.empty_cache()
+    wgs, iters = 256 * 2, 4000
+    mo = torch.zeros(wgs * 4, device=dev)
+    kda.peak_mfma(mo, wgs, iters)
+    torch.cuda.synchronize()
+    tf = []
+    flops = wgs * 4 * iters * 8 * 32768
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kda.peak_mfma(mo, wgs, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        tf.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    st, mf = _stats(gbs), _stats(tf)
+    print(json.dumps({
+        "metric": "practical ceilings of one MI355X: HBM stream at the chunk kernel's 5:1 read/write mix; bf16 MFMA loop",
+        "stream": {"bytes_per_launch": 6 * n16 * 16, "read_write_ratio": 5, "GB_s": st,
+                   "frac_of_peak_median": st["median"] / HBM_PEAK_GBS, "peak": HBM_PEAK_GBS},
+        "mfma_bf16": {"flops_per_launch": flops, "workgroups": wgs, "TFLOP_s": mf,
+                      "frac_of_peak_median": mf["median"] / MFMA_BF16_PEAK_TFLOPS, "peak": MFMA_BF16_PEAK_TFLOPS}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="varlen")
+    ap.add_argument("--groups", type=int, default=7, help="timing groups per mode (median / p10 / p90)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large", action="store_true", help="skip the large-workload sub-record of the default run")
+    ap.add_argument("--peak", action="store_true", help="measure the practical HBM and MFMA ceilings instead")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="instead of the bench, copy this many MiB device-to-device 5 times (PMC calibration)")
     a = ap.parse_args()
@@ -313,7 +582,6 @@ def main():
 
     import torch
     import gated_delta_rule_38_amd as kda
-    import workloads
     kda.load_library()
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs the GPU")
@@ -328,68 +596,35 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_each_way": n * 4, "copies": 5}))
         return
-
+    if a.peak:
+        return peak_main(a)
     if a.config in workloads.DECODE_WORKLOADS:
         return decode_main(a, workloads.DECODE_WORKLOADS[a.config])
     w = workloads.WORKLOADS[a.config]
-    x = workloads.make_inputs(w, device=dev)
-    torch.cuda.synchronize()
-    step = lambda: kda.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"],
-                               out=out, final_state=fin)
-    out = torch.empty_like(x["v"])
-    fin = torch.empty((w.n_seq, w.H, w.D, w.D), dtype=torch.float32, device=dev)
-    step()
-    torch.cuda.synchronize()
-    gate = correctness_gate(kda, x, w, out, fin)
-    settle(step)
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    kda.profile_read()            # drop anything recorded so far
-    kda.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kda.profile_enable(False)
-    chunk_ms, chunk_n = kda.profile_read("kda_chunk")
-    elapsed = t1 - t0
-    ms_step = elapsed / a.steps * 1e3
-    tokens_s = w.tokens * a.steps / elapsed
-
-    bytes_, flops, per_th = algorithmic(w)
-    launches_per_step = max(1, chunk_n // a.steps)
-    kern_ms = chunk_ms / max(1, chunk_n)                 # average chunk-kernel launch
-    # algorithmic bytes of one chunk-kernel launch: the single-segment plan does
-    # the whole workload in one launch
-    bytes_launch = bytes_ / launches_per_step
-    achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
-    tr = traffic_from_profile(a.config) if launches_per_step == 1 else None
-    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    tflops = flops / launches_per_step / (kern_ms * 1e-3) / 1e12
+    r = prefill_record(kda, w, a.steps, a.warmup, a.groups, 16 if w.name in ("varlen", "large") else 8)
+    elapsed = r["elapsed"]
     rec = {
-        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": w.tokens * a.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": elapsed / a.steps * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; see workloads.py)",
-        "config": w.describe(),
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": tr},
-        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
-                 "flops_per_launch": flops / launches_per_step,
-                 # the most the matrix cores can be fed when the launch moves its
-                 # algorithmic bytes at the HBM peak (flops / bytes x 8 TB/s)
-                 "frac_ceiling_at_hbm_peak": (flops / bytes_) * HBM_PEAK_GBS * 1e9 / (mfma_peak * 1e12)},
-        "kernel": {"name": "kda_chunk", "avg_ms": kern_ms, "launches_per_step": launches_per_step,
-                   "algorithmic_bytes_per_launch": bytes_launch, "bytes_per_token_head": per_th,
-                   "kernel_source_sha": source_sha("chunk_kernel")},
-        "correctness": {"sampled_rel_l2_max": gate},
-        "work_balance": work_balance(w) if launches_per_step == 1 else None,
-        "timing_modes": dict(timing_modes(kda, x, w, out, fin), pipelined_ms=ms_step),
+        "config": w.describe(), "roofline": r["roofline"], "mfma": r["mfma"], "kernel": r["kernel"],
+        "correctness": r["checks"],
+        "work_balance": work_balance(w) if r["kernel"]["launches_per_step"] == 1 else None,
+        "timing_modes": r["timing_modes"],
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(x, w, a.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(r["x"], w, a.cpu_budget)
+    if a.config == "varlen" and not a.no_large:
+        # the roofline workload (B=16, H=64, T=8192), timed the same way in the same run
+        del r
+        torch.cuda.empty_cache()
+        wl = workloads.WORKLOADS["large"]
+        steps_l = max(3, min(a.steps, 10))
+        rl = prefill_record(kda, wl, steps_l, min(a.warmup, 5), a.groups, 16)
+        rec["large"] = {"config": wl.describe(), "steps": steps_l, "ms_per_step": rl["elapsed"] / steps_l * 1e3,
+                        "tokens_per_s": wl.tokens * steps_l / rl["elapsed"], "roofline": rl["roofline"],
+                        "mfma": rl["mfma"], "kernel": rl["kernel"], "correctness": rl["checks"],
+                        "timing_modes": rl["timing_modes"]}
     print(json.dumps(rec))
 
 

@@ -26,8 +26,10 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
           5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP",
           9: "KDA_ERR_RANGE"}
 EXPORTS = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_ws", "kda_prefill_noalloc", "kda_prep", "kda_decode",
-           "kda_release_cached_workspace", "kda_profile_enable", "kda_profile_read",
-           "kda_status_string", "kda_last_error", "kda_abi_version")
+           "kda_release_cached_workspace", "kda_profile_enable", "kda_profile_read", "kda_profile_read_kernels",
+           "kda_status_string", "kda_last_error", "kda_abi_version",
+           # measurement probes (include/kda_peak.h)
+           "kda_peak_stream", "kda_peak_mfma")
 
 
 class KdaTensor(ctypes.Structure):
@@ -41,6 +43,10 @@ class KdaOptions(ctypes.Structure):
                 ("gate_act", ctypes.c_int32), ("gate_lower_bound", ctypes.c_float), ("beta_act", ctypes.c_int32),
                 ("out_gate", ctypes.POINTER(KdaTensor)), ("norm_weight", ctypes.POINTER(KdaTensor)),
                 ("norm_eps", ctypes.c_float)]
+
+
+class KdaProfileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class KdaError(RuntimeError):
@@ -81,6 +87,13 @@ def load_library(path: str = LIB_PATH):
     lib.kda_profile_enable.restype = None
     lib.kda_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.kda_profile_read.restype = ctypes.c_int
+    lib.kda_profile_read_kernels.argtypes = [ctypes.POINTER(KdaProfileEntry), ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_profile_read_kernels.restype = ctypes.c_int
+    lib.kda_peak_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), V, ctypes.c_int64, V]
+    lib.kda_peak_stream.restype = ctypes.c_int
+    lib.kda_peak_mfma.argtypes = [V, ctypes.c_int32, ctypes.c_int32, V]
+    lib.kda_peak_mfma.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -325,6 +338,36 @@ def profile_read(kernel: Optional[str] = None) -> Tuple[float, int]:
     n = ctypes.c_int64(0)
     _check(load_library().kda_profile_read(kernel.encode() if kernel else None, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def profile_read_kernels() -> dict:
+    """{kernel name: (launches, summed milliseconds)} of every launch recorded since the last
+    read, grouped by kernel; synchronises their events and clears them all."""
+    entries = (KdaProfileEntry * 16)()
+    n = ctypes.c_int32(0)
+    _check(load_library().kda_profile_read_kernels(entries, 16, ctypes.byref(n)))
+    return {entries[i].name.decode(): (entries[i].launches, entries[i].total_ms) for i in range(n.value)}
+
+
+def peak_stream(inputs, out, stream=None) -> None:
+    """Measurement probe: out = xor of the five inputs (16-byte elements, equal sizes)."""
+    import torch
+    if len(inputs) != 5 or any(t.numel() * t.element_size() != out.numel() * out.element_size() for t in inputs):
+        raise ValueError("five inputs of out's size")
+    _require_gpu(*inputs, out)
+    arr = (ctypes.c_void_p * 5)(*[t.data_ptr() for t in inputs])
+    _, st = _stream(out.device, stream)
+    n16 = out.numel() * out.element_size() // 16
+    _check(load_library().kda_peak_stream(arr, ctypes.c_void_p(out.data_ptr()), n16, ctypes.c_void_p(st)))
+
+
+def peak_mfma(out, workgroups: int, iters: int, stream=None) -> None:
+    """Measurement probe: a loop of independent bf16 MFMAs (out: fp32, workgroups * 4 floats)."""
+    _require_gpu(out)
+    if out.numel() < workgroups * 4:
+        raise ValueError("out holds one float per wave")
+    _, st = _stream(out.device, stream)
+    _check(load_library().kda_peak_mfma(ctypes.c_void_p(out.data_ptr()), workgroups, iters, ctypes.c_void_p(st)))
 
 
 def release_cached_workspace() -> None:

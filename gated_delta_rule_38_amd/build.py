@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_pipe.hip", "kda_prep.hip", "kda_combine.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_pipe.hip", "kda_prep.hip", "kda_combine.hip", "kda_decode.hip",
+           "kda_peak.hip"]
 # -packed-fp32-ops: no v_pk_*_f32 generation in device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -973,6 +973,36 @@ kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *lau
     return st;
 }
 
+kda_status_t kda_profile_read_kernels(kda_profile_entry_t *entries, int32_t max_entries, int32_t *count)
+{
+    if (!count || (max_entries > 0 && !entries)) return fail(KDA_ERR_NULL, "entries or count is NULL");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    std::vector<kda_profile_entry_t> agg;
+    kda_status_t st = KDA_OK;
+    for (auto &r : g_prof) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == KDA_OK) st = hip_fail(e, "profile event");
+        kda_profile_entry_t *x = nullptr;
+        for (auto &a : agg)
+            if (strcmp(a.name, r.name) == 0) x = &a;
+        if (!x) {
+            agg.push_back(kda_profile_entry_t{});
+            x = &agg.back();
+            snprintf(x->name, sizeof(x->name), "%s", r.name);
+        }
+        x->launches += 1;
+        x->total_ms += ms;
+        g_prof_pool.emplace_back(r.a, r.b);
+    }
+    g_prof.clear();
+    const int32_t n = (int32_t)std::min<size_t>(agg.size(), (size_t)std::max(0, max_entries));
+    for (int32_t i = 0; i < n; ++i) entries[i] = agg[i];
+    *count = n;
+    return st;
+}
+
 const char *kda_status_string(kda_status_t s)
 {
     switch (s) {

@@ -280,6 +280,18 @@ void kda_release_cached_workspace(void);
 void kda_profile_enable(int on);
 kda_status_t kda_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 
+/* The same records grouped by kernel name (one entry per name, in first-launch order):
+ * synchronises the events, writes at most max_entries entries and their number to *count,
+ * and clears every recorded launch.  Names: "kda_chunk" (single-segment pass),
+ * "kda_chunk_segbuild" (segment maps), "kda_combine", "kda_chunk_segout" (segment outputs),
+ * "kda_prep", "kda_decode". */
+typedef struct {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+} kda_profile_entry_t;
+kda_status_t kda_profile_read_kernels(kda_profile_entry_t *entries, int32_t max_entries, int32_t *count);
+
 const char *kda_status_string(kda_status_t status);
 const char *kda_last_error(void);
 int kda_abi_version(void);

@@ -12,7 +12,8 @@ import gated_delta_rule_38_amd as kda
 from gated_delta_rule_38_amd import KdaTensor, KDA_BF16, KDA_F32, KDA_I32
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kda.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -24,12 +25,15 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
+    """Every function declared in include/*.h (kda.h and the measurement probes of
+    kda_peak.h) is exported by libkda.so and bound by the Python package."""
+    assert len(HEADERS) >= 2
     names = header_functions()
     assert set(names) == set(kda.EXPORTS), names
     for n in names:
@@ -467,3 +471,19 @@ def test_decode_pool_may_not_overlap_norm_operands(lib):
         st = lib.kda_decode(r(s["q"]), r(s["k"]), r(s["v"]), r(s["g"]), r(s["beta"]), r(s["pool"]), r(s["idx"]),
                             r(s["ntok"]), r(s["out"]), 1, ctypes.byref(opts), None)
         assert st == 5 and b"state_pool" in lib.kda_last_error(), (which, st, lib.kda_last_error())
+
+
+def test_peak_probes_validate(lib):
+    """The probes refuse NULL pointers and empty sizes before any launch."""
+    arr = (ctypes.c_void_p * 5)(*([FAKE] * 5))
+    assert lib.kda_peak_stream(arr, None, 16, None) == 1
+    assert lib.kda_peak_stream(arr, ctypes.c_void_p(FAKE), 0, None) == 2
+    assert lib.kda_peak_mfma(None, 4, 4, None) == 1
+    assert lib.kda_peak_mfma(ctypes.c_void_p(FAKE), 0, 4, None) == 2
+
+
+def test_profile_read_kernels_without_records(lib):
+    entries = (kda.KdaProfileEntry * 4)()
+    n = ctypes.c_int32(-1)
+    assert lib.kda_profile_read_kernels(entries, 4, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.kda_profile_read_kernels(None, 4, ctypes.byref(n)) == 1

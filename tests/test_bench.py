@@ -97,3 +97,54 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_sampled_chains_cross_the_2gib_offset_of_g():
+    """On the large workload g is 2^32 bytes: the sample holds the last chain whose g rows
+    all lie below 2^31 bytes, the first at or past it, and the chain of the highest offset,
+    besides the first and the last; 16 distinct chains in all."""
+    w = workloads.WORKLOADS["large"]
+    ch = bench.sample_chains(w, 16)
+    assert len(ch) == 16 and len(set(ch)) == 16
+    T, H, D = 8192, 64, 128
+    lo = lambda n, h: ((n * T) * H + h) * D * 4
+    assert (8, 0) in ch and lo(8, 0) == 1 << 31           # first chain at 2^31
+    assert (7, 63) in ch and lo(7, 63) < 1 << 31          # last chain below it
+    assert (15, 63) in ch and (0, 0) in ch
+    # a small workload has no such chains: first, last and random ones
+    v = bench.sample_chains(workloads.WORKLOADS["varlen"], 16)
+    assert len(v) == 16 and v[0] == (0, 0) and v[1] == (7, 31)
+
+
+def test_whole_call_roofline_from_a_multi_launch_profile():
+    """A segmented call's roofline divides the call's algorithmic bytes by the sum of all its
+    launches (segment build, COMBINE, segment output) per step, not by the chunk launches
+    alone; the split gives each kernel's share."""
+    w = workloads.WORKLOADS["eqlen"]
+    steps = 4
+    prof = {"kda_chunk_segbuild": (steps, 0.080 * steps), "kda_combine": (steps, 0.020 * steps),
+            "kda_chunk_segout": (steps, 0.050 * steps)}
+    roof, mfma, kern = bench.kernel_record(w, prof, steps)
+    bytes_, flops, _ = bench.algorithmic(w)
+    assert kern["launches_per_step"] == 3 and kern["avg_ms"] == pytest.approx(0.150)
+    assert roof["achieved"] == pytest.approx(bytes_ / 0.150e-3 / 1e9)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / 8000.0)
+    assert mfma["achieved"] == pytest.approx(flops / 0.150e-3 / 1e12)
+    shares = {s["name"]: s["share"] for s in kern["split"]}
+    assert shares == pytest.approx({"kda_chunk_segbuild": 0.08 / 0.15, "kda_combine": 0.02 / 0.15,
+                                    "kda_chunk_segout": 0.05 / 0.15})
+    # one launch: the kernel's own duration
+    roof1, _, kern1 = bench.kernel_record(workloads.WORKLOADS["varlen"], {"kda_chunk": (steps, 0.46 * steps)}, steps)
+    assert kern1["launches_per_step"] == 1 and kern1["name"] == "kda_chunk"
+    assert roof1["achieved"] == pytest.approx(bench.algorithmic(workloads.WORKLOADS["varlen"])[0] / 0.46e-3 / 1e9)
+
+
+def test_timing_statistics():
+    st = bench._stats([5.0, 1.0, 3.0, 2.0, 4.0, 6.0, 7.0])
+    assert st["median"] == 4.0 and st["groups"] == 7
+    assert st["p10"] == pytest.approx(1.6) and st["p90"] == pytest.approx(6.4)
+
+
+def test_host_info_fields():
+    info = bench._host_info()
+    assert set(info) == {"cpu_model", "nproc", "affinity"} and info["nproc"] >= 1
