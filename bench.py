@@ -12,10 +12,12 @@ bits; a HIP-graph replay with a changed q is checked against the oracle on the
 new q).  Then the step runs untimed for at least 0.2 s (`settle`: the GPU
 returns to steady clocks after the host-side oracle), W warm-up steps, and K
 timed steps: `value` is their back-to-back ("pipelined") rate.  `roofline` and
-`mfma` come from the library's HIP events on the launch stream over those K
-steps, summed over every launch of a call (one launch on a single-segment
-plan; segment build, COMBINE and segment output on a segmented one) with the
-per-kernel split in `kernel.split`.  `timing_modes` gives the three modes of
+`mfma` come from HIP events on the launch stream over those K steps: around
+the one launch of a single-segment plan (the library's own events), or
+bracketing the K steps when a call makes several launches (segment build,
+COMBINE and segment output on a segmented plan; events around each of them
+would add gaps of their own), with the per-kernel split in `kernel.split` from
+a second, profiled pass.  `timing_modes` gives the three modes of
 the cudnn-frontend KDA PR (pipelined, per call, HIP graph of 8 calls), each
 over 7 timing groups as median / p10 / p90.  `cpu_baseline` is the float64
 oracle on the host's cores (and on one thread) over a bounded sample.  The
@@ -452,20 +454,22 @@ def settle(step, seconds=0.2):
         torch.cuda.synchronize()
 
 
-def kernel_record(w, prof, steps):
+def kernel_record(w, prof, steps, call_ms=None):
     """Roofline, matrix-core rate and per-kernel split of one step from the library's own
-    HIP events: {kernel name: (launches, summed ms)} over `steps` steps.  The whole call is
-    every launch of the step (one launch on a single-segment plan; segment build, COMBINE
-    and segment output on a segmented one), so the HBM and MFMA fractions are those of the
-    call; the split gives each kernel's share."""
+    HIP events: {kernel name: (launches, summed ms)} over `steps` steps.  One launch: its
+    average duration.  Several launches (segment build, COMBINE and segment output on a
+    segmented plan): the whole call, `call_ms` (events bracketing the timed steps, the gaps
+    between launches included) when given, else the launches' summed durations; the split
+    gives each kernel's share of the summed durations."""
     bytes_, flops, per_th = algorithmic(w)
-    total_ms = sum(ms for _, ms in prof.values()) / steps
+    kernels_ms = sum(ms for _, ms in prof.values()) / steps
     launches = sum(n for n, _ in prof.values()) // steps
+    total_ms = kernels_ms if (launches == 1 or call_ms is None) else call_ms
     achieved = bytes_ / (total_ms * 1e-3) / 1e9
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     tflops = flops / (total_ms * 1e-3) / 1e12
     split = [{"name": name, "launches_per_step": n // steps, "avg_ms": ms / max(1, n), "ms_per_step": ms / steps,
-              "share": (ms / steps) / total_ms} for name, (n, ms) in prof.items()]
+              "share": (ms / steps) / kernels_ms} for name, (n, ms) in prof.items()]
     tr = traffic_from_profile(w.name) if launches == 1 else traffic_from_profile(w.name, "whole_call")
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": tr}
@@ -475,7 +479,8 @@ def kernel_record(w, prof, steps):
             # HBM peak (flops / bytes x 8 TB/s)
             "frac_ceiling_at_hbm_peak": (flops / bytes_) * HBM_PEAK_GBS * 1e9 / (mfma_peak * 1e12)}
     kern = {"name": "kda_chunk" if launches == 1 else "whole call", "scope": "one launch" if launches == 1 else
-            f"{launches} launches per call", "avg_ms": total_ms, "launches_per_step": launches,
+            f"{launches} launches per call" + (", timed by events bracketing the steps" if call_ms else ""),
+            "avg_ms": total_ms, "kernels_ms_per_step": kernels_ms, "launches_per_step": launches,
             "algorithmic_bytes_per_launch" if launches == 1 else "algorithmic_bytes_per_call": bytes_,
             "bytes_per_token_head": per_th, "kernel_source_sha": source_sha("chunk_kernel"), "split": split}
     return roof, mfma, kern
@@ -497,17 +502,47 @@ def prefill_record(kda, w, steps, warmup, groups, checks_count):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    kda.profile_read()            # drop anything recorded so far
+    # launches per call (a one-step profile)
+    kda.profile_read()
     kda.profile_enable(True)
+    step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
     kda.profile_enable(False)
-    prof = kda.profile_read_kernels()
-    roof, mfma, kern = kernel_record(w, prof, steps)
+    launches = sum(n for n, _ in kda.profile_read_kernels().values())
+    settle(step, 0.05)
+    if launches == 1:
+        # one launch per call: the library's HIP events around every launch of the timed steps
+        kda.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kda.profile_enable(False)
+        prof = kda.profile_read_kernels()
+        roof, mfma, kern = kernel_record(w, prof, steps)
+    else:
+        # several launches per call: events around every launch would add their own gaps between
+        # the launches, so the timed steps are bracketed by two events on the launch stream (the
+        # whole call, gaps included); the per-kernel split comes from a second, profiled pass
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        call_ms = e0.elapsed_time(e1) / steps
+        kda.profile_enable(True)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        kda.profile_enable(False)
+        prof = kda.profile_read_kernels()
+        roof, mfma, kern = kernel_record(w, prof, steps, call_ms=call_ms)
     modes = timing_modes(kda, x, w, out, fin, steps, groups)
     return {"x": x, "elapsed": t1 - t0, "roofline": roof, "mfma": mfma, "kernel": kern, "checks": checks,
             "timing_modes": modes}

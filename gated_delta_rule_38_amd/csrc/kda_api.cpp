@@ -366,23 +366,28 @@ int device_cus()
     return cus;
 }
 
-// Segment count from a cost model in units of one chunk step of a launch that leaves most
-// CUs idle (measured on MI355X).  One segment: C steps (the longest chain's chunks).  nseg
-// segments: the segment-build pass runs 2 chains nseg workgroups, i.e. ceil(2 chains nseg /
-// CUs) rounds of ceil(C / nseg) steps, the output pass ceil(chains nseg / CUs) rounds, and
-// COMBINE one matrix step per segment boundary (~1.35); passes that fill every CU run their
-// steps ~1.3x slower (the clock drops under full load).  The cheapest count wins, ties to
-// fewer segments, keeping >= 8 chunks per segment.  (With every CU already holding a chain,
-// segmenting cannot pay and one segment is kept.)
-int choose_nseg(int64_t chains, int64_t C, int cus)
+// Segment count from a cost model in units of one chunk step of a launch that leaves most CUs
+// idle (~2.07 us on MI355X).  One segment: C steps (the longest chain's chunks).  nseg segments
+// of ceil(C / nseg) chunks: the map pass builds segments 0 .. nseg - 2, one workgroup per
+// segment on the pipelined kernel (both maps; measured as fast per step as an output step) or
+// two on the single-role kernel, in ceil(workgroups / CUs) rounds; the output pass runs
+// ceil(chains nseg / CUs) rounds.  A pass that fills the CUs runs its steps ~1.2x slower (the
+// clock drops under full load) and pays ~3 steps of its own (the first state, the pipeline's
+// fill, the final stores); COMBINE costs ~2.9 + 1.14 per map segment.  Measured on the
+// equal-length (32 chains x 128 chunks) and long (8 x 2048) workloads, this picks their fastest
+// forced counts (8 and 32).  The cheapest count wins, ties to fewer segments, keeping >= 8
+// chunks per segment.  (With every CU already holding a chain, segmenting cannot pay and one
+// segment is kept.)
+int choose_nseg(int64_t chains, int64_t C, int cus, bool merged_maps)
 {
     if (chains <= 0 || chains >= cus || C < 16) return 1;
     double best = (double)C;
     int pick = 1;
     for (int nseg = 2; nseg <= 64 && C / nseg >= 8; ++nseg) {
-        const double steps = (double)((C + nseg - 1) / nseg);
-        const double rounds = (double)((2 * chains * nseg + cus - 1) / cus + (chains * nseg + cus - 1) / cus);
-        const double cost = 1.3 * rounds * steps + 1.35 * (nseg - 1);
+        const double steps = (double)((C + nseg - 1) / nseg) + 3.0;
+        const int64_t wg1 = chains * (nseg - 1) * (merged_maps ? 1 : 2), wg2 = chains * nseg;
+        const double r1 = (double)((wg1 + cus - 1) / cus), r2 = (double)((wg2 + cus - 1) / cus);
+        const double cost = 1.2 * steps * (r1 + r2) + 2.9 + 1.14 * (nseg - 1);
         if (cost < best) { best = cost; pick = nseg; }
     }
     return pick;
@@ -410,9 +415,9 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
         if (o->nseg > 64) return fail(KDA_ERR_UNSUPPORTED, "nseg %d > 64", o->nseg);
         pl.nseg = o->nseg;
     } else {
-        pl.nseg = choose_nseg(chains, max_chunks, device_cus());
+        pl.nseg = choose_nseg(chains, max_chunks, device_cus(), pl.pipe);
     }
-    // the segment-build launch has chains * nseg * 2 workgroups (a 32-bit grid)
+    // the segment-build launch has up to chains * (nseg - 1) * 2 workgroups (a 32-bit grid)
     if (chains * pl.nseg * 2 > (int64_t)INT32_MAX)
         return fail(KDA_ERR_UNSUPPORTED, "%lld chains x %d segments exceed one launch", (long long)chains, pl.nseg);
     const int prep = o ? o->prep : 0;
@@ -436,8 +441,8 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
         }
         if (nseg > 1) {
             const size_t dd = (size_t)P.D * P.D * 4;
-            pl.off_maps = off;
-            off += align256((size_t)chains * nseg * 2 * dd);
+            pl.off_maps = off;                                   // segments 0 .. nseg - 2
+            off += align256((size_t)chains * (nseg - 1) * 2 * dd);
             pl.off_start = off;
             off += align256((size_t)chains * nseg * dd);
         }
@@ -606,9 +611,11 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     }
     cp.ws_maps = (float *)(wsb + pl.off_maps);
     cp.ws_start = (const float *)(wsb + pl.off_start);
-    cp.role = kda::ROLE_SEG_M;   // the launch covers both M and C roles
+    // The maps of segments 0 .. nseg - 2 (COMBINE never reads the last segment's): the pipelined
+    // kernel builds M and C of a segment in one workgroup, the single-role kernel in two.
+    cp.role = pl.pipe ? kda::ROLE_SEG_MC : kda::ROLE_SEG_M;
     if ((e = timed("kda_chunk_segbuild", st, [&] {
-             return chunk((int)(chains * pl.nseg * 2));
+             return chunk((int)(chains * (pl.nseg - 1) * (pl.pipe ? 1 : 2)));
          })) != hipSuccess)
         return hip_fail(e, "segment-build launch");
     kda::CombineParams mp{};

@@ -137,12 +137,14 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
     // ------------------------------------------------ which chain / segment
     int wg = blockIdx.x;
     int role = p.role;
-    if (role == ROLE_SEG_M) {
+    int per_chain = p.nseg;             // workgroups' segments per chain in this launch
+    if (role == ROLE_SEG_M) {           // two workgroups (M, C) per segment 0 .. nseg - 2
         role = (wg & 1) ? ROLE_SEG_C : ROLE_SEG_M;
         wg >>= 1;
+        per_chain = p.nseg - 1;
     }
-    const int seg = wg % p.nseg;
-    const int chain = wg / p.nseg;
+    const int seg = wg % per_chain;
+    const int chain = wg / per_chain;
     const int n = chain / p.H, h = chain % p.H;
     int64_t t0, bsel;
     int len;
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
         if (p.sT) { dst = p.sT + n * p.sT_sn + h * p.sT_sh; rs = p.sT_sr; }
         if (p.sTh) dsth = p.sTh + n * p.sT_sn + h * p.sT_sh;
     } else if (role == ROLE_SEG_M || role == ROLE_SEG_C) {
-        dst = p.ws_maps + (((int64_t)chain * p.nseg + seg) * 2 + (role == ROLE_SEG_C)) * D * D;
+        dst = p.ws_maps + map_offset(chain, p.nseg, seg, role == ROLE_SEG_C, D);
     }
     if (dst) {
 #pragma unroll

@@ -193,7 +193,11 @@ __device__ __forceinline__ void decay_tile(f32x16 &s, const float4 dd)
 // A token's row spans the 4 consumer waves, so each wave leaves its partial sum of squares
 // in LDS and keeps its O tile in registers across the step's barrier; the next interval 1
 // (or, for the last chunk, the end of the chain) normalises and stores it.
-template <bool STALL, bool OUT, bool NORM>
+// MC (without OUT): the segment-map role ROLE_SEG_MC -- the consumer waves carry both maps of
+// the segment on their 32 value columns, C (start state 0, V as given) and M (start state I,
+// V = 0), from the same operands: each fragment of Kt, T diag(beta) and Kh read from LDS feeds
+// the product of both.  One workgroup then builds both maps of a segment.
+template <bool STALL, bool OUT, bool NORM, bool MC>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[NORM ? SMEM_NORM : SMEM];
@@ -210,11 +214,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     const int l32 = lane & 31, g2 = lane >> 5, l16 = lane & 15, g4 = lane >> 4;
     const bool producer = wave >= 4;
 
+    const int stall_iters = (STALL && wave == p.stall_wave) ? p.stall_iters : 0;   // wave-uniform
     auto sync = [&]() {
         __syncthreads();
         if constexpr (STALL) {
-            if (wave == p.stall_wave)
-                for (int s = 0; s < p.stall_iters; ++s) __builtin_amdgcn_s_sleep(127);
+            for (int s = 0; s < stall_iters; ++s) __builtin_amdgcn_s_sleep(127);
         }
     };
 
@@ -280,13 +284,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 
     // ------------------------------------------------ chain / segment
     int wg = blockIdx.x;
-    int role = p.role;
-    if (role == ROLE_SEG_M) {
-        role = (wg & 1) ? ROLE_SEG_C : ROLE_SEG_M;
-        wg >>= 1;
-    }
-    const int seg = wg % p.nseg;
-    const int chain = wg / p.nseg;
+    const int role = p.role;
+    // the map launch covers segments 0 .. nseg - 2 (COMBINE never reads the last segment's maps)
+    const int per_chain = (role == ROLE_SEG_MC) ? p.nseg - 1 : p.nseg;
+    const int seg = wg % per_chain;
+    const int chain = wg / per_chain;
     const int h = chain % p.H;
     const int n = p.lpt ? longest_first(p.cu, p.N, chain / p.H, smem) : chain / p.H;
     int64_t t0, bsel;
@@ -298,7 +300,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     const int c_end = min(c_begin + cps, nchunks);
     const int nck = c_end - c_begin;
     constexpr bool has_out = OUT;
-    const bool has_v = (role != ROLE_SEG_M);
 
     // ------------------------------------------------ gate-factored operands (all waves)
     // Thread tid handles tokens 2*(tid>>5) and 2*(tid>>5)+1, channels 4*(tid&31)..+3 of a
@@ -594,7 +595,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     } else {
         // ============================================ consumer waves
         const int cw = wave;
-        const float vscale = has_v ? 1.f : 0.f;     // the transition-map role runs with V = 0
         // transposed reads: lane k of each 16-lane group addresses row k/4 and channel
         // 4*(k%4) of a 16-channel slice; it receives 4 rows of channel (its slice) + (lane%16)
         const int tr_row = (lane & 15) >> 2, tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -648,7 +648,6 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 src = p.ws_start + ((int64_t)chain * p.nseg + seg) * D * D;
             }
             const bf16 *srch = (role == ROLE_OUT && p.s0h) ? p.s0h + n * p.s0_sn + h * p.s0_sh : nullptr;
-            const float one = (role == ROLE_SEG_M) ? 1.f : 0.f;
             if (src) {              // one straight-line block of 64 loads
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
@@ -669,20 +668,35 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) S[m][4 * q + r] = (32 * m + 8 * q + 4 * g2 + r == vcol) ? one : 0.f;
+                        for (int r = 0; r < 4; ++r) S[m][4 * q + r] = 0.f;     // C map, or no initial state
             }
+        }
+        // MC: the M map of this wave's columns, from the identity
+        f32x16 SM[4];
+        if constexpr (MC) {
+            const int diag = vcol - 4 * g2;     // row 32m + 8q + 4 g2 + r is this lane's column
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) SM[m][4 * q + r] = (32 * m + 8 * q + r == diag) ? 1.f : 0.f;
         }
         // V enters R = V - Kt S on the matrix cores: IdV[j] is the A operand of an identity
         // over tokens 16j..16j+15 (element e of lane (i, g) is 1 where token 16j + 8(e/4) + 4g +
-        // e%4 is row i), scaled by vscale
+        // e%4 is row i)
+        auto make_idv = [&](Frag8<bf16> (&id)[2]) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float t8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t8[e] = (l32 == 16 * j + 8 * (e >> 2) + 4 * g2 + (e & 3)) ? 1.f : 0.f;
+                id[j].set(t8);
+            }
+        };
+        // held across the loop, except in the map role (two states): rebuilt there each step
         Frag8<bf16> IdV[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float t8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t8[e] = (l32 == 16 * j + 8 * (e >> 2) + 4 * g2 + (e & 3)) ? vscale : 0.f;
-            IdV[j].set(t8);
-        }
+        if constexpr (!MC) make_idv(IdV);
         if (nck > 0) prefetch_qkv(c_begin);
         sync();
         sync();
@@ -702,9 +716,12 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             // computed on stale data and never read.
             operands(std::false_type{}, smem + (t & 1) * B_SIZE);
             prefetch_qkv(min(c_begin + t + 1, c_last));
-            Frag8<bf16> RB[2];
+            // two maps hold twice the state: keep the operand arithmetic and the R products apart
+            if constexpr (MC) __builtin_amdgcn_sched_barrier(0);
+            Frag8<bf16> RB[2], RBM[2];
             {
-                f32x16 R = {};
+                f32x16 R = {}, RM = {};
+                if constexpr (MC) make_idv(IdV);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     Frag8<bf16> fv;
@@ -712,19 +729,35 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     fv.load44_tr(p0, p0 + 8 * KR_LD);
                     mma32(R, IdV[j], fv);
                 }
+                if constexpr (OUT) {        // the bf16 state feeds O too: all 8 fragments, up front
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    float t8[8];
+                    for (int s = 0; s < 8; ++s) {
+                        float t8[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t8[e] = S[s >> 1][8 * (s & 1) + e];
-                    SB[s].set(t8);
+                        for (int e = 0; e < 8; ++e) t8[e] = S[s >> 1][8 * (s & 1) + e];
+                        SB[s].set(t8);
+                    }
                 }
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     Frag8<bf16> fa;
                     const bf16 *row = cKt + l32 * W_LD + 16 * s + 4 * g2;
                     fa.load44(row, row + 8);
+                    if constexpr (!OUT) {       // maps: each fragment converted where it is used
+                        float t8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = S[s >> 1][8 * (s & 1) + e];
+                        SB[s].set(t8);
+                    }
                     mma32(R, fa, SB[s]);
+                    if constexpr (MC) {           // R_M = -Kt M (V = 0), from the same Kt fragment
+                        float t8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = SM[s >> 1][8 * (s & 1) + e];
+                        Frag8<bf16> sbm;
+                        sbm.set(t8);
+                        mma32(RM, fa, sbm);
+                    }
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -732,6 +765,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) t8[e] = R[8 * s + e];
                     RB[s].set(t8);
+                    if constexpr (MC) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = RM[8 * s + e];
+                        RBM[s].set(t8);
+                    }
                 }
             }
             if (cact && cw == 0) build_T_off(sBeta + ((t + 2) % 3) * C, (bf16 *)(CB + B_T));
@@ -748,14 +786,22 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     decay_tile<1>(S[1], dd);
                     decay_tile<2>(S[2], dd);
                     decay_tile<3>(S[3], dd);
+                    if constexpr (MC) {
+                        decay_tile<0>(SM[0], dd);
+                        decay_tile<1>(SM[1], dd);
+                        decay_tile<2>(SM[2], dd);
+                        decay_tile<3>(SM[3], dd);
+                    }
                 }
-                f32x16 U = {};
+                f32x16 U = {}, UM = {};
+                Frag8<bf16> UBM[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     Frag8<bf16> fa;
                     const bf16 *row = cT + l32 * P_LD + 16 * s + 4 * g2;
                     fa.load44(row, row + 8);
                     mma32(U, fa, RB[s]);
+                    if constexpr (MC) mma32(UM, fa, RBM[s]);
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -763,6 +809,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) t8[e] = U[8 * s + e];
                     UB[s].set(t8);
+                    if constexpr (MC) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = UM[8 * s + e];
+                        UBM[s].set(t8);
+                    }
                 }
                 // O = Qt S + P U (always formed: without outputs it is discarded), then the
                 // state update, in one block so the three MFMA chains and the conversions can
@@ -793,6 +844,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                         const bf16 *p0 = cKh + (16 * s + 4 * g2 + tr_row) * KR_LD + 32 * m + tr_col;
                         fa.load44_tr(p0, p0 + 8 * KR_LD);
                         mma32(S[m], fa, UB[s]);
+                        if constexpr (MC) mma32(SM[m], fa, UBM[s]);
                     }
                 }
                 if constexpr (NORM) {
@@ -837,8 +889,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         if (role == ROLE_OUT || (role == ROLE_SEG_OUT && seg == p.nseg - 1)) {
             if (p.sT) { dst = p.sT + n * p.sT_sn + h * p.sT_sh; rs = p.sT_sr; }
             if (p.sTh) dsth = p.sTh + n * p.sT_sn + h * p.sT_sh;
-        } else if (role == ROLE_SEG_M || role == ROLE_SEG_C) {
-            dst = p.ws_maps + (((int64_t)chain * p.nseg + seg) * 2 + (role == ROLE_SEG_C)) * D * D;
+        } else if (role == ROLE_SEG_MC) {
+            dst = p.ws_maps + map_offset(chain, p.nseg, seg, 1, D);   // C
         }
         if (dst) {
 #pragma unroll
@@ -847,6 +899,15 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) dst[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol] = S[m][4 * q + r];
+        }
+        if constexpr (MC) {     // M (an empty segment -- a chain shorter than nseg segments -- leaves I)
+            float *dm = p.ws_maps + map_offset(chain, p.nseg, seg, 0, D);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dm[(32 * m + 8 * q + 4 * g2 + r) * D + vcol] = SM[m][4 * q + r];
         }
         if (dsth) {
 #pragma unroll
@@ -865,14 +926,15 @@ hipError_t launch_chunk_pipe(const ChunkParams &p, int grid, bool stall, hipStre
 {
     if (grid <= 0) return hipSuccess;
     const bool out = p.role == ROLE_OUT || p.role == ROLE_SEG_OUT;
+    if (!out && p.role != ROLE_SEG_MC) return hipErrorInvalidValue;   // maps: the merged role only
     const bool norm = out && p.z;
-#define KDA_PIPE(S, O, N) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<S, O, N>), dim3(grid), dim3(pipe::NT), 0, st, p)
-    if (stall && norm) KDA_PIPE(true, true, true);
-    else if (stall && out) KDA_PIPE(true, true, false);
-    else if (stall) KDA_PIPE(true, false, false);
-    else if (norm) KDA_PIPE(false, true, true);
-    else if (out) KDA_PIPE(false, true, false);
-    else KDA_PIPE(false, false, false);
+#define KDA_PIPE(S, O, N, M) hipLaunchKernelGGL((pipe::chunk_pipe_kernel<S, O, N, M>), dim3(grid), dim3(pipe::NT), 0, st, p)
+    if (stall && norm) KDA_PIPE(true, true, true, false);
+    else if (stall && out) KDA_PIPE(true, true, false, false);
+    else if (stall) KDA_PIPE(true, false, false, true);
+    else if (norm) KDA_PIPE(false, true, true, false);
+    else if (out) KDA_PIPE(false, true, false, false);
+    else KDA_PIPE(false, false, false, true);
 #undef KDA_PIPE
     return hipGetLastError();
 }

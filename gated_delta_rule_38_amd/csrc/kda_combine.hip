@@ -12,7 +12,7 @@
 // C_s stay fp32: they compose many chunk maps).  Narrow slabs put D/16
 // workgroups on every chain, so a handful of chains still spreads over many
 // CUs; M_s and C_s do not depend on the scan, so each wave loads the operands
-// of the segments up to three steps ahead while it multiplies the current one.
+// of the segments two steps ahead while it multiplies the current one.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
     const int n = chain / p.H, h = chain % p.H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     float *start = p.start + (int64_t)chain * p.nseg * D * D;
-    const float *maps = p.maps + (int64_t)chain * p.nseg * 2 * D * D;
+    const float *maps = p.maps + map_offset(chain, p.nseg, 0, 0, D);
 
     for (int e = tid; e < D * SL; e += NT) {
         const int ch = e / SL, v = e % SL;
@@ -42,9 +42,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
     // channels k is taken in the order k = 16j + 4(lane/16) + e for MFMA 4j + e, so each lane
     // feeds four consecutive MFMAs from one 16-byte read of its M row and one of the slab.
     const int mrow = 16 * wave + l16;
-    // M_s and C_s of the next PF segments wait in registers (a ring indexed at compile time by
-    // unrolling the segment loop PF times)
-    constexpr int PF = 3;
+    // M_s and C_s of the next PF segments wait in registers, a ring indexed at compile time (the
+    // segment loop is unrolled PF times).  Every step issues the same loads -- those of segment
+    // s + PF, clamped to the last one -- and the loop has no exit inside its unrolled body, so
+    // the compiler's wait before a step's products covers only the loads of that step, issued
+    // PF steps earlier, not the younger ones in flight.
+    constexpr int PF = 2;
     float4 m[PF][KB];
     float c[PF][4];
     auto load_maps = [&](int s, float4 (&mm)[KB], float (&cc)[4]) {
@@ -55,34 +58,37 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
         for (int r = 0; r < 4; ++r) cc[r] = C[(16 * wave + 4 * g4 + r) * D + v0 + l16];
     };
     const int steps = p.nseg - 1;        // start[s + 1] = M_s start[s] + C_s for s < steps
+    const int last = steps - 1;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_maps(min(u, last), m[u], c[u]);
+    __syncthreads();
+    auto step = [&](int s, float4 (&mm)[KB], float (&cc)[4]) {
+        const float *cur = sS[s & 1];
+        f32x4 acc = {cc[0], cc[1], cc[2], cc[3]};
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const float4 b = *(const float4 *)(cur + l16 * ST_LD + 16 * j + 4 * g4);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mm[j].x, b.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mm[j].y, b.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mm[j].z, b.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mm[j].w, b.w, acc, 0, 0, 0);
+        }
+        load_maps(min(s + PF, last), mm, cc);
+        // lane (column l16, group g4) holds rows 16w + 4 g4 + r of start[s+1]
+        *(float4 *)(sS[(s + 1) & 1] + l16 * ST_LD + 16 * wave + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        float *st = start + (int64_t)(s + 1) * D * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[(16 * wave + 4 * g4 + r) * D + v0 + l16] = acc[r];
+        __syncthreads();
+    };
+    int s = 0;
+    for (; s + PF <= steps; s += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) step(s + u, m[u], c[u]);
+    }
 #pragma unroll
     for (int u = 0; u < PF; ++u)
-        if (u < steps) load_maps(u, m[u], c[u]);
-    __syncthreads();
-    for (int s0 = 0; s0 < steps; s0 += PF) {
-#pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int s = s0 + u;
-            if (s >= steps) break;
-            const float *cur = sS[s & 1];
-            f32x4 acc = {c[u][0], c[u][1], c[u][2], c[u][3]};
-#pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                const float4 b = *(const float4 *)(cur + l16 * ST_LD + 16 * j + 4 * g4);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].x, b.x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].y, b.y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].z, b.z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u][j].w, b.w, acc, 0, 0, 0);
-            }
-            if (s + PF < steps) load_maps(s + PF, m[u], c[u]);
-            // lane (column l16, group g4) holds rows 16w + 4 g4 + r of start[s+1]
-            *(float4 *)(sS[(s + 1) & 1] + l16 * ST_LD + 16 * wave + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            float *st = start + (int64_t)(s + 1) * D * D;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st[(16 * wave + 4 * g4 + r) * D + v0 + l16] = acc[r];
-            __syncthreads();
-        }
-    }
+        if (s + u < steps) step(s + u, m[u], c[u]);
 }
 
 hipError_t launch_combine(const CombineParams &p, int D, int chains, hipStream_t st)

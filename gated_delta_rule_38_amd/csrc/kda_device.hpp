@@ -187,8 +187,17 @@ enum Role : int32_t {
     ROLE_OUT = 0,      // one chain per workgroup: start state -> outputs + final state
     ROLE_SEG_M = 1,    // segment operator M: V = 0, start state = I, no outputs
     ROLE_SEG_C = 2,    // segment offset C: start state = 0, no outputs
-    ROLE_SEG_OUT = 3   // one segment: start state from workspace -> outputs (+ final state)
+    ROLE_SEG_OUT = 3,  // one segment: start state from workspace -> outputs (+ final state)
+    ROLE_SEG_MC = 4    // both maps of one segment in one workgroup (pipelined kernel): the
+                       // consumer waves carry C, the producer waves carry M
 };
+// Segment maps are built for segments 0 .. nseg - 2 only: COMBINE never reads the last one's.
+// Map (M or C) `which` (0 = M, 1 = C) of segment seg of chain `chain`, in a workspace of
+// [chain][nseg - 1][2][D][D] fp32.
+__device__ __forceinline__ int64_t map_offset(int chain, int nseg, int seg, int which, int D)
+{
+    return (((int64_t)chain * (nseg - 1) + seg) * 2 + which) * D * D;
+}
 
 struct ChunkParams {
     const void *q, *k, *v;     // ET
@@ -200,7 +209,7 @@ struct ChunkParams {
     float *sT;                 // final state or NULL (fp32)
     bf16 *sTh;                 // final state or NULL (bf16; sT is then NULL)
     const int32_t *cu;         // NULL: dense layout
-    float *ws_maps;            // [chain][seg][2][D][D] segment operators (M, C)
+    float *ws_maps;            // [chain][nseg - 1][2][D][D] segment operators (M, C) of segments 0 .. nseg - 2
     const float *ws_start;     // [chain][seg][D][D] segment start states
     // strides in elements: batch, token, head
     int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, g_sb, g_st, g_sh;
@@ -264,7 +273,7 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-    const float *maps;         // [chain][seg][2][D][D]
+    const float *maps;         // [chain][nseg - 1][2][D][D]
     float *start;              // [chain][seg][D][D]
     const float *s0;           // initial state (fp32), or NULL
     const bf16 *s0h;           // initial state (bf16), or NULL

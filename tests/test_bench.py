@@ -148,3 +148,15 @@ def test_timing_statistics():
 def test_host_info_fields():
     info = bench._host_info()
     assert set(info) == {"cpu_model", "nproc", "affinity"} and info["nproc"] >= 1
+
+
+def test_whole_call_timed_by_bracketing_events():
+    """With several launches per call the roofline uses the call's duration from events
+    bracketing the timed steps (gaps between launches included), and the split still gives
+    each kernel's share of the launches' summed durations."""
+    w = workloads.WORKLOADS["long"]
+    prof = {"kda_chunk_segbuild": (2, 0.30), "kda_combine": (2, 0.15), "kda_chunk_segout": (2, 0.31)}
+    roof, _, kern = bench.kernel_record(w, prof, 2, call_ms=0.40)
+    assert kern["avg_ms"] == 0.40 and kern["kernels_ms_per_step"] == pytest.approx(0.38)
+    assert roof["achieved"] == pytest.approx(bench.algorithmic(w)[0] / 0.40e-3 / 1e9)
+    assert sum(s["share"] for s in kern["split"]) == pytest.approx(1.0)
