@@ -42,7 +42,7 @@ class KdaOptions(ctypes.Structure):
                 ("stall_wave", ctypes.c_int32), ("stall_cycles", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("gate_act", ctypes.c_int32), ("gate_lower_bound", ctypes.c_float), ("beta_act", ctypes.c_int32),
                 ("out_gate", ctypes.POINTER(KdaTensor)), ("norm_weight", ctypes.POINTER(KdaTensor)),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("split_chains", ctypes.c_int32)]
 
 
 class KdaProfileEntry(ctypes.Structure):
@@ -163,9 +163,9 @@ def _stream(device, stream):
 
 def options(nseg: int = 0, prep: int = 0, stall_wave: int = -1, stall_cycles: int = 0, variant: int = 0,
             gate_logits: bool = False, gate_lower_bound: float = -5.0, beta_logits: bool = False,
-            out_gate=None, norm_weight=None, norm_eps: float = 1e-6) -> KdaOptions:
+            out_gate=None, norm_weight=None, norm_eps: float = 1e-6, split_chains: int = 0) -> KdaOptions:
     o = KdaOptions()
-    o.nseg, o.prep, o.variant = nseg, prep, variant
+    o.nseg, o.prep, o.variant, o.split_chains = nseg, prep, variant, split_chains
     o.gate_act, o.gate_lower_bound, o.beta_act = int(bool(gate_logits)), gate_lower_bound, int(bool(beta_logits))
     o.norm_eps = norm_eps
     if out_gate is not None or norm_weight is not None:
@@ -194,13 +194,13 @@ def _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, want_final
 
 def workspace_size(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, final_state=None,
                    nseg: int = 0, prep: int = 0, variant: int = 0, gate_logits: bool = False,
-                   gate_lower_bound: float = -5.0, beta_logits: bool = False) -> int:
+                   gate_lower_bound: float = -5.0, beta_logits: bool = False, split_chains: int = 0) -> int:
     lib = load_library()
     out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, False)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     n = ctypes.c_size_t(0)
     opts = options(nseg, prep, variant=variant, gate_logits=gate_logits, gate_lower_bound=gate_lower_bound,
-                   beta_logits=beta_logits)
+                   beta_logits=beta_logits, split_chains=split_chains)
     _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(n)))
     return n.value
 
@@ -209,7 +209,7 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
             output_final_state: bool = True, nseg: int = 0, prep: int = 0, stall_wave: int = -1,
             stall_cycles: int = 0, variant: int = 0, gate_logits: bool = False, gate_lower_bound: float = -5.0,
             beta_logits: bool = False, out_gate=None, norm_weight=None, norm_eps: float = 1e-6,
-            workspace=None, stream=None) -> Tuple:
+            split_chains: int = 0, workspace=None, stream=None) -> Tuple:
     """KDA chunked prefill.  Returns (out, final_state).
 
     Dense layout: q, k, g [B, T, H, K], v [B, T, H, V], beta [B, T, H].
@@ -236,12 +236,13 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, out=None, fin
         out, final_state = _alloc_outputs(q, v, cu_seqlens, initial_state, out, final_state, output_final_state)
     ds = _descs(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     plain = (nseg == 0 and prep == 0 and stall_wave < 0 and variant == 0 and workspace is None
-             and not gate_logits and not beta_logits and out_gate is None and norm_weight is None)
+             and not gate_logits and not beta_logits and out_gate is None and norm_weight is None
+             and split_chains == 0)
     if plain:
         _check(lib.kda_prefill(*[_ptr(d) for d in ds], ctypes.c_void_p(st)))
         return out, final_state
     opts = options(nseg, prep, stall_wave, stall_cycles, variant, gate_logits, gate_lower_bound, beta_logits,
-                   out_gate, norm_weight, norm_eps)
+                   out_gate, norm_weight, norm_eps, split_chains)
     need = ctypes.c_size_t(0)
     _check(lib.kda_prefill_workspace_size(*[_ptr(d) for d in ds], ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value:

@@ -349,6 +349,7 @@ kda::CheckG g_view(const kda_tensor_t *g, int64_t rows, int64_t rows_per_b, int6
 // ------------------------------------------------------------------ plan
 struct Plan {
     int nseg = 1;
+    int64_t seg_chains = 0;     // chains cut into nseg segments: the last seg_chains of the N*H
     bool pipe = false;          // pipelined 32-token kernel (d = 128, bf16)
     int chunk = 64;
     bool standalone_prep = false;
@@ -393,6 +394,31 @@ int choose_nseg(int64_t chains, int64_t C, int cus, bool merged_maps)
     return pick;
 }
 
+// Split plans: chains = k CUs + r with k >= 1 leave a last round of r chains on r CUs.  Cutting
+// only those r chains into s segments -- their maps, COMBINE, then one launch holding their
+// segment outputs and the k CUs whole chains -- ends at about k rounds plus two short
+// segment passes.  Same cost units as choose_nseg; returns r (and s) when that beats k + 1 whole
+// rounds (the last one at the low-load clock), else 0.
+int64_t choose_split(int64_t chains, int64_t C, int cus, int &s_out)
+{
+    if (chains <= cus || C < 16) return 0;
+    const int64_t k = chains / cus, r = chains % cus;
+    if (r == 0) return 0;
+    const double whole = 1.2 * k * (C + 3) + 1.0 * (C + 3);
+    double best = whole;
+    int pick = 0;
+    for (int s = 2; s <= 16 && C / s >= 8; ++s) {
+        const double steps = (double)((C + s - 1) / s) + 3.0;
+        const double maps = (double)((r * (s - 1) + cus - 1) / cus) * steps;
+        const double outs = k * (double)(C + 3) + (double)((r * s + cus - 1) / cus) * steps;
+        const double cost = 1.2 * (maps + outs) + 2.9 + 1.14 * (s - 1);
+        if (cost < best) { best = cost; pick = s; }
+    }
+    if (!pick) return 0;
+    s_out = pick;
+    return r;
+}
+
 // max_bytes > 0 caps the workspace (the no-alloc entry point's fixed scratch): an automatic
 // segment count is lowered until the plan fits (one segment needs none); a forced segment
 // count or standalone PREP that does not fit is refused.
@@ -411,11 +437,25 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
     pl.pipe = pipe_ok && variant != 1;
     pl.chunk = pl.pipe ? 32 : 64;
     const int64_t max_chunks = P.dense ? (P.T + pl.chunk - 1) / pl.chunk : (P.Ttot + pl.chunk - 1) / pl.chunk;
+    const int cus = device_cus();
     if (o && o->nseg > 0) {
         if (o->nseg > 64) return fail(KDA_ERR_UNSUPPORTED, "nseg %d > 64", o->nseg);
         pl.nseg = o->nseg;
     } else {
-        pl.nseg = choose_nseg(chains, max_chunks, device_cus(), pl.pipe);
+        pl.nseg = choose_nseg(chains, max_chunks, cus, pl.pipe);
+    }
+    pl.seg_chains = pl.nseg > 1 ? chains : 0;
+    const int split = o ? o->split_chains : 0;
+    if (split < 0) return fail(KDA_ERR_UNSUPPORTED, "split_chains %d", split);
+    if (split > 0) {
+        if (!(o->nseg > 1) || !pl.pipe || split > chains)
+            return fail(KDA_ERR_UNSUPPORTED, "split_chains needs a forced nseg > 1, the pipelined kernel and at most "
+                                             "N*H chains");
+        pl.seg_chains = split;
+    } else if (!(o && o->nseg > 0) && pl.pipe && P.dense) {
+        int s = 1;
+        const int64_t r = choose_split(chains, max_chunks, cus, s);
+        if (r > 0) { pl.nseg = s; pl.seg_chains = r; }
     }
     // the segment-build launch has up to chains * (nseg - 1) * 2 workgroups (a 32-bit grid)
     if (chains * pl.nseg * 2 > (int64_t)INT32_MAX)
@@ -441,10 +481,11 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
         }
         if (nseg > 1) {
             const size_t dd = (size_t)P.D * P.D * 4;
+            const size_t sc = (size_t)pl.seg_chains;           // the segmented chains' slots
             pl.off_maps = off;                                   // segments 0 .. nseg - 2
-            off += align256((size_t)chains * (nseg - 1) * 2 * dd);
+            off += align256(sc * (nseg - 1) * 2 * dd);
             pl.off_start = off;
-            off += align256((size_t)chains * nseg * dd);
+            off += align256(sc * nseg * dd);
         }
         return off;
     };
@@ -455,6 +496,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
             return fail(KDA_ERR_WORKSPACE, "the plan needs %zu bytes of scratch, more than the %zu the no-alloc entry point has",
                         pl.bytes, max_bytes);
         while (pl.nseg > 1 && layout(pl.nseg) > max_bytes) --pl.nseg;
+        if (pl.nseg == 1) pl.seg_chains = 0;
         pl.bytes = layout(pl.nseg);
     }
     // Chain order.  With more chains than CUs, workgroups start in launch order as CUs free up,
@@ -468,10 +510,10 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
     else if (ord && strcmp(ord, "longest") == 0) pl.lpt = lpt_ok;
     else pl.lpt = lpt_ok && chains > device_cus();
     if (env_on("KDA_LOG"))
-        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d kernel=%s chunk=%d prep=%s order=%s workspace=%zu B\n",
+        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d segmented=%lld kernel=%s chunk=%d prep=%s order=%s workspace=%zu B\n",
                 (long long)P.N, (long long)P.H, (long long)P.D, P.dense ? "dense" : "packed", (long long)chains,
-                pl.nseg, pl.pipe ? "pipelined" : "single-role", pl.chunk, pl.standalone_prep ? "standalone" : "in-chunk",
-                pl.lpt ? "longest-first" : "natural", pl.bytes);
+                pl.nseg, (long long)pl.seg_chains, pl.pipe ? "pipelined" : "single-role", pl.chunk,
+                pl.standalone_prep ? "standalone" : "in-chunk", pl.lpt ? "longest-first" : "natural", pl.bytes);
     return KDA_OK;
 }
 
@@ -603,30 +645,37 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
         cp.g_sb = pp.y_sb; cp.g_st = pp.y_st; cp.g_sh = pp.y_sh;
         cp.g_is_gamma = 1;
     }
+    cp.seg_chain0 = 0;
+    cp.n_segwg = 0;
     if (pl.nseg == 1) {
         cp.role = kda::ROLE_OUT;
         if ((e = timed("kda_chunk", st, [&] { return chunk((int)chains); })) != hipSuccess)
             return hip_fail(e, "chunk launch");
         return KDA_OK;
     }
+    // chains seg_chain0 .. chains - 1 are segmented (all of them unless the plan splits)
+    const int64_t segc = pl.seg_chains, whole = chains - segc;
+    cp.seg_chain0 = (int32_t)whole;
+    cp.n_segwg = (int32_t)(segc * pl.nseg);
     cp.ws_maps = (float *)(wsb + pl.off_maps);
     cp.ws_start = (const float *)(wsb + pl.off_start);
     // The maps of segments 0 .. nseg - 2 (COMBINE never reads the last segment's): the pipelined
     // kernel builds M and C of a segment in one workgroup, the single-role kernel in two.
     cp.role = pl.pipe ? kda::ROLE_SEG_MC : kda::ROLE_SEG_M;
     if ((e = timed("kda_chunk_segbuild", st, [&] {
-             return chunk((int)(chains * (pl.nseg - 1) * (pl.pipe ? 1 : 2)));
+             return chunk((int)(segc * (pl.nseg - 1) * (pl.pipe ? 1 : 2)));
          })) != hipSuccess)
         return hip_fail(e, "segment-build launch");
     kda::CombineParams mp{};
     mp.maps = cp.ws_maps; mp.start = (float *)(wsb + pl.off_start);
     mp.s0 = cp.s0; mp.s0h = cp.s0h; mp.s0_sn = P.s0_sn; mp.s0_sh = P.s0_sh; mp.s0_sr = P.s0_sr;
-    mp.N = (int32_t)P.N; mp.H = (int32_t)P.H; mp.nseg = pl.nseg;
-    if ((e = timed("kda_combine", st, [&] { return kda::launch_combine(mp, D, (int)chains, st); })) != hipSuccess)
+    mp.N = (int32_t)P.N; mp.H = (int32_t)P.H; mp.nseg = pl.nseg; mp.seg_chain0 = cp.seg_chain0;
+    if ((e = timed("kda_combine", st, [&] { return kda::launch_combine(mp, D, (int)segc, st); })) != hipSuccess)
         return hip_fail(e, "combine launch");
+    // the segment outputs, then (a split plan) the whole chains 0 .. seg_chain0 - 1
     cp.role = kda::ROLE_SEG_OUT;
     if ((e = timed("kda_chunk_segout", st, [&] {
-             return chunk((int)(chains * pl.nseg));
+             return chunk((int)(segc * pl.nseg + whole));
          })) != hipSuccess)
         return hip_fail(e, "segment-output launch");
     return KDA_OK;

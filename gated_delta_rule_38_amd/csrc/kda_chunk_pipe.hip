@@ -283,19 +283,30 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     };
 
     // ------------------------------------------------ chain / segment
-    int wg = blockIdx.x;
-    const int role = p.role;
-    // the map launch covers segments 0 .. nseg - 2 (COMBINE never reads the last segment's maps)
-    const int per_chain = (role == ROLE_SEG_MC) ? p.nseg - 1 : p.nseg;
-    const int seg = wg % per_chain;
-    const int chain = wg / per_chain;
+    // chain: the (sequence, head) chain; lchain: its workspace slot among the segmented chains;
+    // nseg: the segments of this chain (1 for a chain run whole)
+    const int wg = blockIdx.x;
+    int role = p.role, nseg = p.nseg, seg = 0, chain, lchain = 0;
+    if (role == ROLE_SEG_MC) {          // maps of segments 0 .. nseg - 2 (COMBINE never reads the last's)
+        lchain = wg / (nseg - 1);
+        seg = wg % (nseg - 1);
+        chain = p.seg_chain0 + lchain;
+    } else if (role == ROLE_SEG_OUT && wg < p.n_segwg) {
+        lchain = wg / nseg;
+        seg = wg % nseg;
+        chain = p.seg_chain0 + lchain;
+    } else {                            // a whole chain (the launch's trailing workgroups in a split plan)
+        chain = (role == ROLE_SEG_OUT) ? wg - p.n_segwg : wg;
+        role = ROLE_OUT;
+        nseg = 1;
+    }
     const int h = chain % p.H;
     const int n = p.lpt ? longest_first(p.cu, p.N, chain / p.H, smem) : chain / p.H;
     int64_t t0, bsel;
     int len;
     seq_range(p.cu, n, p.T, t0, len, bsel);
     const int nchunks = (len + C - 1) / C;
-    const int cps = (nchunks + p.nseg - 1) / p.nseg;
+    const int cps = (nchunks + nseg - 1) / nseg;
     const int c_begin = min(seg * cps, nchunks);
     const int c_end = min(c_begin + cps, nchunks);
     const int nck = c_end - c_begin;
@@ -645,7 +656,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                 src = p.s0 + n * p.s0_sn + h * p.s0_sh;
                 rs = p.s0_sr;
             } else if (role == ROLE_SEG_OUT) {
-                src = p.ws_start + ((int64_t)chain * p.nseg + seg) * D * D;
+                src = p.ws_start + ((int64_t)lchain * nseg + seg) * D * D;
             }
             const bf16 *srch = (role == ROLE_OUT && p.s0h) ? p.s0h + n * p.s0_sn + h * p.s0_sh : nullptr;
             if (src) {              // one straight-line block of 64 loads
@@ -886,11 +897,11 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         float *dst = nullptr;
         bf16 *dsth = nullptr;         // bf16 final state (rounded to nearest even)
         int64_t rs = D;
-        if (role == ROLE_OUT || (role == ROLE_SEG_OUT && seg == p.nseg - 1)) {
+        if (role == ROLE_OUT || (role == ROLE_SEG_OUT && seg == nseg - 1)) {
             if (p.sT) { dst = p.sT + n * p.sT_sn + h * p.sT_sh; rs = p.sT_sr; }
             if (p.sTh) dsth = p.sTh + n * p.sT_sn + h * p.sT_sh;
         } else if (role == ROLE_SEG_MC) {
-            dst = p.ws_maps + map_offset(chain, p.nseg, seg, 1, D);   // C
+            dst = p.ws_maps + map_offset(lchain, nseg, seg, 1, D);   // C
         }
         if (dst) {
 #pragma unroll
@@ -901,7 +912,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     for (int r = 0; r < 4; ++r) dst[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol] = S[m][4 * q + r];
         }
         if constexpr (MC) {     // M (an empty segment -- a chain shorter than nseg segments -- leaves I)
-            float *dm = p.ws_maps + map_offset(chain, p.nseg, seg, 0, D);
+            float *dm = p.ws_maps + map_offset(lchain, nseg, seg, 0, D);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll

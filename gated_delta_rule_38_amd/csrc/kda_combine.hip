@@ -25,11 +25,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
     // the slab's current state, transposed ([value column][key channel]), double-buffered so
     // that one barrier per segment orders every write after the reads it replaces
     __shared__ __attribute__((aligned(16))) float sS[2][SL * ST_LD];
-    const int chain = blockIdx.x, slab = blockIdx.y, v0 = SL * slab;
+    const int lchain = blockIdx.x, chain = p.seg_chain0 + lchain, slab = blockIdx.y, v0 = SL * slab;
     const int n = chain / p.H, h = chain % p.H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
-    float *start = p.start + (int64_t)chain * p.nseg * D * D;
-    const float *maps = p.maps + map_offset(chain, p.nseg, 0, 0, D);
+    float *start = p.start + (int64_t)lchain * p.nseg * D * D;
+    const float *maps = p.maps + map_offset(lchain, p.nseg, 0, 0, D);
 
     for (int e = tid; e < D * SL; e += NT) {
         const int ch = e / SL, v = e % SL;

@@ -230,6 +230,12 @@ struct ChunkParams {
     float eps;
     int32_t lpt;               // packed layout, one segment: workgroup rank r runs the r-th
                                // longest sequence (ties: lower index first); N <= LPT_MAX_SEQ
+    // Segmented plans cut chains seg_chain0 .. N*H - 1 into nseg segments (workspace slots are
+    // indexed from seg_chain0); chains below seg_chain0 run whole.  In a ROLE_SEG_OUT launch,
+    // workgroups 0 .. n_segwg - 1 run the segments and the ones after them run chains
+    // 0 .. seg_chain0 - 1 whole (ROLE_OUT).
+    int32_t seg_chain0;
+    int32_t n_segwg;
 };
 
 // Longest-first chain order: at most this many sequences (one launch ranks them all in LDS).
@@ -273,12 +279,13 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-    const float *maps;         // [chain][nseg - 1][2][D][D]
-    float *start;              // [chain][seg][D][D]
+    const float *maps;         // [chain - seg_chain0][nseg - 1][2][D][D]
+    float *start;              // [chain - seg_chain0][seg][D][D]
     const float *s0;           // initial state (fp32), or NULL
     const bf16 *s0h;           // initial state (bf16), or NULL
     int64_t s0_sn, s0_sh, s0_sr;
     int32_t N, H, nseg;
+    int32_t seg_chain0;        // workgroup x runs chain seg_chain0 + x
 };
 
 // A token-major fp32 view for the debug-mode range check of g: element (row r, head h,

@@ -140,6 +140,12 @@ typedef struct {
     const kda_tensor_t *out_gate;
     const kda_tensor_t *norm_weight;
     float norm_eps;
+    /* split_chains = n > 0 (with a forced nseg > 1): only the last n (sequence, head) chains
+     * are cut into segments and the others run whole, their segment outputs and the whole
+     * chains in one launch (pipelined kernel only; a test knob -- the planner picks such split
+     * plans itself for dense batches with a little more than a multiple of the CU count of
+     * chains).  0 = planner's choice. */
+    int32_t split_chains;
 } kda_options_t;
 
 /*

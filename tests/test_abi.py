@@ -488,3 +488,43 @@ def test_profile_read_kernels_without_records(lib):
     n = ctypes.c_int32(-1)
     assert lib.kda_profile_read_kernels(entries, 4, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.kda_profile_read_kernels(None, 4, ctypes.byref(n)) == 1
+
+
+def test_planner_splits_chains_just_above_the_cu_count(tmp_path):
+    """288 equal chains (B=9, H=32, T=4096) on 256 CUs: instead of a second round of 32 chains on
+    32 CUs, only the last 32 chains are cut into segments (8) and the other 256 run whole; the
+    workspace holds the 32 chains' maps and start states.  256 chains (one full round) and the
+    packed layout (lengths unknown on the host) are not split; a forced split is refused without a
+    forced segment count or on the single-role kernel."""
+    import subprocess, sys, textwrap
+    code = textwrap.dedent(f"""
+        import ctypes, sys
+        sys.path.insert(0, {ROOT!r}); sys.path.insert(0, {os.path.join(ROOT, 'tests')!r})
+        import test_abi as t
+        import gated_delta_rule_38_amd as kda
+        lib = kda.load_library()
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        D = 128
+        def dense(B, H, T):
+            gap = 1 << 36
+            return [t.desc([B, T, H, D]), t.desc([B, T, H, D], base=t.FAKE + gap), t.desc([B, T, H, D], base=t.FAKE + 2 * gap),
+                    t.desc([B, T, H, D], t.KDA_F32, t.FAKE + 3 * gap), t.desc([B, T, H], t.KDA_F32, t.FAKE + 4 * gap), None, None,
+                    t.desc([B, T, H, D], base=t.FAKE + 5 * gap), None]
+        for B, H, T, kw in ((9, 32, 4096, {{}}), (8, 32, 4096, {{}}), (2, 3, 300, dict(nseg=3, split_chains=2)),
+                            (2, 3, 300, dict(split_chains=2)), (2, 3, 300, dict(nseg=3, split_chains=2, variant=1))):
+            n = ctypes.c_size_t(0)
+            st = lib.kda_prefill_workspace_size(*(r(d) for d in dense(B, H, T)), ctypes.byref(kda.options(**kw)), ctypes.byref(n))
+            sys.stderr.flush()
+            print("case", B, H, T, sorted(kw.items()), "status", st, "bytes", n.value, flush=True)
+    """)
+    env = dict(os.environ, KDA_LOG="1")
+    p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stderr[-2000:]
+    cases = [l for l in p.stdout.splitlines() if l.startswith("case")]
+    plans = [l for l in p.stderr.splitlines() if l.startswith("kda: plan")]
+    dd = 128 * 128 * 4
+    assert "status 0" in cases[0] and f"bytes {32 * (3 * 8 - 2) * dd}" in cases[0], cases[0]
+    assert "nseg=8 segmented=32" in plans[0], plans[0]
+    assert "status 0 bytes 0" in cases[1] and "nseg=1 segmented=0" in plans[1]
+    assert "status 0" in cases[2] and f"bytes {2 * (3 * 3 - 2) * dd}" in cases[2] and "nseg=3 segmented=2" in plans[2]
+    assert "status 6" in cases[3] and "status 6" in cases[4]

@@ -766,3 +766,48 @@ def test_check_rejects_gates_out_of_range(kda, monkeypatch):
                         gate_logits=True, beta_logits=True)
         assert e.value.status == 9
         monkeypatch.delenv("KDA_CHECK")
+
+
+@pytest.mark.parametrize("dense", [True, False])
+@pytest.mark.parametrize("nseg,split", [(3, 2), (8, 1), (4, 5)])
+def test_split_plan_matches_oracle_and_whole_chains_keep_their_bits(kda, dense, nseg, split):
+    """A split plan cuts only the last `split` chains into segments; their segment outputs and
+    the other chains, run whole, share one launch.  Everything matches the oracle, and the
+    chains run whole give exactly the bits of the one-segment plan."""
+    import torch
+    if dense:
+        w = workloads.custom([300] * 3, H=2, D=128, dense=True, seed=80)
+    else:
+        w = workloads.custom([700, 64, 1, 300], H=2, D=128, seed=80)
+    x = gen(w)
+    say("split plan", "dense" if dense else "packed", "nseg", nseg, "split", split)
+    out, sT = run(kda, x, nseg=nseg, split_chains=split)
+    check_full(x, out, sT, TOL["bf16"])
+    o1, s1 = run(kda, x, nseg=1)
+    chains = w.n_seq * w.H
+    whole = [(c // w.H, c % w.H) for c in range(chains - split)]
+    for n, h in whole:
+        assert torch_equal(out_slice(x, out, n, h), out_slice(x, o1, n, h)), (n, h)
+        assert torch_equal(sT[n, h], s1[n, h]), (n, h)
+
+
+@pytest.mark.parametrize("wave", [0, 3, 4, 7])
+def test_split_plan_stalled_wave_gives_same_bits(kda, wave):
+    w = workloads.custom([300] * 3, H=2, D=128, dense=True, seed=81)
+    x = gen(w)
+    o0, s0 = run(kda, x, nseg=3, split_chains=2)
+    o1, s1 = run(kda, x, nseg=3, split_chains=2, stall_wave=wave, stall_cycles=127 * 6)
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+
+
+def test_planner_split_on_288_chains(kda):
+    """288 equal chains: the planner segments only 32 of them; sampled chains of both kinds
+    (whole and segmented) against the oracle, including the first and last of each kind."""
+    import torch
+    w = workloads.WORKLOADS["eqlen288"]
+    x = gen(w)
+    out, sT = run(kda, x)
+    torch.cuda.synchronize()
+    chains = [(0, 0), (7, 31), (3, 17), (8, 0), (8, 31), (8, 13)]     # chains 256..287 are n = 8
+    worst = check_chains(x, out, sT, chains, TOL["bf16"])
+    say(f"eqlen288 worst sampled rel-L2 {worst:.2e}")

@@ -70,6 +70,10 @@ WORKLOADS = {
     "varlen_h64": Workload("varlen_h64", tuple(varlen_lengths()), H=64, D=128, dtype="bf16", dense=False),
     "long": Workload("long", (65536,), H=8, D=128, dtype="bf16", dense=True, floor_channels=13),
     "large": Workload("large", (8192,) * 16, H=64, D=128, dtype="bf16", dense=True),
+    # 256 and 288 equal chains: one full round of the CUs, and a full round plus 32 chains
+    # (the planner then segments only those 32)
+    "eqlen256": Workload("eqlen256", (4096,) * 8, H=32, D=128, dtype="bf16", dense=True),
+    "eqlen288": Workload("eqlen288", (4096,) * 9, H=32, D=128, dtype="bf16", dense=True),
 }
 
 
