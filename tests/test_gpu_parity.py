@@ -149,15 +149,26 @@ def test_gate_extremes(kda, gate):
 
 
 def _sample(w, count, seed=0):
+    """The first and last chains, on a dense layout the chains on either side of the 2^31-byte
+    offset of g (the first whose g rows start at or past it, the last wholly below it: where a
+    32-bit byte offset would wrap) and the one of the highest offset, then seeded random ones."""
     rng = np.random.default_rng(seed)
     chains = {(w.n_seq - 1, w.H - 1), (0, 0)}
-    while len(chains) < count:
+    if w.dense:
+        T, H, D = w.lengths[0], w.H, w.D
+        lo = lambda n, h: ((n * T) * H + h) * D * 4
+        live = [(n, h) for n in range(w.n_seq) for h in range(H)]
+        above = [c for c in live if lo(*c) >= 1 << 31]
+        if above:
+            chains.add(min(above, key=lambda c: lo(*c)))
+            chains.add(max((c for c in live if lo(*c) < 1 << 31), key=lambda c: lo(*c)))
+    while len(chains) < min(count, w.n_seq * w.H):
         chains.add((int(rng.integers(w.n_seq)), int(rng.integers(w.H))))
     return sorted(chains)
 
 
-@pytest.mark.parametrize("name,count", [("eqlen", 6), ("varlen", 6), ("varlen_padded", 4), ("long", 1),
-                                        ("large", 3)])
+@pytest.mark.parametrize("name,count", [("eqlen", 8), ("varlen", 12), ("varlen_padded", 6), ("long", 8),
+                                        ("large", 16), ("eqlen288", 8)])
 def test_workload_sampled_chains(kda, name, count):
     import torch
     w = workloads.WORKLOADS[name]
@@ -811,3 +822,26 @@ def test_planner_split_on_288_chains(kda):
     chains = [(0, 0), (7, 31), (3, 17), (8, 0), (8, 31), (8, 13)]     # chains 256..287 are n = 8
     worst = check_chains(x, out, sT, chains, TOL["bf16"])
     say(f"eqlen288 worst sampled rel-L2 {worst:.2e}")
+
+
+
+@pytest.mark.parametrize("name", ["varlen", "eqlen", "long"])
+def test_full_size_bits_stable_under_repeat_and_stall(kda, name):
+    """The full-size workloads in the bench's launch configuration (one launch on varlen; map
+    pass, COMBINE and segment outputs on eqlen and long): a second call, and calls with a
+    consumer wave or a producer wave stalled after every barrier, give the first call's bits."""
+    import torch
+    w = workloads.WORKLOADS[name]
+    x = gen(w)
+    o0, s0 = run(kda, x)
+    o1, s1 = run(kda, x)
+    torch.cuda.synchronize()
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+    for wave in (0, 5):          # the options leave the segment count to the planner: the same plan
+        say(name, "full size, stalled wave", wave)
+        o2, s2 = run(kda, x, stall_wave=wave, stall_cycles=127 * 2)
+        torch.cuda.synchronize()
+        assert torch_equal(o0, o2) and torch_equal(s0, s2), f"wave {wave}"
+    del x, o0, o1, s0, s1
+    torch.cuda.empty_cache()
+
