@@ -8,35 +8,22 @@
 
 namespace kda {
 
-// Each workgroup streams one contiguous tile of 2048 16-byte elements of every array (32 KB),
-// four elements per thread in flight, the loads non-temporal: of the stream shapes measured on
-// MI355X (grid-stride with 2 or 4 elements per thread and 8-32 workgroups per CU, tiles of
-// 2048-65536 elements, staggered array offsets, temporal or non-temporal loads) this one was
-// the fastest.
+// One 16-byte element of every array per thread, loads and stores non-temporal: of the stream
+// shapes measured on MI355X (grid-stride loops with 2 or 4 elements per thread and 8-32
+// workgroups per CU; contiguous tiles of 256-65536 elements per workgroup with 1, 2 or 4
+// elements per thread; staggered array offsets; temporal or non-temporal loads and stores)
+// this one was the fastest, 5.9-6.0 TB/s at the 5:1 mix.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr int64_t STREAM_TILE = 2048;
 
 __global__ __launch_bounds__(256) void peak_stream_kernel(const u32x4 *a, const u32x4 *b, const u32x4 *c,
                                                           const u32x4 *d, const u32x4 *e, u32x4 *out, int64_t n)
 {
-    const int64_t base = (int64_t)blockIdx.x * STREAM_TILE;
-    const int64_t end = n < base + STREAM_TILE ? n : base + STREAM_TILE;
-    for (int64_t i = base + threadIdx.x; i < end; i += 4 * 256) {
-        u32x4 r[4];
-        bool ok[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = i + u * 256;
-            ok[u] = j < end;
-            const int64_t jj = ok[u] ? j : i;          // in-bounds stand-in, never stored
-            r[u] = __builtin_nontemporal_load(a + jj) ^ __builtin_nontemporal_load(b + jj) ^
-                   __builtin_nontemporal_load(c + jj) ^ __builtin_nontemporal_load(d + jj) ^
-                   __builtin_nontemporal_load(e + jj);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (ok[u]) out[i + u * 256] = r[u];
-    }
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const u32x4 r = __builtin_nontemporal_load(a + i) ^ __builtin_nontemporal_load(b + i) ^
+                    __builtin_nontemporal_load(c + i) ^ __builtin_nontemporal_load(d + i) ^
+                    __builtin_nontemporal_load(e + i);
+    __builtin_nontemporal_store(r, out + i);
 }
 
 // Eight independent accumulator chains per wave keep the matrix core's pipeline full; the
@@ -80,7 +67,7 @@ kda_status_t kda_peak_stream(const void *const in[5], void *out, int64_t n16, vo
     for (int i = 0; i < 5; ++i)
         if (!in[i]) return KDA_ERR_NULL;
     if (n16 <= 0) return KDA_ERR_SHAPE;
-    const int64_t blocks = (n16 + kda::STREAM_TILE - 1) / kda::STREAM_TILE;
+    const int64_t blocks = (n16 + 255) / 256;
     if (blocks > INT32_MAX) return KDA_ERR_SHAPE;
     typedef kda::u32x4 V;
     hipLaunchKernelGGL(kda::peak_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
