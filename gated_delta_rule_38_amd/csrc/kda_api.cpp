@@ -374,7 +374,7 @@ int device_cus()
 // two on the single-role kernel, in ceil(workgroups / CUs) rounds; the output pass runs
 // ceil(chains nseg / CUs) rounds.  A pass that fills the CUs runs its steps ~1.2x slower (the
 // clock drops under full load) and pays ~3 steps of its own (the first state, the pipeline's
-// fill, the final stores); COMBINE costs ~2.9 + 1.14 per map segment.  Measured on the
+// fill, the final stores); COMBINE costs ~3.5 + 0.78 per map segment.  Measured on the
 // equal-length (32 chains x 128 chunks) and long (8 x 2048) workloads, this picks their fastest
 // forced counts (8 and 32).  The cheapest count wins, ties to fewer segments, keeping >= 8
 // chunks per segment.  (With every CU already holding a chain, segmenting cannot pay and one
@@ -388,7 +388,7 @@ int choose_nseg(int64_t chains, int64_t C, int cus, bool merged_maps)
         const double steps = (double)((C + nseg - 1) / nseg) + 3.0;
         const int64_t wg1 = chains * (nseg - 1) * (merged_maps ? 1 : 2), wg2 = chains * nseg;
         const double r1 = (double)((wg1 + cus - 1) / cus), r2 = (double)((wg2 + cus - 1) / cus);
-        const double cost = 1.2 * steps * (r1 + r2) + 2.9 + 1.14 * (nseg - 1);
+        const double cost = 1.2 * steps * (r1 + r2) + 3.5 + 0.78 * (nseg - 1);
         if (cost < best) { best = cost; pick = nseg; }
     }
     return pick;
@@ -411,7 +411,7 @@ int64_t choose_split(int64_t chains, int64_t C, int cus, int &s_out)
         const double steps = (double)((C + s - 1) / s) + 3.0;
         const double maps = (double)((r * (s - 1) + cus - 1) / cus) * steps;
         const double outs = k * (double)(C + 3) + (double)((r * s + cus - 1) / cus) * steps;
-        const double cost = 1.2 * (maps + outs) + 2.9 + 1.14 * (s - 1);
+        const double cost = 1.2 * (maps + outs) + 3.5 + 0.78 * (s - 1);
         if (cost < best) { best = cost; pick = s; }
     }
     if (!pick) return 0;

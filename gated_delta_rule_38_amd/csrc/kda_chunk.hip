@@ -641,7 +641,9 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
     } else if (role == ROLE_SEG_M || role == ROLE_SEG_C) {
         dst = p.ws_maps + map_offset(chain, p.nseg, seg, role == ROLE_SEG_C, D);
     }
-    if (dst) {
+    if (dst && role == ROLE_SEG_M) {
+        store_map_m(dst, S, lane, vcol, D);
+    } else if (dst) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
 #pragma unroll

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
     // Wave w produces rows 16w..16w+15 of the slab with 16x16x4 fp32 MFMAs.  The sum over key
     // channels k is taken in the order k = 16j + 4(lane/16) + e for MFMA 4j + e, so each lane
     // feeds four consecutive MFMAs from one 16-byte read of its M row and one of the slab.
-    const int mrow = 16 * wave + l16;
+    // M is stored in this read order (map_m_index): load j of a wave is one contiguous 1 KB run.
     // M_s and C_s of the next PF segments wait in registers, a ring indexed at compile time (the
     // segment loop is unrolled PF times).  Every step issues the same loads -- those of segment
     // s + PF, clamped to the last one -- and the loop has no exit inside its unrolled body, so
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void combine_kernel(const CombinePar
     auto load_maps = [&](int s, float4 (&mm)[KB], float (&cc)[4]) {
         const float *M = maps + (int64_t)s * 2 * D * D, *C = M + D * D;
 #pragma unroll
-        for (int j = 0; j < KB; ++j) mm[j] = *(const float4 *)(M + mrow * D + 16 * j + 4 * g4);
+        for (int j = 0; j < KB; ++j) mm[j] = *(const float4 *)(M + ((wave * KB + j) * 64 + lane) * 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) cc[r] = C[(16 * wave + 4 * g4 + r) * D + v0 + l16];
     };
