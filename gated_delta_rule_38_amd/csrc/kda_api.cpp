@@ -374,7 +374,7 @@ int device_cus()
 // two on the single-role kernel, in ceil(workgroups / CUs) rounds; the output pass runs
 // ceil(chains nseg / CUs) rounds.  A pass that fills the CUs runs its steps ~1.2x slower (the
 // clock drops under full load) and pays ~3 steps of its own (the first state, the pipeline's
-// fill, the final stores); COMBINE costs ~3.5 + 0.78 per map segment.  Measured on the
+// fill, the final stores); COMBINE costs ~4.4 + 0.45 per map segment.  Measured on the
 // equal-length (32 chains x 128 chunks) and long (8 x 2048) workloads, this picks their fastest
 // forced counts (8 and 32).  The cheapest count wins, ties to fewer segments, keeping >= 8
 // chunks per segment.  (With every CU already holding a chain, segmenting cannot pay and one
@@ -388,7 +388,7 @@ int choose_nseg(int64_t chains, int64_t C, int cus, bool merged_maps)
         const double steps = (double)((C + nseg - 1) / nseg) + 3.0;
         const int64_t wg1 = chains * (nseg - 1) * (merged_maps ? 1 : 2), wg2 = chains * nseg;
         const double r1 = (double)((wg1 + cus - 1) / cus), r2 = (double)((wg2 + cus - 1) / cus);
-        const double cost = 1.2 * steps * (r1 + r2) + 3.5 + 0.78 * (nseg - 1);
+        const double cost = 1.2 * steps * (r1 + r2) + 4.4 + 0.45 * (nseg - 1);
         if (cost < best) { best = cost; pick = nseg; }
     }
     return pick;
@@ -411,7 +411,7 @@ int64_t choose_split(int64_t chains, int64_t C, int cus, int &s_out)
         const double steps = (double)((C + s - 1) / s) + 3.0;
         const double maps = (double)((r * (s - 1) + cus - 1) / cus) * steps;
         const double outs = k * (double)(C + 3) + (double)((r * s + cus - 1) / cus) * steps;
-        const double cost = 1.2 * (maps + outs) + 3.5 + 0.78 * (s - 1);
+        const double cost = 1.2 * (maps + outs) + 4.4 + 0.45 * (s - 1);
         if (cost < best) { best = cost; pick = s; }
     }
     if (!pick) return 0;
@@ -670,7 +670,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     mp.maps = cp.ws_maps; mp.start = (float *)(wsb + pl.off_start);
     mp.s0 = cp.s0; mp.s0h = cp.s0h; mp.s0_sn = P.s0_sn; mp.s0_sh = P.s0_sh; mp.s0_sr = P.s0_sr;
     mp.N = (int32_t)P.N; mp.H = (int32_t)P.H; mp.nseg = pl.nseg; mp.seg_chain0 = cp.seg_chain0;
-    if ((e = timed("kda_combine", st, [&] { return kda::launch_combine(mp, D, (int)segc, st); })) != hipSuccess)
+    if ((e = timed("kda_combine", st, [&] { return kda::launch_combine(mp, D, !P.fp32, (int)segc, st); })) != hipSuccess)
         return hip_fail(e, "combine launch");
     // the segment outputs, then (a split plan) the whole chains 0 .. seg_chain0 - 1
     cp.role = kda::ROLE_SEG_OUT;

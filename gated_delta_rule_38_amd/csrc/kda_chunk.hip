@@ -32,6 +32,8 @@
 // is rewritten within a chunk or by the next chunk has a workgroup barrier
 // between its last reader and its next writer (the inter-chunk shared-memory
 // race fixed in TensorRT-LLM PR #19826 is exactly a missing one).
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(64 * (D / 32), 1) void chunk_kernel(const ChunkPara
         dst = p.ws_maps + map_offset(chain, p.nseg, seg, role == ROLE_SEG_C, D);
     }
     if (dst && role == ROLE_SEG_M) {
-        store_map_m(dst, S, lane, vcol, D);
+        store_map_m<std::is_same<ET, bf16>::value>(dst, S, lane, vcol, D);
     } else if (dst) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m)

@@ -912,7 +912,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
                     for (int r = 0; r < 4; ++r) dst[(32 * m + 8 * q + 4 * g2 + r) * rs + vcol] = S[m][4 * q + r];
         }
         if constexpr (MC) {     // M (an empty segment -- a chain shorter than nseg segments -- leaves I)
-            store_map_m(p.ws_maps + map_offset(lchain, nseg, seg, 0, D), SM, lane, vcol, D);
+            store_map_m<true>(p.ws_maps + map_offset(lchain, nseg, seg, 0, D), SM, lane, vcol, D);
         }
         if (dsth) {
 #pragma unroll

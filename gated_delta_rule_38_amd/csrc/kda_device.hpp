@@ -200,21 +200,38 @@ __device__ __forceinline__ int64_t map_offset(int chain, int nseg, int seg, int 
 }
 
 // C is row-major ([key channel][value column], like a state).  M is stored in the order COMBINE
-// feeds it to the matrix cores: the wave that forms rows 16w .. 16w + 15 reads, for each block
-// of 16 columns j, one contiguous 1 KB run of 64 lanes x 4 floats, lane = 16 (k % 16) / 4 +
-// row % 16 holding columns k = 16 j + 4 (lane / 16) + 0..3 of its row.  Every load is then one
-// run of whole cache lines instead of 16 rows x 64 bytes (on MI355X a COMBINE step took 30%
-// less time).  Element (row, k) of a D x D map M:
+// feeds it to the matrix cores, so that each of a wave's loads is one contiguous 1 KB run of 64
+// lanes x 16 bytes instead of 16 rows x 64 bytes (on MI355X a COMBINE step took 30% less time).
+// The wave that forms rows 16w .. 16w + 15 of a start state holds, in lane l, row 16w + l % 16:
+//   * fp32 maps (fp32 I/O): run j of the wave holds columns k = 16j + 4(l / 16) + 0..3;
+//   * split maps (bf16 I/O): M = Mh + Ml, both bf16 (Mh = M rounded to nearest even, Ml = the
+//     remainder rounded), so the product M S runs as Mh Sh + Mh Sl + Ml Sh on the bf16 matrix
+//     cores with a relative error near 2^-16; for each 32-column block b, run 2b holds Mh and
+//     run 2b + 1 Ml of columns k = 32b + 8(l / 16) + 0..7.
+// Element (row, k) of a D x D fp32 map, in floats:
 __device__ __forceinline__ int map_m_index(int row, int k, int D)
 {
     return (((row >> 4) * (D >> 4) + (k >> 4)) * 64 + ((k & 15) >> 2) * 16 + (row & 15)) * 4 + (k & 3);
 }
+// Element (row, k) of Mh of a split map, in bf16 elements (Ml's is 512 further).
+__device__ __forceinline__ int map_m_split_index(int row, int k, int D)
+{
+    return (((row >> 4) * (D >> 4) + 2 * (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (row & 15)) * 8 + (k & 7);
+}
+
+// x = hi + lo to about 16 significant bits, two values at a time: hi = x rounded to bf16 (nearest
+// even), lo = the remainder x - hi (exact in fp32) rounded to bf16; each as a packed word.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    hi = pack2(a, b);
+    lo = pack2(a - __builtin_bit_cast(float, hi << 16), b - __builtin_bit_cast(float, hi & 0xffff0000u));
+}
 
 // Store a map M held in 32x32 MFMA accumulators -- tile m, element 4q + r at row
-// 32m + 8q + 4(lane / 32) + r, column `vcol` -- in map_m_index order.  Lanes 2a and 2a + 1
-// (columns c, c + 1) first swap two of their four rows (a quad permute [1,0,3,2]), so each lane
-// holds two consecutive columns of two rows and stores two 8-byte pairs.
-template <int NM>
+// 32m + 8q + 4(lane / 32) + r, column `vcol` -- in COMBINE's order (SPLIT: as Mh and Ml).
+// Lanes 2a and 2a + 1 (columns c, c + 1) first swap two of their four rows (a quad permute
+// [1,0,3,2]), so each lane holds two consecutive columns of two rows and stores them as pairs.
+template <bool SPLIT, int NM>
 __device__ __forceinline__ void store_map_m(float *dm, const f32x16 (&S)[NM], int lane, int vcol, int D)
 {
     const bool odd = lane & 1;
@@ -223,8 +240,8 @@ __device__ __forceinline__ void store_map_m(float *dm, const f32x16 (&S)[NM], in
     for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            // rows rb + {0, 2} of this lane's pair of columns: an even lane keeps rows 0 and 2 of
-            // its column and takes those of its odd neighbour; an odd lane rows 1 and 3
+            // an even lane keeps rows 0 and 2 of its column and takes those of its odd
+            // neighbour; an odd lane rows 1 and 3
             const float a0 = S[m][4 * q], a1 = S[m][4 * q + 1], a2 = S[m][4 * q + 2], a3 = S[m][4 * q + 3];
             const float s0 = odd ? a0 : a1, s1 = odd ? a2 : a3;
             const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xf, 0xf, false));
@@ -233,8 +250,29 @@ __device__ __forceinline__ void store_map_m(float *dm, const f32x16 (&S)[NM], in
             const float2 lo = odd ? make_float2(r0, a1) : make_float2(a0, r0);
             const float2 hi = odd ? make_float2(r1, a3) : make_float2(a2, r1);
             const int row = 32 * m + 8 * q + rb;
-            *(float2 *)(dm + map_m_index(row, k0, D)) = lo;
-            *(float2 *)(dm + map_m_index(row + 2, k0, D)) = hi;
+            if constexpr (SPLIT) {
+                // lanes l and l ^ 2 hold the same rows for columns k0 .. k0 + 1 and k0 ^ 2 ..:
+                // a lane with bit 1 clear keeps row `row` and takes its partner's, the other
+                // keeps row + 2, so each stores 4 consecutive columns of one row (8 bytes of
+                // Mh, 8 of Ml)
+                uint32_t ha, la, hb, lb;
+                split2(lo.x, lo.y, ha, la);         // row
+                split2(hi.x, hi.y, hb, lb);         // row + 2
+                const bool up = lane & 2;
+                const uint32_t sh = up ? ha : hb, sl = up ? la : lb;
+                const uint32_t rh = __builtin_amdgcn_mov_dpp(sh, 0x4E, 0xf, 0xf, false);
+                const uint32_t rl = __builtin_amdgcn_mov_dpp(sl, 0x4E, 0xf, 0xf, false);
+                // bit 1 clear: row, columns (k0, k0 + 1) then the partner's (k0 + 2, k0 + 3);
+                // bit 1 set: row + 2, the partner's (k0 - 2, k0 - 1) then its own
+                const uint2 h2 = up ? make_uint2(rh, hb) : make_uint2(ha, rh);
+                const uint2 l2 = up ? make_uint2(rl, lb) : make_uint2(la, rl);
+                const int i = map_m_split_index(up ? row + 2 : row, k0 & ~3, D);
+                *(uint2 *)((bf16 *)dm + i) = h2;
+                *(uint2 *)((bf16 *)dm + i + 512) = l2;
+            } else {
+                *(float2 *)(dm + map_m_index(row, k0, D)) = lo;
+                *(float2 *)(dm + map_m_index(row + 2, k0, D)) = hi;
+            }
         }
 }
 
@@ -249,7 +287,7 @@ struct ChunkParams {
     bf16 *sTh;                 // final state or NULL (bf16; sT is then NULL)
     const int32_t *cu;         // NULL: dense layout
     float *ws_maps;            // [chain][nseg - 1][2][D x D] segment operators (M, C) of segments 0 .. nseg - 2
-                               // (M in map_m_index order, C row-major)
+                               // (M in COMBINE's order, split on bf16 I/O; C row-major)
     const float *ws_start;     // [chain][seg][D][D] segment start states
     // strides in elements: batch, token, head
     int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, g_sb, g_st, g_sh;
@@ -319,7 +357,7 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-    const float *maps;         // [chain - seg_chain0][nseg - 1][2][D][D]
+    const float *maps;         // [chain - seg_chain0][nseg - 1][2][D x D] (M in COMBINE's order)
     float *start;              // [chain - seg_chain0][seg][D][D]
     const float *s0;           // initial state (fp32), or NULL
     const bf16 *s0h;           // initial state (bf16), or NULL

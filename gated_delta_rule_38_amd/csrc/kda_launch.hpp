@@ -17,7 +17,7 @@ hipError_t launch_check_slots(const int32_t *idx, int32_t R, int32_t P, int32_t 
 // PREP kernel over `nvc` virtual chunks x H heads.
 hipError_t launch_prep(const PrepParams &p, int nvc, hipStream_t st);
 // COMBINE kernel over chains x D/16 value slabs.
-hipError_t launch_combine(const CombineParams &p, int D, int chains, hipStream_t st);
+hipError_t launch_combine(const CombineParams &p, int D, bool split, int chains, hipStream_t st);
 // DECODE kernel over requests x heads x D/32 value slabs.
 hipError_t launch_decode(const DecodeParams &p, int D, bool io_f32, bool state_bf16, hipStream_t st);
 }  // namespace kda
