@@ -172,7 +172,9 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
 
 /* Bytes of device workspace kda_prefill_ws needs for these descriptors and
  * options: 0 when the plan is a single chunk-kernel launch; with nseg > 1 the
- * segment maps and segment start states (fp32 K x V each); with the standalone
+ * segment maps and segment start states (K x V each, 4 bytes an element: the
+ * start states and the C maps fp32, the M maps fp32 or, on bf16 I/O, split into
+ * two bf16 parts, in an internal order); with the standalone
  * PREP kernel the in-chunk gate sums (fp32, g's size).  Sized exactly for the
  * plan, never by N*H alone (the workspace review of the cudnn-frontend PR
  * #1056).  Validates everything kda_prefill_ws validates and launches nothing. */
