@@ -23,7 +23,8 @@ over 7 timing groups as median / p10 / p90.  `cpu_baseline` is the float64
 oracle on the host's cores (and on one thread) over a bounded sample.  The
 default (varlen, the H = 32 workload of the headline metric) also measures the
 large workload (B=16, H=64, T=8192; the roofline workload) the same way, in
-`large`.  Prints ONE JSON line.
+`large`, and the two segmented-plan workloads (eqlen: B=2, H=16, T=4096; long:
+B=1, H=8, T=65536) in `segmented`.  Prints ONE JSON line.
 """
 import argparse
 import hashlib
@@ -606,6 +607,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large", action="store_true", help="skip the large-workload sub-record of the default run")
+    ap.add_argument("--no-segmented", action="store_true",
+                    help="skip the segmented-plan sub-records (eqlen, long) of the default run")
     ap.add_argument("--peak", action="store_true", help="measure the practical HBM and MFMA ceilings instead")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="instead of the bench, copy this many MiB device-to-device 5 times (PMC calibration)")
@@ -649,9 +652,9 @@ def main():
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(r["x"], w, a.cpu_budget)
+    r = None                # the sub-records below allocate their own inputs
     if a.config == "varlen" and not a.no_large:
         # the roofline workload (B=16, H=64, T=8192), timed the same way in the same run
-        del r
         torch.cuda.empty_cache()
         wl = workloads.WORKLOADS["large"]
         steps_l = max(3, min(a.steps, 10))
@@ -660,6 +663,20 @@ def main():
                         "tokens_per_s": wl.tokens * steps_l / rl["elapsed"], "roofline": rl["roofline"],
                         "mfma": rl["mfma"], "kernel": rl["kernel"], "correctness": rl["checks"],
                         "timing_modes": rl["timing_modes"]}
+    if a.config == "varlen" and not a.no_segmented:
+        # the workloads with too few chains to fill the CUs, on segmented plans (map pass, COMBINE,
+        # segment outputs): whole-call roofline and the per-kernel split, timed the same way
+        rec["segmented"] = {}
+        rl = None
+        for name in ("eqlen", "long"):
+            rs = None
+            torch.cuda.empty_cache()
+            ws = workloads.WORKLOADS[name]
+            rs = prefill_record(kda, ws, a.steps, min(a.warmup, 5), a.groups, 8)
+            rec["segmented"][name] = {
+                "config": ws.describe(), "steps": a.steps, "ms_per_step": rs["elapsed"] / a.steps * 1e3,
+                "tokens_per_s": ws.tokens * a.steps / rs["elapsed"], "roofline": rs["roofline"], "mfma": rs["mfma"],
+                "kernel": rs["kernel"], "correctness": rs["checks"], "timing_modes": rs["timing_modes"]}
     print(json.dumps(rec))
 
 
