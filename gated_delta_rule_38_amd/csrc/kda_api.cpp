@@ -368,21 +368,22 @@ int device_cus()
 }
 
 // Segment count from a cost model in units of one chunk step of a launch that leaves most CUs
-// idle (~2.07 us on MI355X).  One segment: C steps (the longest chain's chunks).  nseg segments
+// idle (~2.07 us on MI355X).  One segment: C + 3 steps (the longest chain's chunks and the pass's
+// fixed cost below).  nseg segments
 // of ceil(C / nseg) chunks: the map pass builds segments 0 .. nseg - 2, one workgroup per
 // segment on the pipelined kernel (both maps; measured as fast per step as an output step) or
 // two on the single-role kernel, in ceil(workgroups / CUs) rounds; the output pass runs
 // ceil(chains nseg / CUs) rounds.  A pass that fills the CUs runs its steps ~1.2x slower (the
 // clock drops under full load) and pays ~3 steps of its own (the first state, the pipeline's
-// fill, the final stores); COMBINE costs ~4.4 + 0.45 per map segment.  Measured on the
-// equal-length (32 chains x 128 chunks) and long (8 x 2048) workloads, this picks their fastest
-// forced counts (8 and 32).  The cheapest count wins, ties to fewer segments, keeping >= 8
+// fill, the final stores); COMBINE costs ~4.4 + 0.45 per map segment.  Measured on MI355X over
+// 17 dense shapes (8 to 192 chains, 32 to 2048 chunks), this picks the fastest forced count at
+// every one of them.  The cheapest count wins, ties to fewer segments, keeping >= 8
 // chunks per segment.  (With every CU already holding a chain, segmenting cannot pay and one
 // segment is kept.)
 int choose_nseg(int64_t chains, int64_t C, int cus, bool merged_maps)
 {
     if (chains <= 0 || chains >= cus || C < 16) return 1;
-    double best = (double)C;
+    double best = (double)C + 3.0;
     int pick = 1;
     for (int nseg = 2; nseg <= 64 && C / nseg >= 8; ++nseg) {
         const double steps = (double)((C + nseg - 1) / nseg) + 3.0;

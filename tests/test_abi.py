@@ -435,12 +435,14 @@ def test_plan_chain_order(tmp_path):
 
 
 @pytest.mark.parametrize("B,H,T,nseg", [(2, 16, 4096, 8), (1, 8, 65536, 32), (3, 32, 4096, 1), (4, 32, 4096, 1),
-                                        (8, 32, 8192, 1), (1, 2, 256, 1), (1, 8, 16384, 32)])
+                                        (8, 32, 8192, 1), (1, 2, 256, 1), (1, 8, 16384, 32), (2, 16, 1024, 4),
+                                        (1, 16, 8192, 16), (4, 16, 8192, 4), (1, 8, 4096, 16)])
 def test_planner_segment_counts(lib, B, H, T, nseg):
     """The planner's segment count (read off the workspace size, chains x (3 nseg - 2) states)
-    on 256 CUs: the fastest forced counts measured on the equal-length and long workloads (8
-    and 32), one segment where the segment passes would need more rounds than they save (96
-    and 128 chains)."""
+    on 256 CUs: the fastest forced count measured on MI355X for each shape (equal-length 8, long
+    32; 32 chains of 1,024 tokens 4, where one segment pays its pass's fixed cost too; 16 chains
+    of 8,192 tokens 16; 64 chains of 8,192 tokens 4; 8 chains of 4,096 tokens 16), one segment
+    where the segment passes would need more rounds than they save (96 and 128 chains)."""
     D = 128
     gap = 1 << 36
     s = [desc([B, T, H, D]), desc([B, T, H, D], base=FAKE + gap), desc([B, T, H, D], base=FAKE + 2 * gap),
