@@ -74,6 +74,22 @@ def test_noalloc_matches_ws_two_calls_second_smaller(kda, forced):
         assert oracle.rel_l2(s_na.cpu().numpy(), s_ref) <= 5e-3
 
 
+def test_noalloc_split_plan_matches(kda):
+    """288 equal chains (B=9, H=32, T=1024): the planner splits the 32 chains past the CU
+    count into segments and runs the other 256 whole; the no-alloc call plans the same (its
+    scratch holds the 32 chains' maps and start states) and gives the same bits."""
+    import torch
+    w = workloads.custom([1024] * 9, H=32, D=128, dense=True, seed=520)
+    x = workloads.make_inputs(w, device="cuda")
+    need = kda.workspace_size(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], None)
+    dd = 128 * 128 * 4
+    say("noalloc split plan", "scratch", need)
+    assert 0 < need <= kda.NOALLOC_SCRATCH_BYTES and need % (32 * dd) == 0     # 32 segmented chains only
+    (o_ws, s_ws), (o_na, s_na) = both(kda, x)
+    assert torch.equal(bits(o_ws), bits(o_na)) and torch.equal(bits(s_ws), bits(s_na))
+    assert not torch.isnan(o_na.float()).any() and not torch.isnan(s_na).any()
+
+
 def test_noalloc_single_segment_and_standalone_prep(kda):
     import torch
     w = workloads.custom([900, 1, 77], H=2, D=128, seed=510)
