@@ -614,7 +614,7 @@ def main():
                     help="instead of the bench, copy this many MiB device-to-device 5 times (PMC calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -4,7 +4,7 @@
 // Per 64-token chunk with start state S0 (d_k x d_v fp32, row = key channel),
 // in-chunk inclusive log-decay cumsum Gamma (vector over key channels), the WY/UT
 // form of the gated delta rule (derived from the recurrence; the pages name the
-// "WY-form chunk" in TensorRT-LLM PR #19960 and use 64-token chunks, "v64", in
+// WY-form chunk in TensorRT-LLM PR #19960 and use 64-token chunks (v64) in
 // the cudnn-frontend Hopper kernel of PR #1056):
 //     A_ij = beta_i sum_c k_ic k_jc e^{G_ic - G_jc}  (j < i),   T = (I + A)^-1
 //     P_ij =        sum_c q_ic k_jc e^{G_ic - G_jc}  (j <= i)

@@ -1,6 +1,6 @@
 // COMBINE kernel: the sequential scan of segment maps for chains too few to
 // fill the GPU (the segment-scan COMBINE of the cudnn-frontend Hopper KDA
-// prefill PR #1056, which scans "independent value-row slabs").
+// prefill PR #1056, which scans the state's value columns in independent slabs).
 //
 // A segment of a chain maps its start state affinely to its end state,
 //     S_end = M_s S_start + C_s,

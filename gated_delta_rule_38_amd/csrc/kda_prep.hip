@@ -1,7 +1,7 @@
 // PREP kernel: the in-chunk inclusive cumulative sum of the log decays g.
 //
 // Chunks are `chunk` tokens (the chunk kernel's length) and restart at every sequence start, so a chunk never
-// straddles two sequences -- the "gap-safe virtual chunk mapping" of the
+// straddles two sequences -- the virtual chunk map, safe across sequence gaps, of the
 // cudnn-frontend Hopper KDA prefill PR (#1056, walkthrough).  Virtual chunk v
 // maps to (sequence n, chunk j of n) through the running count of
 // ceil(len_n / chunk); the packed layout's grid is the host-known bound

@@ -19,9 +19,9 @@
  * unless KDA_CHECK=1 (below) checks them first.  beta is the value in (0, 1)
  * (no sigmoid is applied).  No scale is applied to q.  The kernels compute the
  * chunked WY/UT form of this recurrence (TensorRT-LLM PR #19960 names the
- * "WY-form chunk"): the production kernel (head size 128, bf16) takes 32-token
+ * WY-form chunk): the production kernel (head size 128, bf16) takes 32-token
  * chunks, the others (head size 64, the fp32 debug mode, variant 1) 64-token
- * chunks ("v64" in the cudnn-frontend kernel name); results do not depend on
+ * chunks (the v64 of the cudnn-frontend kernel name); results do not depend on
  * the chunk length beyond rounding.
  *
  * Tensors (all pointers are DEVICE memory owned by the caller; the library
@@ -93,7 +93,7 @@ typedef enum {
     KDA_ERR_DTYPE = 3,       /* dtype not allowed for that argument                 */
     KDA_ERR_LAYOUT = 4,      /* last-dimension stride != 1 or negative stride       */
     KDA_ERR_ALIAS = 5,       /* forbidden overlap between outputs and inputs        */
-    KDA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement         */
+    KDA_ERR_UNSUPPORTED = 6, /* valid request this library does not implement       */
     KDA_ERR_WORKSPACE = 7,   /* workspace too small or allocation failed            */
     KDA_ERR_HIP = 8,         /* HIP runtime error while enqueueing                  */
     KDA_ERR_RANGE = 9        /* an input value outside its documented range         */
@@ -112,7 +112,7 @@ typedef struct {
     int64_t stride[4];
 } kda_tensor_t;
 
-/* Planner and test knobs.  A zero-filled struct (or NULL) means "automatic". */
+/* Planner and test knobs.  A zero-filled struct (or NULL) means automatic. */
 typedef struct {
     int32_t nseg;          /* segments per (sequence, head) chain; 0 = planner's choice, 1..64 forces */
     int32_t prep;          /* 0 or 2 = in-chunk (fused) gate scan; 1 = standalone PREP kernel first     */
@@ -121,7 +121,7 @@ typedef struct {
     int32_t variant;       /* 0 = planner; 1 = single-role 64-token chunk kernel; 2 = pipelined      */
                            /* 32-token chunk kernel (head size 128, bf16 only)                       */
     /* Activations fused into the gate scan (the production gate lower bound of the
-     * cudnn-frontend PR's correctness section, and the "beta_sigmoid" path of the
+     * cudnn-frontend PR's correctness section, and the beta-sigmoid path of the
      * TensorRT-LLM KDA prefill fix PR #19826):
      *   gate_act = 1: g holds logits x and the log decay is gate_lower_bound * sigmoid(x),
      *                 gate_lower_bound in [-5, 0] (the range the kernels are guaranteed on);
@@ -227,7 +227,7 @@ kda_status_t kda_prefill_noalloc(const kda_tensor_t *q, const kda_tensor_t *k, c
 /*
  * kda_prep -- the standalone PREP kernel: the in-chunk inclusive cumulative sum
  * of g over `chunk`-token chunks (32 or 64) that restart at every sequence
- * start (the "gap-safe virtual chunk mapping" of the cudnn-frontend PR's
+ * start (the virtual chunk map, safe across sequence gaps, of the cudnn-frontend PR's
  * walkthrough: a chunk never straddles two sequences).  gamma has g's shape
  * and dtype (fp32), must not overlap g, and receives for token t of chunk
  * [t0, t0 + L):

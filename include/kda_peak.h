@@ -1,5 +1,5 @@
 /*
- * kda_peak.h -- measurement probes for the rooflines the KDA prefill is judged
+ * kda_peak.h -- measurement probes for the rooflines the KDA prefill is measured
  * against on MI355X (not part of the KDA path): the HBM bandwidth a plain stream
  * of the chunk kernel's read/write mix reaches, and the bf16 matrix-core rate a
  * loop of independent MFMAs reaches.  Both enqueue one kernel on `stream`,

@@ -21,7 +21,7 @@ Contents
                            whole tensor in float64.
 
 The method (the reading of the pages, which name Kimi Delta Attention and its
-"WY-form chunk" but never print the recurrence): per sequence n and head h,
+a WY-form chunk but never print the recurrence): per sequence n and head h,
     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
     o_t = S_t^T q_t,
 S_{-1} = initial state (zeros if None); the final state is S after the last
@@ -147,7 +147,7 @@ def activations(g_logits=None, beta_logits=None, lower_bound: float = -5.0):
 
     The pages name a production gate lower bound of -5 (cudnn-frontend PR #1056,
     correctness section: the fp64 oracle is run "at the production gate") and a
-    "beta_sigmoid" prefill test (TensorRT-LLM PR #19826, description) but print
+    beta-sigmoid prefill test (TensorRT-LLM PR #19826, description) but print
     no formula; the reading taken here is the plainest one consistent with a
     lower bound: the per-token, per-channel log decay is lower_bound * sigmoid(x),
     so it lies in [lower_bound, 0], and beta = sigmoid(b) lies in (0, 1).

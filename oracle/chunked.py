@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  It pins the token
 recurrence and the chunk algebra the HIP kernels use: run with chunk sizes 16
 and 64 it must agree with ``oracle.recurrence`` to ~1e-12 (pin P7).
 
-The pages name a "WY-form chunk" (TensorRT-LLM PR #19960, KDA MTP verify item)
-and 64-token chunks ("v64" in the cudnn-frontend Hopper kernel's name, PR #1056)
+The pages name a WY-form chunk (TensorRT-LLM PR #19960, KDA MTP verify item)
+and 64-token chunks (the v64 of the cudnn-frontend Hopper kernel's name, PR #1056)
 but print no chunk equations.  The form below is derived from the recurrence.
 Unrolling S_t = D_t S_{t-1} + k_t u_t^T inside one chunk (rows 0..L-1, start
 state S0, Gamma_i = sum_{s<=i} g_s the in-chunk inclusive cumulative sum of the

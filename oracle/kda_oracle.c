@@ -8,7 +8,7 @@
  * What it computes (the reading taken of the pages): Kimi Delta Attention, the
  * gated delta-rule recurrence that the TensorRT-LLM KDA prefill kernel
  * (PR #19826) and the cudnn-frontend Hopper KDA prefill (PR #1056) implement.
- * The pages name the method but never print its equations; this build reads it
+ * The pages name the method but never print its equations; this oracle reads it
  * as, for every sequence n and head h independently, over the sequence's tokens
  * t in order,
  *
@@ -18,9 +18,9 @@
  * with S a d_k x d_v matrix (row = key channel), S_{-1} the initial state
  * (zeros when none is given), and the final state S after the last token.
  * Decay is applied first, the delta correction is taken against the decayed
- * state, and the output reads the updated state.  The cudnn-frontend PR scores
- * its kernel against "an fp64 oracle at the production gate with a non-zero
- * initial_state" (Correctness section); this is that oracle for this build.
+ * state, and the output reads the updated state.  The cudnn-frontend PR checks
+ * its kernel against a float64 oracle run at the production gate bound with a
+ * non-zero initial state (Correctness section); this file is such an oracle.
  *
  * The update is written as the equivalent rank-one form
  *     S <- D S;  r = k^T S;  S <- S + beta k (v - r)^T

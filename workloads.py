@@ -12,7 +12,7 @@ Value recipe (the reading of the workloads; the pages fix only the gate floor):
     [-5, 0].  -5 is the production ``gate_lower_bound`` the cudnn-frontend
     Hopper KDA prefill PR (#1056, description and "Correctness") measures at;
   * beta = sigmoid(N(0, 1)) in float32, already a value in (0, 1) (the
-    TensorRT-LLM KDA prefill fix PR #19826 names a "beta_sigmoid" test);
+    TensorRT-LLM KDA prefill fix PR #19826 names a beta-sigmoid test);
   * initial state ~ N(0, 0.1^2) in float32 (sigma = 0.1), or zeros;
   * the long-sequence workload pins 13 of 128 channels of every head at exactly
     g = -5 for every token (10% of channels at the gate floor).
