@@ -146,7 +146,7 @@ def activations(g_logits=None, beta_logits=None, lower_bound: float = -5.0):
     """Float64 activations for gate and beta inputs given as logits.
 
     The pages name a production gate lower bound of -5 (cudnn-frontend PR #1056,
-    correctness section: the fp64 oracle is run "at the production gate") and a
+    correctness section: its fp64 oracle runs at that production bound) and a
     beta-sigmoid prefill test (TensorRT-LLM PR #19826, description) but print
     no formula; the reading taken here is the plainest one consistent with a
     lower bound: the per-token, per-channel log decay is lower_bound * sigmoid(x),
