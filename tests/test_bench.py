@@ -160,3 +160,21 @@ def test_whole_call_timed_by_bracketing_events():
     assert kern["avg_ms"] == 0.40 and kern["kernels_ms_per_step"] == pytest.approx(0.38)
     assert roof["achieved"] == pytest.approx(bench.algorithmic(w)[0] / 0.40e-3 / 1e9)
     assert sum(s["share"] for s in kern["split"]) == pytest.approx(1.0)
+
+
+def test_committed_traffic_figures_match_the_current_kernel_sources():
+    """Every committed HBM-traffic figure was taken on the kernel sources as they stand (the
+    bench reports null for a stale one): a kernel edit without a fresh counter pass shows up
+    here.  The figure itself sits within a few per cent of the algorithmic bytes (single
+    launches) or above them by the segmented path's maps and second input pass."""
+    import glob
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")))
+    assert len(files) >= 7
+    for f in files:
+        rec = json.load(open(f))
+        kernel = os.path.basename(f)[: -len("_" + rec["workload"] + "_traffic.json")]
+        assert kernel in bench.KERNEL_SOURCES, f
+        assert rec["kernel_source_sha"] == bench.source_sha(kernel), f"{f}: taken on other kernel sources"
+        assert os.path.exists(os.path.join(ROOT, "profiles", rec["source"])), f
+        ratio = rec["hbm_bytes_per_launch"] / rec.get("algorithmic_bytes", rec.get("algorithmic_bytes_per_launch"))
+        assert (0.99 <= ratio <= 1.05) if kernel != "whole_call" else (1.5 <= ratio <= 2.2), (f, ratio)
