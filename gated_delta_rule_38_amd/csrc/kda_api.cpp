@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -354,10 +355,19 @@ struct Plan {
     int chunk = 64;
     bool standalone_prep = false;
     bool lpt = false;           // chains started longest sequence first
+    int cap_slots = 0;          // capped concurrency: groups of H workgroups (0 = off)
     size_t off_gamma = 0, off_maps = 0, off_start = 0, bytes = 0;
+    size_t off_flags = 0;       // the capped schedule's flags, last in the workspace: a smaller
+                                // workspace that holds everything before them runs uncapped
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Capped concurrency: on MI355X the chunk kernel's step time stays within 6% of its low-load
+// value up to about 160 concurrent chains (dense 4,096-token chains: 128 -> 2.00 us, 160 ->
+// 2.04, 192 -> 2.26, 256 -> 2.67 us per step).
+constexpr int64_t kCapChains = 160;
+std::atomic<uint32_t> g_cap_epoch{0};
 
 int device_cus()
 {
@@ -474,6 +484,20 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
     if (o && o->out_gate && 32 * o->out_gate->stride[o->out_gate->ndim - 3] * 2 + 1024 > (int64_t)INT32_MAX)
         return fail(KDA_ERR_UNSUPPORTED, "out_gate token stride too large for the pipelined kernel");
     pl.standalone_prep = prep == 1;   // otherwise every chunk-kernel pass scans its own chunks
+    // Capped concurrency (the kernel's cap_wait): a packed batch on one segment with every chain
+    // resident at once, and more chains than the cap.  The kernel decides from the lengths
+    // whether the packing leaves the longest sequence as the bound, else it runs uncapped.
+    // KDA_CAP sets the cap in chains (0 turns it off).
+    {
+        const char *ce = getenv("KDA_CAP");
+        const int64_t cap = ce ? atoll(ce) : kCapChains;
+        const int64_t S = (cap > 0 && P.H > 0) ? cap / P.H : 0;
+        const int cus = device_cus();
+        const bool norm = o && o->out_gate;
+        if (pl.pipe && !P.dense && !norm && P.N > 1 && P.N <= kda::CAP_MAX_N && chains <= cus && S >= 1 &&
+            S * P.H < chains && S <= kda::CAP_MAX_SLOTS && P.N * S <= kda::CAP_MAX_WORK)
+            pl.cap_slots = (int)S;
+    }
     auto layout = [&](int nseg) {
         size_t off = 0;
         if (pl.standalone_prep) {
@@ -488,6 +512,10 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
             pl.off_start = off;
             off += align256(sc * nseg * dd);
         }
+        if (nseg == 1 && pl.cap_slots > 0) {
+            pl.off_flags = off;
+            off += align256((size_t)chains * 4);
+        }
         return off;
     };
     pl.bytes = layout(pl.nseg);
@@ -499,6 +527,10 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
         while (pl.nseg > 1 && layout(pl.nseg) > max_bytes) --pl.nseg;
         if (pl.nseg == 1) pl.seg_chains = 0;
         pl.bytes = layout(pl.nseg);
+        if (pl.bytes > max_bytes) {      // only the capped schedule's flags can be left
+            pl.cap_slots = 0;
+            pl.bytes = layout(pl.nseg);
+        }
     }
     // Chain order.  With more chains than CUs, workgroups start in launch order as CUs free up,
     // so a packed batch of mixed lengths finishes sooner when its longest sequences start first
@@ -507,14 +539,16 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
     // at most LPT_MAX_SEQ sequences).  KDA_ORDER=natural or =longest overrides the choice.
     const char *ord = getenv("KDA_ORDER");
     const bool lpt_ok = pl.pipe && pl.nseg == 1 && !P.dense && P.N > 1 && P.N <= kda::LPT_MAX_SEQ;
+    if (pl.nseg > 1) pl.cap_slots = 0;
     if (ord && strcmp(ord, "natural") == 0) pl.lpt = false;
     else if (ord && strcmp(ord, "longest") == 0) pl.lpt = lpt_ok;
     else pl.lpt = lpt_ok && chains > device_cus();
     if (env_on("KDA_LOG"))
-        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d segmented=%lld kernel=%s chunk=%d prep=%s order=%s workspace=%zu B\n",
+        fprintf(stderr, "kda: plan N=%lld H=%lld D=%lld %s chains=%lld nseg=%d segmented=%lld kernel=%s chunk=%d prep=%s order=%s cap=%d workspace=%zu B\n",
                 (long long)P.N, (long long)P.H, (long long)P.D, P.dense ? "dense" : "packed", (long long)chains,
                 pl.nseg, (long long)pl.seg_chains, pl.pipe ? "pipelined" : "single-role", pl.chunk,
-                pl.standalone_prep ? "standalone" : "in-chunk", pl.lpt ? "longest-first" : "natural", pl.bytes);
+                pl.standalone_prep ? "standalone" : "in-chunk", pl.lpt ? "longest-first" : "natural",
+                pl.cap_slots * (int)P.H, pl.bytes);
     return KDA_OK;
 }
 
@@ -568,9 +602,12 @@ hipError_t timed(const char *name, hipStream_t st, F &&launch)
 kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void *ws, size_t ws_bytes, hipStream_t st,
                  int32_t *check_flags = nullptr)
 {
-    if (ws_bytes < pl.bytes || (pl.bytes && !ws))
+    // the capped schedule's flags come last: a workspace without them runs uncapped
+    const size_t need = pl.cap_slots > 0 ? pl.off_flags : pl.bytes;
+    if (ws_bytes < need || (need && !ws))
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.bytes);
-    if (pl.bytes && ((uintptr_t)ws % 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws && need && ((uintptr_t)ws % 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const bool cap_on = pl.cap_slots > 0 && ws && ws_bytes >= pl.bytes && (uintptr_t)ws % 256 == 0;
     const int64_t chains = P.N * P.H;
     if (chains == 0) return KDA_OK;
     char *wsb = (char *)ws;
@@ -609,6 +646,17 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     cp.gate_lb = o ? o->gate_lower_bound : 0.f;
     cp.beta_act = (o && o->beta_act) ? 1 : 0;
     cp.lpt = pl.lpt ? 1 : 0;
+    if (cap_on) {
+        cp.cap_slots = pl.cap_slots;
+        cp.cap_flags = (uint32_t *)(wsb + pl.off_flags);
+        // a fresh value per call, never 0: flags left by earlier calls (or the workspace's first
+        // contents, unless they happen to match) do not release a waiting workgroup early
+        uint32_t e = g_cap_epoch.fetch_add(1) + 1;
+        if (e == 0) e = g_cap_epoch.fetch_add(1) + 1;
+        cp.cap_epoch = e;
+        const char *we = getenv("KDA_CAP_WAIT_US");
+        cp.cap_wait_us = we ? std::max(1, atoi(we)) : 0;
+    }
     if (o && o->out_gate) {
         cp.z = o->out_gate->data;
         cp.nw = (const float *)o->norm_weight->data;

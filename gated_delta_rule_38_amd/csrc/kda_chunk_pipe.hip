@@ -84,6 +84,10 @@ constexpr int S_NRM = SMEM;
 constexpr int S_NW = S_NRM + C * 4 * 4;
 constexpr int SMEM_NORM = S_NW + D * 4;
 static_assert(SMEM_NORM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+// capped concurrency (without the norm): its packing scratch where the norm keeps its sums
+constexpr int S_CAP = SMEM;
+constexpr int SMEM_CAP = S_CAP + 4 * (3 * CAP_MAX_N + 2 * CAP_MAX_SLOTS + 4);
+static_assert(SMEM_CAP <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
 static_assert(4 * (LPT_MAX_SEQ + 1) <= B_SIZE, "longest-first scratch fits in operand buffer 0");
 static_assert(B_SIZE % 16 == 0 && S_GRAW % 16 == 0 && S_X % 16 == 0 && S_A10 % 16 == 0 && S_AD % 16 == 0 && S_TB % 16 == 0 &&
               S_SC % 16 == 0 && S_DEC % 16 == 0 && S_BETA % 16 == 0, "16-byte aligned regions");
@@ -117,6 +121,65 @@ __device__ int longest_first(const int32_t *cu, int N, int r, char *smem)
     const int n = sLen[N];
     __syncthreads();
     return n;
+}
+
+// Capped concurrency: the step time of this kernel hardly depends on how many chains run at
+// once up to about 160 of 256 CUs and then climbs (the clock and HBM under full load), while a
+// packed batch of mixed lengths ends with its longest chain.  So the sequences are packed,
+// longest first, into cap_slots groups of H workgroups (each into the least-loaded group; the
+// per-sequence cost is its chunks plus 3 for the pipeline's fill), and when the longest
+// sequence alone still bounds the packing, a workgroup whose sequence follows another one in
+// its group waits for that sequence's chain of the same head to finish before its main loop.
+// Every chain is resident at once (chains <= CUs), so a predecessor is always running; the
+// wait is bounded all the same, and it orders no data.  Every thread calls it at the same
+// point of its prologue (after its first loads are issued, so their latency overlaps); thread
+// i < N brings sequence i's length in tokens; sc is the dedicated scratch (S_CAP).
+__device__ void cap_wait(const ChunkParams &p, int n, int h, int len_i, char *sc)
+{
+    const int N = p.N, S = p.cap_slots;
+    int *sLen = (int *)sc, *sOrd = sLen + CAP_MAX_N, *sPred = sOrd + CAP_MAX_N, *sLoad = sPred + CAP_MAX_N;
+    int *sLast = sLoad + CAP_MAX_SLOTS, *sOk = sLast + CAP_MAX_SLOTS;
+    if ((int)threadIdx.x < N) sLen[threadIdx.x] = (len_i + C - 1) / C + 3;
+    __syncthreads();
+    if ((int)threadIdx.x < N) {
+        const int i = threadIdx.x, li = sLen[i];
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = sLen[j];
+            rank += (lj > li) | ((lj == li) & (j < i));
+        }
+        sOrd[rank] = i;                 // the ranks are a permutation
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int g = 0; g < S; ++g) {
+            sLoad[g] = 0;
+            sLast[g] = -1;
+        }
+        for (int r = 0; r < N; ++r) {
+            const int i = sOrd[r];
+            int best = 0;
+            for (int g = 1; g < S; ++g) best = sLoad[g] < sLoad[best] ? g : best;
+            sPred[i] = sLast[best];
+            sLast[best] = i;
+            sLoad[best] += sLen[i];
+        }
+        int most = 0;
+        for (int g = 0; g < S; ++g) most = max(most, sLoad[g]);
+        const int pred = (most <= sLen[sOrd[0]] + 2) ? sPred[n] : -1;
+        if (pred >= 0) {
+            // bound: the given one, else 8 us per chunk of the predecessor plus 2 ms (100 MHz ticks)
+            const uint64_t limit = 100ull * (p.cap_wait_us > 0 ? (uint64_t)p.cap_wait_us
+                                                                  : 8ull * (uint64_t)sLen[pred] + 2000ull);
+            const uint32_t *f = p.cap_flags + (int64_t)pred * p.H + h;
+            const uint64_t ts = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.cap_epoch &&
+                   __builtin_amdgcn_s_memrealtime() - ts < limit)
+                __builtin_amdgcn_s_sleep(32);
+        }
+        (void)sOk;
+    }
+    __syncthreads();
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4a+b receives
@@ -200,7 +263,7 @@ __device__ __forceinline__ void decay_tile(f32x16 &s, const float4 dd)
 template <bool STALL, bool OUT, bool NORM, bool MC>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
-    __shared__ __attribute__((aligned(16))) char smem[NORM ? SMEM_NORM : SMEM];
+    __shared__ __attribute__((aligned(16))) char smem[NORM ? SMEM_NORM : (OUT && !MC) ? SMEM_CAP : SMEM];
     float *sG = (float *)(smem + S_G), *sGraw = (float *)(smem + S_GRAW);
     bf16 *sX = (bf16 *)(smem + S_X), *sY = (bf16 *)(smem + S_Y), *sZ = (bf16 *)(smem + S_Z);
     bf16 *sKb = (bf16 *)(smem + S_KB), *sA10 = (bf16 *)(smem + S_A10);
@@ -302,6 +365,9 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     }
     const int h = chain % p.H;
     const int n = p.lpt ? longest_first(p.cu, p.N, chain / p.H, smem) : chain / p.H;
+    const bool capped = OUT && !MC && !NORM && role == ROLE_OUT && p.cap_slots > 0;
+    int cap_len = 0;                    // capped: sequence tid's length (threads tid < N), for cap_wait
+    if (capped && tid < p.N) cap_len = p.cu[tid + 1] - p.cu[tid];
     int64_t t0, bsel;
     int len;
     seq_range(p.cu, n, p.T, t0, len, bsel);
@@ -494,6 +560,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
             stage_g(c_begin, 0);
             prefetch_g(min(c_begin + 1, c_last));
         }
+        if (capped) cap_wait(p, n, h, cap_len, smem + S_CAP);
         sync();
         if (nck > 0 && sc >= 0) {
             float4 gcol[C / 4];
@@ -709,6 +776,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         Frag8<bf16> IdV[2];
         if constexpr (!MC) make_idv(IdV);
         if (nck > 0) prefetch_qkv(c_begin);
+        if (capped) cap_wait(p, n, h, cap_len, smem + S_CAP);
         sync();
         sync();
         for (int t = 0; nck > 0 && t <= nck; ++t) {
@@ -922,6 +990,10 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) dsth[(32 * m + 8 * q + 4 * g2 + r) * p.sT_sr + vcol] = (bf16)S[m][4 * q + r];
         }
+        // capped concurrency: this chain is done (its last stores are issued); a workgroup
+        // queued behind its sequence may start
+        if (capped && tid == 0)
+            __hip_atomic_store(p.cap_flags + (int64_t)n * p.H + h, p.cap_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

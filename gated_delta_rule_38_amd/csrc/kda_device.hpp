@@ -314,10 +314,25 @@ struct ChunkParams {
     // 0 .. seg_chain0 - 1 whole (ROLE_OUT).
     int32_t seg_chain0;
     int32_t n_segwg;
+    // Capped concurrency (packed layout, one segment, every chain resident at once): the
+    // sequences, longest first, are packed into cap_slots groups of H workgroups, each
+    // sequence into the least-loaded group; a workgroup whose sequence follows another one in
+    // its group first waits until the chain of the same head of that sequence has set its
+    // flag to cap_epoch, or until cap_wait_us (0: a bound from the predecessor's length) has
+    // passed.  The wait orders no data: it only keeps fewer chains running at once.  0 = off.
+    int32_t cap_slots;
+    uint32_t cap_epoch;
+    int32_t cap_wait_us;
+    uint32_t *cap_flags;       // [N * H] in the workspace, chain n * H + h
 };
 
 // Longest-first chain order: at most this many sequences (one launch ranks them all in LDS).
 constexpr int LPT_MAX_SEQ = 512;
+// Capped concurrency: at most this many groups, and N * groups <= CAP_MAX_WORK (one thread
+// packs the sequences at the start of every workgroup).
+constexpr int CAP_MAX_SLOTS = 16;
+constexpr int CAP_MAX_WORK = 4096;
+constexpr int CAP_MAX_N = 128;     // sequences
 
 struct PrepParams {
     const float *g;

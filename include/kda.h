@@ -73,6 +73,19 @@
  *                ranks the lengths on the device); results are the same bits in any
  *                order.  KDA_ORDER=natural keeps launch order, KDA_ORDER=longest ranks
  *                whenever the plan allows it.
+ *   KDA_CAP      chains allowed to run at once in a packed single-segment launch whose
+ *                chains all fit the compute units (default 160; 0 turns it off).  With
+ *                more chains than that (at most 128 sequences, no output norm), the
+ *                kernel packs the sequences longest first into groups of H workgroups and,
+ *                when the longest sequence still bounds the packing, a workgroup whose
+ *                sequence follows another in its group waits (bounded) for that
+ *                sequence's chain of the same head before its main loop: mixed-length
+ *                batches finish sooner, results are the same bits.  The plan then needs 4
+ *                bytes of workspace per chain, last in the workspace; a workspace without
+ *                them runs the launch uncapped.  A captured graph replays one call's flag
+ *                value, so replays after the first run uncapped.
+ *   KDA_CAP_WAIT_US  bound of each such wait in microseconds (test knob; default: 8 us
+ *                per chunk of the awaited sequence plus 2 ms).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -171,7 +184,8 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
                          kda_tensor_t *out, kda_tensor_t *final_state, void *stream);
 
 /* Bytes of device workspace kda_prefill_ws needs for these descriptors and
- * options: 0 when the plan is a single chunk-kernel launch; with nseg > 1 the
+ * options: 0 when the plan is a single chunk-kernel launch (4 bytes per chain when it
+ * caps the chains running at once, see KDA_CAP); with nseg > 1 the
  * segment maps and segment start states (K x V each, 4 bytes an element: the
  * start states and the C maps fp32, the M maps fp32 or, on bf16 I/O, split into
  * two bf16 parts, in an internal order); with the standalone

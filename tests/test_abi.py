@@ -530,3 +530,41 @@ def test_planner_splits_chains_just_above_the_cu_count(tmp_path):
     assert "status 0 bytes 0" in cases[1] and "nseg=1 segmented=0" in plans[1]
     assert "status 0" in cases[2] and f"bytes {2 * (3 * 3 - 2) * dd}" in cases[2] and "nseg=3 segmented=2" in plans[2]
     assert "status 6" in cases[3] and "status 6" in cases[4]
+
+
+def test_plan_capped_concurrency(tmp_path):
+    """A packed single-segment launch with every chain resident (<= 256 without a GPU) and
+    more chains than the cap (160) plans the capped schedule: groups of H workgroups, a
+    4-byte flag per chain last in the workspace.  Not with at most 160 chains, more chains
+    than CUs (longest first instead), the dense layout, more than 16 groups, or KDA_CAP=0."""
+    import subprocess, sys, textwrap
+    code = textwrap.dedent(f"""
+        import ctypes, os, sys
+        sys.path.insert(0, {ROOT!r}); sys.path.insert(0, {os.path.join(ROOT, 'tests')!r})
+        import test_abi as t
+        import gated_delta_rule_38_amd as kda
+        lib = kda.load_library()
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        def plan(T, H, N, cap=None):
+            os.environ.pop("KDA_CAP", None)
+            if cap is not None: os.environ["KDA_CAP"] = str(cap)
+            s = t.packed_set(T=T, H=H, N=N)
+            n = ctypes.c_size_t(0)
+            st = lib.kda_prefill_workspace_size(*(r(s[x]) for x in ("q", "k", "v", "g", "beta", "s0", "cu", "out", "sT")),
+                                                ctypes.byref(kda.options(nseg=1)), ctypes.byref(n))
+            sys.stderr.flush()
+            print("case", T, H, N, cap, "status", st, "bytes", n.value, flush=True)
+        plan(32768, 32, 8)               # 256 chains: 5 groups of 32
+        plan(32768, 32, 8, 0)            # turned off
+        plan(32768, 32, 4)               # 128 chains: under the cap
+        plan(32768, 64, 5)               # 320 chains > 256 CUs: longest first
+        plan(32768, 2, 100)              # 200 chains in 80 groups of 2: more than 16 groups
+        plan(32768, 16, 12, 96)          # a cap of 96 chains: 6 groups of 16
+    """)
+    env = dict(os.environ, KDA_LOG="1")
+    p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0 and p.stdout.count("status 0") == 6, p.stdout + p.stderr[-2000:]
+    caps = [int(l.split("cap=")[1].split()[0]) for l in p.stderr.splitlines() if l.startswith("kda: plan")]
+    assert caps == [160, 0, 0, 0, 0, 96], caps
+    sizes = [int(l.split("bytes ")[1]) for l in p.stdout.splitlines() if l.startswith("case")]
+    assert sizes == [1024, 0, 0, 0, 0, 768], sizes

@@ -716,6 +716,39 @@ def test_longest_first_order_same_bits(kda, monkeypatch):
     check_chains(x, out, sT, [(5, 47), (1, 0), (3, 20), (2, 5)], TOL["bf16"])
 
 
+def test_capped_concurrency_same_bits(kda, monkeypatch):
+    """The capped schedule (packed, one segment, more chains than the 160-chain cap, every
+    chain resident) only delays when some workgroups start: outputs and final states are the
+    bits of the uncapped launch (KDA_CAP=0).  On the varlen lengths the packing leaves the
+    longest sequence as the bound, so the short sequences queue; on equal lengths it would
+    lengthen the call and nothing waits.  Each also with every wait cut short by a 1 us bound
+    (KDA_CAP_WAIT_US=1), a stalled wave and the output norm; then the capped varlen batch
+    against the oracle on its longest, shortest and queued sequences."""
+    import torch
+    varl = workloads.custom(workloads.varlen_lengths(), H=32, D=128, seed=95)    # 256 chains
+    eq = workloads.custom([1000] * 8, H=32, D=128, seed=96)
+    for w in (varl, eq):
+        x = gen(w)
+        z, nw = _norm_inputs(x, 97)
+        for kw, env in ((dict(nseg=1), {}), (dict(nseg=1), {"KDA_CAP_WAIT_US": "1"}),
+                        (dict(nseg=1, stall_wave=3, stall_cycles=127 * 2), {}),
+                        (dict(nseg=1, out_gate=z, norm_weight=nw, norm_eps=1e-6), {})):
+            say("capped", w.lengths, w.H, sorted(kw), env)
+            monkeypatch.setenv("KDA_CAP", "0")
+            o0, s0 = run(kda, x, **kw)
+            monkeypatch.delenv("KDA_CAP")
+            for k, v in env.items():
+                monkeypatch.setenv(k, v)
+            o1, s1 = run(kda, x, **kw)
+            for k in env:
+                monkeypatch.delenv(k)
+            torch.cuda.synchronize()
+            assert torch_equal(o0, o1) and torch_equal(s0, s1)
+    x = gen(varl)
+    out, sT = run(kda, x)
+    check_chains(x, out, sT, [(7, 0), (7, 31), (4, 5), (0, 17), (6, 31), (3, 2)], TOL["bf16"])
+
+
 @pytest.mark.parametrize("as_handle", [False, True])
 def test_explicit_stream_argument(kda, as_handle):
     """prefill(stream=...) on a stream other than torch's current one, given as a
