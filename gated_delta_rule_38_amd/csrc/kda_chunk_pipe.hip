@@ -149,9 +149,12 @@ __device__ void cap_wait(const ChunkParams &p, int n, int h, int len_i, char *sc
             rank += (lj > li) | ((lj == li) & (j < i));
         }
         sOrd[rank] = i;                 // the ranks are a permutation
+        if (i == n) sOk[0] = rank;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    // the S longest sequences open the groups: their workgroups (the ones that bound the call)
+    // skip the packing
+    if (threadIdx.x == 0 && sOk[0] >= S) {
         for (int g = 0; g < S; ++g) {
             sLoad[g] = 0;
             sLast[g] = -1;
@@ -177,7 +180,6 @@ __device__ void cap_wait(const ChunkParams &p, int n, int h, int len_i, char *sc
                    __builtin_amdgcn_s_memrealtime() - ts < limit)
                 __builtin_amdgcn_s_sleep(32);
         }
-        (void)sOk;
     }
     __syncthreads();
 }
