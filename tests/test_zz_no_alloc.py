@@ -90,6 +90,22 @@ def test_noalloc_split_plan_matches(kda):
     assert not torch.isnan(o_na.float()).any() and not torch.isnan(s_na).any()
 
 
+def test_noalloc_capped_plan_matches(kda):
+    """A packed batch of mixed lengths whose 256 chains fit the CUs runs the capped schedule
+    (short sequences queue behind others, their flags in the scratch): the no-alloc call gives
+    kda_prefill's bits, twice in a row (the flags of the first call are left in the
+    scratch)."""
+    import torch
+    w = workloads.custom(workloads.varlen_lengths(), H=32, D=128, seed=530)
+    x = workloads.make_inputs(w, device="cuda")
+    need = kda.workspace_size(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
+    say("noalloc capped plan", "scratch", need)
+    assert need == 256 * 4                                    # one flag per chain
+    for i in range(2):
+        (o_ws, s_ws), (o_na, s_na) = both(kda, x)
+        assert torch.equal(bits(o_ws), bits(o_na)) and torch.equal(bits(s_ws), bits(s_na)), f"call {i}"
+
+
 def test_noalloc_single_segment_and_standalone_prep(kda):
     import torch
     w = workloads.custom([900, 1, 77], H=2, D=128, seed=510)
