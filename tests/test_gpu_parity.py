@@ -749,6 +749,35 @@ def test_capped_concurrency_same_bits(kda, monkeypatch):
     check_chains(x, out, sT, [(7, 0), (7, 31), (4, 5), (0, 17), (6, 31), (3, 2)], TOL["bf16"])
 
 
+def _capped_case(i):
+    rng = np.random.default_rng(7000 + i)
+    H = int(rng.choice([16, 32, 64]))
+    N = int(rng.integers(161 // H + 1, 256 // H + 1))
+    lengths = [int(x) if rng.random() > 0.1 else 0 for x in rng.integers(1, 2500, N)]
+    return lengths, H
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_capped_concurrency_random_batches(kda, monkeypatch, i):
+    """Seeded packed batches of 161 to 256 chains (mixed lengths, some empty sequences, 16 to
+    64 heads: 10, 5 or 2 groups): the capped schedule gives the uncapped bits, and sampled
+    chains match the oracle."""
+    import torch
+    lengths, H = _capped_case(i)
+    say("capped random", i, lengths, H)
+    x = gen(workloads.custom(lengths, H=H, D=128, seed=7100 + i))
+    monkeypatch.setenv("KDA_CAP", "0")
+    o0, s0 = run(kda, x)
+    monkeypatch.delenv("KDA_CAP")
+    o1, s1 = run(kda, x)
+    torch.cuda.synchronize()
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+    N = len(lengths)
+    longest = int(np.argmax(lengths))
+    shortest = int(np.argmin([L if L > 0 else 10 ** 9 for L in lengths]))
+    check_chains(x, o1, s1, [(longest, 0), (shortest, H - 1), (N - 1, H // 2)], TOL["bf16"])
+
+
 @pytest.mark.parametrize("as_handle", [False, True])
 def test_explicit_stream_argument(kda, as_handle):
     """prefill(stream=...) on a stream other than torch's current one, given as a
