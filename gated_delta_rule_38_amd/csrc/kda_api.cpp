@@ -493,8 +493,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
         const int64_t cap = ce ? atoll(ce) : kCapChains;
         const int64_t S = (cap > 0 && P.H > 0) ? cap / P.H : 0;
         const int cus = device_cus();
-        const bool norm = o && o->out_gate;
-        if (pl.pipe && !P.dense && !norm && P.N > 1 && P.N <= kda::CAP_MAX_N && chains <= cus && S >= 1 &&
+        if (pl.pipe && !P.dense && P.N > 1 && P.N <= kda::CAP_MAX_N && chains <= cus && S >= 1 &&
             S * P.H < chains && S <= kda::CAP_MAX_SLOTS && P.N * S <= kda::CAP_MAX_WORK)
             pl.cap_slots = (int)S;
     }

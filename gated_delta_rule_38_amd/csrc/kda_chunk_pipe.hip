@@ -84,8 +84,8 @@ constexpr int S_NRM = SMEM;
 constexpr int S_NW = S_NRM + C * 4 * 4;
 constexpr int SMEM_NORM = S_NW + D * 4;
 static_assert(SMEM_NORM <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-// capped concurrency (without the norm): its packing scratch where the norm keeps its sums
-constexpr int S_CAP = SMEM;
+// capped concurrency: its packing scratch, after the norm's sums
+constexpr int S_CAP = SMEM_NORM;
 constexpr int SMEM_CAP = S_CAP + 4 * (3 * CAP_MAX_N + 2 * CAP_MAX_SLOTS + 4);
 static_assert(SMEM_CAP <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
 static_assert(4 * (LPT_MAX_SEQ + 1) <= B_SIZE, "longest-first scratch fits in operand buffer 0");
@@ -265,7 +265,7 @@ __device__ __forceinline__ void decay_tile(f32x16 &s, const float4 dd)
 template <bool STALL, bool OUT, bool NORM, bool MC>
 __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
 {
-    __shared__ __attribute__((aligned(16))) char smem[NORM ? SMEM_NORM : (OUT && !MC) ? SMEM_CAP : SMEM];
+    __shared__ __attribute__((aligned(16))) char smem[(OUT && !MC) ? SMEM_CAP : SMEM];
     float *sG = (float *)(smem + S_G), *sGraw = (float *)(smem + S_GRAW);
     bf16 *sX = (bf16 *)(smem + S_X), *sY = (bf16 *)(smem + S_Y), *sZ = (bf16 *)(smem + S_Z);
     bf16 *sKb = (bf16 *)(smem + S_KB), *sA10 = (bf16 *)(smem + S_A10);
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
     }
     const int h = chain % p.H;
     const int n = p.lpt ? longest_first(p.cu, p.N, chain / p.H, smem) : chain / p.H;
-    const bool capped = OUT && !MC && !NORM && role == ROLE_OUT && p.cap_slots > 0;
+    const bool capped = OUT && !MC && role == ROLE_OUT && p.cap_slots > 0;
     int cap_len = 0;                    // capped: sequence tid's length (threads tid < N), for cap_wait
     if (capped && tid < p.N) cap_len = p.cu[tid + 1] - p.cu[tid];
     int64_t t0, bsel;

@@ -75,7 +75,7 @@
  *                whenever the plan allows it.
  *   KDA_CAP      chains allowed to run at once in a packed single-segment launch whose
  *                chains all fit the compute units (default 160; 0 turns it off).  With
- *                more chains than that (at most 128 sequences, no output norm), the
+ *                more chains than that (at most 128 sequences), the
  *                kernel packs the sequences longest first into groups of H workgroups and,
  *                when the longest sequence still bounds the packing, a workgroup whose
  *                sequence follows another in its group waits (bounded) for that
