@@ -402,7 +402,9 @@ def timing_modes(kda, x, w, out, fin, steps, groups=7, calls=8):
     groups, as median / p10 / p90 of the per-call milliseconds:
       pipelined -- `steps` calls back to back, timed by events on the stream around the group;
       per_call  -- `calls` calls each synchronised (host dispatch included), the group's median;
-      graph     -- `calls` kda_prefill_ws launches captured in one HIP graph, one replay per group."""
+      graph     -- `calls` kda_prefill_ws launches captured in one HIP graph, replayed back to back
+                   max(1, steps // calls) times per group (so that a group holds about as many calls
+                   as a pipelined one and times neither the first launch nor an idle GPU's clock)."""
     import statistics
     import torch
     args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
@@ -435,15 +437,18 @@ def timing_modes(kda, x, w, out, fin, steps, groups=7, calls=8):
             kda.prefill(*args, out=out, final_state=fin, workspace=ws)
     graph.replay()
     torch.cuda.synchronize()
+    reps = max(1, steps // calls)
     for _ in range(groups):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        graph.replay()
+        for _ in range(reps):
+            graph.replay()
         e1.record()
         torch.cuda.synchronize()
-        per_graph.append(e0.elapsed_time(e1) / calls)
+        per_graph.append(e0.elapsed_time(e1) / (calls * reps))
     return {"pipelined_ms": _stats(pipelined), "per_call_ms": _stats(per_call), "graph_ms": _stats(per_graph),
-            "graph_calls": calls, "pipelined_calls_per_group": steps, "per_call_calls_per_group": calls}
+            "graph_calls": calls, "graph_replays_per_group": reps, "pipelined_calls_per_group": steps,
+            "per_call_calls_per_group": calls}
 
 
 def settle(step, seconds=0.2):

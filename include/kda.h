@@ -82,8 +82,9 @@
  *                sequence's chain of the same head before its main loop: mixed-length
  *                batches finish sooner, results are the same bits.  The plan then needs 4
  *                bytes of workspace per chain, last in the workspace; a workspace without
- *                them runs the launch uncapped.  A captured graph replays one call's flag
- *                value, so replays after the first run uncapped.
+ *                them runs the launch uncapped.  A captured call keeps its flag value: a
+ *                graph of two or more calls on one workspace stays capped on every
+ *                replay, a graph of one call runs uncapped after its first replay.
  *   KDA_CAP_WAIT_US  bound of each such wait in microseconds (test knob; default: 8 us
  *                per chunk of the awaited sequence plus 2 ms).
  */

@@ -749,6 +749,50 @@ def test_capped_concurrency_same_bits(kda, monkeypatch):
     check_chains(x, out, sT, [(7, 0), (7, 31), (4, 5), (0, 17), (6, 31), (3, 2)], TOL["bf16"])
 
 
+def test_capped_concurrency_in_graph(kda, monkeypatch):
+    """Capped calls captured in HIP graphs on one workspace, which holds the chains' flags.  A
+    graph of two calls (different q) is replayed three times, with eager work and
+    synchronisations between the replays, and a graph of one call likewise (it runs uncapped
+    after its first replay): every replay gives the bits of eager uncapped calls."""
+    import torch
+    w = workloads.custom(workloads.varlen_lengths(), H=32, D=128, seed=98)    # 256 chains
+    x = gen(w)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(99)
+    q2 = torch.randn(x["q"].shape, generator=gq, device="cuda")
+    x2 = dict(x, q=(q2 / q2.norm(dim=-1, keepdim=True)).to(x["q"].dtype))
+    monkeypatch.setenv("KDA_CAP", "0")
+    refs = [run(kda, x), run(kda, x2)]
+    monkeypatch.delenv("KDA_CAP")
+    torch.cuda.synchronize()
+    ws_bytes = kda.workspace_size(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device="cuda")
+    outs = [(torch.empty_like(x["v"]), torch.empty_like(x["initial_state"])) for _ in range(2)]
+    for ncalls in (2, 1):
+        say("capped graph of", ncalls, "calls")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in range(ncalls):
+                run(kda, (x, x2)[c], out=outs[c][0], final_state=outs[c][1], workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in range(ncalls):
+                run(kda, (x, x2)[c], out=outs[c][0], final_state=outs[c][1], workspace=ws)
+        for rep in range(3):
+            for o, f in outs:
+                o.fill_(float("nan"))
+                f.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            for c in range(ncalls):
+                assert torch_equal(outs[c][0], refs[c][0]) and torch_equal(outs[c][1], refs[c][1]), (ncalls, rep, c)
+            run(kda, x2)              # eager work between the replays
+            torch.cuda.synchronize()
+        del graph
+
+
 def _capped_case(i):
     rng = np.random.default_rng(7000 + i)
     H = int(rng.choice([16, 32, 64]))
