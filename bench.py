@@ -24,7 +24,10 @@ oracle on the host's cores (and on one thread) over a bounded sample.  The
 default (varlen, the H = 32 workload of the headline metric) also measures the
 large workload (B=16, H=64, T=8192; the roofline workload) the same way, in
 `large`, and the two segmented-plan workloads (eqlen: B=2, H=16, T=4096; long:
-B=1, H=8, T=65536) in `segmented`.  Prints ONE JSON line.
+B=1, H=8, T=65536) in `segmented`.  After the timings of varlen and large, `power`
+holds the socket power and GFX clocks amd-smi reports while the same call runs
+back to back for 1.5 s (null without amd-smi; `--no-power` skips it).  Prints
+ONE JSON line.
 """
 import argparse
 import hashlib
@@ -451,6 +454,69 @@ def timing_modes(kda, x, w, out, fin, steps, groups=7, calls=8):
             "per_call_calls_per_group": calls}
 
 
+def parse_amdsmi_metric(text):
+    """(socket power W, lowest GFX clock MHz, highest GFX clock MHz) from the JSON of
+    `amd-smi metric -p -c --json` for a box that shows exactly one GPU; None otherwise."""
+    d = json.loads(text)
+    gpus = d.get("gpu_data") if isinstance(d, dict) else d
+    if not isinstance(gpus, list) or len(gpus) != 1:
+        return None
+    g = gpus[0]
+    pw = float(g["power"]["socket_power"]["value"])
+    clks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+            if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+    if not clks:
+        return None
+    return pw, min(clks), max(clks)
+
+
+def power_sample(step, seconds=1.5):
+    """Socket power and GFX clocks while `step` runs back to back for `seconds` (after the timed
+    steps, so the timing is not affected): `amd-smi metric -p -c --json` polled from a second
+    thread, medians over the samples taken after the first 0.4 s.  None when amd-smi is absent,
+    fails or reports anything but one GPU: the record is context, not a measurement of ours."""
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    if seconds <= 0 or shutil.which("amd-smi") is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        t_start = time.perf_counter()
+        while not stop.is_set():
+            try:
+                p = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=5)
+                v = parse_amdsmi_metric(p.stdout)
+            except Exception:
+                v = None
+            if v is None:
+                samples.append(None)
+                return
+            if time.perf_counter() - t_start > 0.4:
+                samples.append(v)
+            stop.wait(0.2)
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds and th.is_alive():
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=10)
+    if not samples or any(v is None for v in samples):
+        return None
+    return {"socket_power_w": statistics.median(v[0] for v in samples),
+            "gfx_clock_mhz_lowest_xcd": statistics.median(v[1] for v in samples),
+            "gfx_clock_mhz_highest_xcd": statistics.median(v[2] for v in samples),
+            "samples": len(samples), "seconds": seconds, "source": "amd-smi metric -p -c"}
+
+
 def settle(step, seconds=0.2):
     """Untimed steps for at least `seconds` of wall time (GPU back to steady state)."""
     import torch
@@ -492,7 +558,7 @@ def kernel_record(w, prof, steps, call_ms=None):
     return roof, mfma, kern
 
 
-def prefill_record(kda, w, steps, warmup, groups, checks_count):
+def prefill_record(kda, w, steps, warmup, groups, checks_count, power_seconds=0.0):
     """Everything measured on one prefill workload: the pre-timing checks, the K timed steps
     (wall clock, and the library's HIP events for the roofline), and the timing groups."""
     import torch
@@ -550,8 +616,9 @@ def prefill_record(kda, w, steps, warmup, groups, checks_count):
         prof = kda.profile_read_kernels()
         roof, mfma, kern = kernel_record(w, prof, steps, call_ms=call_ms)
     modes = timing_modes(kda, x, w, out, fin, steps, groups)
+    power = power_sample(step, power_seconds)
     return {"x": x, "elapsed": t1 - t0, "roofline": roof, "mfma": mfma, "kernel": kern, "checks": checks,
-            "timing_modes": modes}
+            "timing_modes": modes, "power": power}
 
 
 def peak_main(a):
@@ -615,6 +682,8 @@ def main():
     ap.add_argument("--no-segmented", action="store_true",
                     help="skip the segmented-plan sub-records (eqlen, long) of the default run")
     ap.add_argument("--peak", action="store_true", help="measure the practical HBM and MFMA ceilings instead")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the 1.5 s amd-smi power and clock sample after the varlen and large timings")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="instead of the bench, copy this many MiB device-to-device 5 times (PMC calibration)")
     a = ap.parse_args()
@@ -644,7 +713,8 @@ def main():
     if a.config in workloads.DECODE_WORKLOADS:
         return decode_main(a, workloads.DECODE_WORKLOADS[a.config])
     w = workloads.WORKLOADS[a.config]
-    r = prefill_record(kda, w, a.steps, a.warmup, a.groups, 16 if w.name in ("varlen", "large") else 8)
+    r = prefill_record(kda, w, a.steps, a.warmup, a.groups, 16 if w.name in ("varlen", "large") else 8,
+                       0.0 if a.no_power else 1.5)
     elapsed = r["elapsed"]
     rec = {
         "metric": METRIC, "value": w.tokens * a.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
@@ -654,6 +724,7 @@ def main():
         "correctness": r["checks"],
         "work_balance": work_balance(w) if r["kernel"]["launches_per_step"] == 1 else None,
         "timing_modes": r["timing_modes"],
+        "power": r["power"],
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(r["x"], w, a.cpu_budget)
@@ -663,11 +734,11 @@ def main():
         torch.cuda.empty_cache()
         wl = workloads.WORKLOADS["large"]
         steps_l = max(3, min(a.steps, 10))
-        rl = prefill_record(kda, wl, steps_l, min(a.warmup, 5), a.groups, 16)
+        rl = prefill_record(kda, wl, steps_l, min(a.warmup, 5), a.groups, 16, 0.0 if a.no_power else 1.5)
         rec["large"] = {"config": wl.describe(), "steps": steps_l, "ms_per_step": rl["elapsed"] / steps_l * 1e3,
                         "tokens_per_s": wl.tokens * steps_l / rl["elapsed"], "roofline": rl["roofline"],
                         "mfma": rl["mfma"], "kernel": rl["kernel"], "correctness": rl["checks"],
-                        "timing_modes": rl["timing_modes"]}
+                        "timing_modes": rl["timing_modes"], "power": rl["power"]}
     if a.config == "varlen" and not a.no_segmented:
         # the workloads with too few chains to fill the CUs, on segmented plans (map pass, COMBINE,
         # segment outputs): whole-call roofline and the per-kernel split, timed the same way

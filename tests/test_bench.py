@@ -178,3 +178,17 @@ def test_committed_traffic_figures_match_the_current_kernel_sources():
         assert os.path.exists(os.path.join(ROOT, "profiles", rec["source"])), f
         ratio = rec["hbm_bytes_per_launch"] / rec.get("algorithmic_bytes", rec.get("algorithmic_bytes_per_launch"))
         assert (0.99 <= ratio <= 1.05) if kernel != "whole_call" else (1.5 <= ratio <= 2.2), (f, ratio)
+
+
+def test_power_sample_reads_one_gpu_from_amdsmi_json():
+    """The amd-smi JSON (`metric -p -c --json`, the layout printed on MI355X) gives the socket
+    power and the lowest and highest GFX clock of the XCDs; a listing of several GPUs gives
+    None, since the record could not say which one ran the call."""
+    one = {"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": 1400, "unit": "W"}, "gfx_voltage": "N/A"},
+                         "clock": {"gfx_0": {"clk": {"value": 1729, "unit": "MHz"}, "clk_locked": "DISABLED"},
+                                   "gfx_1": {"clk": {"value": 1847, "unit": "MHz"}},
+                                   "gfx_2": {"clk": {"value": 1780, "unit": "MHz"}},
+                                   "mem_0": {"clk": {"value": 2000, "unit": "MHz"}}}}]}
+    assert bench.parse_amdsmi_metric(json.dumps(one)) == (1400.0, 1729.0, 1847.0)
+    two = {"gpu_data": one["gpu_data"] * 2}
+    assert bench.parse_amdsmi_metric(json.dumps(two)) is None
