@@ -513,7 +513,7 @@ kda_status_t make_plan(const Problem &P, const kda_options_t *o, Plan &pl, size_
         }
         if (nseg == 1 && pl.cap_slots > 0) {
             pl.off_flags = off;
-            off += align256((size_t)chains * 4);
+            off += align256((size_t)chains * 8);
         }
         return off;
     };
@@ -647,7 +647,7 @@ kda_status_t run(const Problem &P, const Plan &pl, const kda_options_t *o, void 
     cp.lpt = pl.lpt ? 1 : 0;
     if (cap_on) {
         cp.cap_slots = pl.cap_slots;
-        cp.cap_flags = (uint32_t *)(wsb + pl.off_flags);
+        cp.cap_flags = (uint64_t *)(wsb + pl.off_flags);
         // a fresh value per call, never 0: flags left by earlier calls (or the workspace's first
         // contents, unless they happen to match) do not release a waiting workgroup early
         uint32_t e = g_cap_epoch.fetch_add(1) + 1;

@@ -134,11 +134,24 @@ __device__ int longest_first(const int32_t *cu, int N, int r, char *smem)
 // wait is bounded all the same, and it orders no data.  Every thread calls it at the same
 // point of its prologue (after its first loads are issued, so their latency overlaps); thread
 // i < N brings sequence i's length in tokens; sc is the dedicated scratch (S_CAP).
-__device__ void cap_wait(const ChunkParams &p, int n, int h, int len_i, char *sc)
+//
+// A chain's flag holds the call's value (low word) and a count (high word).  Thread 0 returns
+// the flag this chain stores when it finishes: the call's value with its previous count plus
+// one when the flag already holds this call's value (a graph replaying the same captured call,
+// whose chains all replay together), else with count 1.  A waiting workgroup waits for its
+// predecessor's flag to reach that same value.
+__device__ uint64_t cap_wait(const ChunkParams &p, int n, int h, int len_i, char *sc)
 {
     const int N = p.N, S = p.cap_slots;
     int *sLen = (int *)sc, *sOrd = sLen + CAP_MAX_N, *sPred = sOrd + CAP_MAX_N, *sLoad = sPred + CAP_MAX_N;
     int *sLast = sLoad + CAP_MAX_SLOTS, *sOk = sLast + CAP_MAX_SLOTS;
+    uint64_t next = 0;
+    if (threadIdx.x == 0) {
+        const uint64_t own = __hip_atomic_load(p.cap_flags + (int64_t)n * p.H + h, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t count = ((uint32_t)own == p.cap_epoch) ? (uint32_t)(own >> 32) + 1u : 1u;
+        next = ((uint64_t)count << 32) | p.cap_epoch;
+    }
     if ((int)threadIdx.x < N) sLen[threadIdx.x] = (len_i + C - 1) / C + 3;
     __syncthreads();
     if ((int)threadIdx.x < N) {
@@ -174,14 +187,15 @@ __device__ void cap_wait(const ChunkParams &p, int n, int h, int len_i, char *sc
             // bound: the given one, else 8 us per chunk of the predecessor plus 2 ms (100 MHz ticks)
             const uint64_t limit = 100ull * (p.cap_wait_us > 0 ? (uint64_t)p.cap_wait_us
                                                                   : 8ull * (uint64_t)sLen[pred] + 2000ull);
-            const uint32_t *f = p.cap_flags + (int64_t)pred * p.H + h;
+            const uint64_t *f = p.cap_flags + (int64_t)pred * p.H + h;
             const uint64_t ts = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.cap_epoch &&
+            while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next &&
                    __builtin_amdgcn_s_memrealtime() - ts < limit)
                 __builtin_amdgcn_s_sleep(32);
         }
     }
     __syncthreads();
+    return next;
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4a+b receives
@@ -778,7 +792,8 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         Frag8<bf16> IdV[2];
         if constexpr (!MC) make_idv(IdV);
         if (nck > 0) prefetch_qkv(c_begin);
-        if (capped) cap_wait(p, n, h, cap_len, smem + S_CAP);
+        uint64_t cap_next = 0;          // thread 0: the flag value this chain stores when it is done
+        if (capped) cap_next = cap_wait(p, n, h, cap_len, smem + S_CAP);
         sync();
         sync();
         for (int t = 0; nck > 0 && t <= nck; ++t) {
@@ -995,7 +1010,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_pipe_kernel(const ChunkParams p)
         // capped concurrency: this chain is done (its last stores are issued); a workgroup
         // queued behind its sequence may start
         if (capped && tid == 0)
-            __hip_atomic_store(p.cap_flags + (int64_t)n * p.H + h, p.cap_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.cap_flags + (int64_t)n * p.H + h, cap_next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -317,13 +317,15 @@ struct ChunkParams {
     // Capped concurrency (packed layout, one segment, every chain resident at once): the
     // sequences, longest first, are packed into cap_slots groups of H workgroups, each
     // sequence into the least-loaded group; a workgroup whose sequence follows another one in
-    // its group first waits until the chain of the same head of that sequence has set its
-    // flag to cap_epoch, or until cap_wait_us (0: a bound from the predecessor's length) has
-    // passed.  The wait orders no data: it only keeps fewer chains running at once.  0 = off.
+    // its group first waits until the chain of the same head of that sequence has stored the
+    // value its own flag will take (cap_epoch, with a count that tells replays of one captured
+    // call apart), or until cap_wait_us (0: a bound from the predecessor's length) has passed.
+    // The wait orders no data: it only keeps fewer chains running at once.  0 = off.
     int32_t cap_slots;
     uint32_t cap_epoch;
     int32_t cap_wait_us;
-    uint32_t *cap_flags;       // [N * H] in the workspace, chain n * H + h
+    uint64_t *cap_flags;       // [N * H] in the workspace, chain n * H + h: the call's value
+                               // (low word) and a count of replays of that call (high word)
 };
 
 // Longest-first chain order: at most this many sequences (one launch ranks them all in LDS).

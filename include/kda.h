@@ -80,11 +80,11 @@
  *                when the longest sequence still bounds the packing, a workgroup whose
  *                sequence follows another in its group waits (bounded) for that
  *                sequence's chain of the same head before its main loop: mixed-length
- *                batches finish sooner, results are the same bits.  The plan then needs 4
+ *                batches finish sooner, results are the same bits.  The plan then needs 8
  *                bytes of workspace per chain, last in the workspace; a workspace without
- *                them runs the launch uncapped.  A captured call keeps its flag value: a
- *                graph of two or more calls on one workspace stays capped on every
- *                replay, a graph of one call runs uncapped after its first replay.
+ *                them runs the launch uncapped.  The flags tell calls and replays of one
+ *                captured call apart, so calls captured in HIP graphs stay capped on
+ *                every replay.
  *   KDA_CAP_WAIT_US  bound of each such wait in microseconds (test knob; default: 8 us
  *                per chunk of the awaited sequence plus 2 ms).
  */
@@ -185,7 +185,7 @@ kda_status_t kda_prefill(const kda_tensor_t *q, const kda_tensor_t *k, const kda
                          kda_tensor_t *out, kda_tensor_t *final_state, void *stream);
 
 /* Bytes of device workspace kda_prefill_ws needs for these descriptors and
- * options: 0 when the plan is a single chunk-kernel launch (4 bytes per chain when it
+ * options: 0 when the plan is a single chunk-kernel launch (8 bytes per chain when it
  * caps the chains running at once, see KDA_CAP); with nseg > 1 the
  * segment maps and segment start states (K x V each, 4 bytes an element: the
  * start states and the C maps fp32, the M maps fp32 or, on bf16 I/O, split into

@@ -535,7 +535,7 @@ def test_planner_splits_chains_just_above_the_cu_count(tmp_path):
 def test_plan_capped_concurrency(tmp_path):
     """A packed single-segment launch with every chain resident (<= 256 without a GPU) and
     more chains than the cap (160) plans the capped schedule: groups of H workgroups, a
-    4-byte flag per chain last in the workspace.  Not with at most 160 chains, more chains
+    8-byte flag per chain last in the workspace.  Not with at most 160 chains, more chains
     than CUs (longest first instead), the dense layout, more than 16 groups, or KDA_CAP=0."""
     import subprocess, sys, textwrap
     code = textwrap.dedent(f"""
@@ -567,4 +567,4 @@ def test_plan_capped_concurrency(tmp_path):
     caps = [int(l.split("cap=")[1].split()[0]) for l in p.stderr.splitlines() if l.startswith("kda: plan")]
     assert caps == [160, 0, 0, 0, 0, 96], caps
     sizes = [int(l.split("bytes ")[1]) for l in p.stdout.splitlines() if l.startswith("case")]
-    assert sizes == [1024, 0, 0, 0, 0, 768], sizes
+    assert sizes == [2048, 0, 0, 0, 0, 1536], sizes

@@ -752,8 +752,9 @@ def test_capped_concurrency_same_bits(kda, monkeypatch):
 def test_capped_concurrency_in_graph(kda, monkeypatch):
     """Capped calls captured in HIP graphs on one workspace, which holds the chains' flags.  A
     graph of two calls (different q) is replayed three times, with eager work and
-    synchronisations between the replays, and a graph of one call likewise (it runs uncapped
-    after its first replay): every replay gives the bits of eager uncapped calls."""
+    synchronisations between the replays, and a graph of one call likewise (its chains find
+    the captured call's value in their own flags and count replays): every replay gives the
+    bits of eager uncapped calls."""
     import torch
     w = workloads.custom(workloads.varlen_lengths(), H=32, D=128, seed=98)    # 256 chains
     x = gen(w)
