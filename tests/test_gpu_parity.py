@@ -716,6 +716,30 @@ def test_longest_first_order_same_bits(kda, monkeypatch):
     check_chains(x, out, sT, [(5, 47), (1, 0), (3, 20), (2, 5)], TOL["bf16"])
 
 
+@pytest.mark.parametrize("N", [512, 600])
+def test_many_short_sequences(kda, monkeypatch, N):
+    """Packed batches of many short ragged sequences (one head, lengths 0 to 160, about one in
+    eight empty): 512 sequences, the most the workgroups rank longest first (512 chains on
+    256 CUs take that order by default), and 600, past it (natural order).  Same bits as the
+    natural order, and the longest, a one-token and an empty sequence, the first and the last
+    against the oracle."""
+    import torch
+    rng = np.random.default_rng(8000 + N)
+    lengths = [int(x) if rng.random() > 0.12 else 0 for x in rng.integers(1, 161, N)]
+    lengths[N // 2] = 1
+    x = gen(workloads.custom(lengths, H=1, D=128, seed=8100 + N))
+    say("many short sequences", N, sum(lengths))
+    monkeypatch.setenv("KDA_ORDER", "natural")
+    o0, s0 = run(kda, x)
+    monkeypatch.delenv("KDA_ORDER")
+    o1, s1 = run(kda, x)
+    torch.cuda.synchronize()
+    assert torch_equal(o0, o1) and torch_equal(s0, s1)
+    empty = lengths.index(0)
+    check_chains(x, o1, s1, [(int(np.argmax(lengths)), 0), (N // 2, 0), (empty, 0), (0, 0), (N - 1, 0)],
+                 TOL["bf16"])
+
+
 def test_capped_concurrency_same_bits(kda, monkeypatch):
     """The capped schedule (packed, one segment, more chains than the 160-chain cap, every
     chain resident) only delays when some workgroups start: outputs and final states are the
