@@ -126,10 +126,11 @@ __device__ int longest_first(const int32_t *cu, int N, int r, char *smem)
 // Capped concurrency: the step time of this kernel hardly depends on how many chains run at
 // once up to about 160 of 256 CUs and then climbs (the clock and HBM under full load), while a
 // packed batch of mixed lengths ends with its longest chain.  So the sequences are packed,
-// longest first, into cap_slots groups of H workgroups (each into the least-loaded group; the
-// per-sequence cost is its chunks plus 3 for the pipeline's fill), and when the longest
-// sequence alone still bounds the packing, a workgroup whose sequence follows another one in
-// its group waits for that sequence's chain of the same head to finish before its main loop.
+// longest first, into groups of H workgroups (each into the least-loaded group; the
+// per-sequence cost is its chunks plus 3 for the pipeline's fill): the fewest groups, from
+// cap_slots up, with which the longest sequence alone still bounds the packing.  A workgroup
+// whose sequence follows another one in its group then waits for that sequence's chain of the
+// same head to finish before its main loop.
 // Every chain is resident at once (chains <= CUs), so a predecessor is always running; the
 // wait is bounded all the same, and it orders no data.  Every thread calls it at the same
 // point of its prologue (after its first loads are issued, so their latency overlaps); thread
@@ -166,23 +167,30 @@ __device__ uint64_t cap_wait(const ChunkParams &p, int n, int h, int len_i, char
     }
     __syncthreads();
     // the S longest sequences open the groups: their workgroups (the ones that bound the call)
-    // skip the packing
+    // skip the packing.  The others pack with S groups, then S + 1, ... (fewer than N) until the
+    // longest sequence alone still bounds the packing; none of those counts: no wait
     if (threadIdx.x == 0 && sOk[0] >= S) {
-        for (int g = 0; g < S; ++g) {
-            sLoad[g] = 0;
-            sLast[g] = -1;
+        int pred = -1;
+        for (int G = S; G < N && G <= CAP_MAX_SLOTS; ++G) {
+            for (int g = 0; g < G; ++g) {
+                sLoad[g] = 0;
+                sLast[g] = -1;
+            }
+            for (int r = 0; r < N; ++r) {
+                const int i = sOrd[r];
+                int best = 0;
+                for (int g = 1; g < G; ++g) best = sLoad[g] < sLoad[best] ? g : best;
+                sPred[i] = sLast[best];
+                sLast[best] = i;
+                sLoad[best] += sLen[i];
+            }
+            int most = 0;
+            for (int g = 0; g < G; ++g) most = max(most, sLoad[g]);
+            if (most <= sLen[sOrd[0]] + 2) {
+                pred = sPred[n];
+                break;
+            }
         }
-        for (int r = 0; r < N; ++r) {
-            const int i = sOrd[r];
-            int best = 0;
-            for (int g = 1; g < S; ++g) best = sLoad[g] < sLoad[best] ? g : best;
-            sPred[i] = sLast[best];
-            sLast[best] = i;
-            sLoad[best] += sLen[i];
-        }
-        int most = 0;
-        for (int g = 0; g < S; ++g) most = max(most, sLoad[g]);
-        const int pred = (most <= sLen[sOrd[0]] + 2) ? sPred[n] : -1;
         if (pred >= 0) {
             // bound: the given one, else 8 us per chunk of the predecessor plus 2 ms (100 MHz ticks)
             const uint64_t limit = 100ull * (p.cap_wait_us > 0 ? (uint64_t)p.cap_wait_us

@@ -76,8 +76,9 @@
  *   KDA_CAP      chains allowed to run at once in a packed single-segment launch whose
  *                chains all fit the compute units (default 160; 0 turns it off).  With
  *                more chains than that (at most 128 sequences), the
- *                kernel packs the sequences longest first into groups of H workgroups and,
- *                when the longest sequence still bounds the packing, a workgroup whose
+ *                kernel packs the sequences longest first into groups of H workgroups (the
+ *                fewest groups, from cap / H up, with which the longest sequence still
+ *                bounds the packing; none: uncapped), and a workgroup whose
  *                sequence follows another in its group waits (bounded) for that
  *                sequence's chain of the same head before its main loop: mixed-length
  *                batches finish sooner, results are the same bits.  The plan then needs 8
